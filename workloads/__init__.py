@@ -1,0 +1,16 @@
+"""Seeded synthetic workloads for paged prefix-reuse attention.
+
+This module only draws inputs: lengths, block placements, block tables, slot
+mappings and N(0,1) values rounded to 16-bit payloads.  It holds none of the
+attention arithmetic.  Both the fp64 oracle (through the tests) and the HIP path
+(through the tests and the benchmark) consume what it returns.
+"""
+from .gen import (  # noqa: F401
+    CONFIGS,
+    Workload,
+    make,
+    make_config,
+    make_custom,
+    round_to_bits,
+    blocks_for,
+)
