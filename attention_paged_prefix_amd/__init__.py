@@ -1,0 +1,170 @@
+"""Paged prefix-reuse attention for MI355X (gfx950): Python binding of libkvb.so.
+
+The calls mirror the C ABI in ``include/kvb.h`` (kvb_write_kv, kvb_paged_prefill,
+kvb_paged_decode, kvb_gather_kv and the workspace-size queries).  This layer only
+marshals arguments: it takes torch device tensors for memory, passes their
+addresses and the current HIP stream, and raises on a non-OK status.  Every step
+of the computation runs in the library's HIP kernels; if the library is missing
+the calls raise instead of falling back to anything else.
+
+Pool layout: ``[num_blocks][num_kv_heads][16][head_dim]`` for K and for V (16-bit
+payloads), one (block, kv-head) tile a contiguous 16 x head_dim run.  The pool of
+fixed 16-token blocks follows kvboost 0.6.0, section "CPU paged attention".
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool  # noqa: F401
+
+__all__ = [
+    "Pool", "write_kv", "paged_prefill", "paged_decode", "gather_kv",
+    "paged_prefill_workspace_size", "paged_decode_workspace_size", "version", "KvbError",
+]
+
+BLOCK_SIZE = 16
+_DT = {torch.float16: KVB_FP16, torch.bfloat16: KVB_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class Pool:
+    """K/V block pool.  ``k``/``v`` are device tensors whose element (block, head,
+    row, e) sits at ``block*block_stride + (head*16 + row)*head_dim + e``."""
+    k: torch.Tensor
+    v: torch.Tensor
+    num_blocks: int
+    num_kv_heads: int
+    head_dim: int
+    block_stride: int
+
+    @classmethod
+    def from_tensors(cls, k: torch.Tensor, v: torch.Tensor) -> "Pool":
+        """Pool from two contiguous ``[num_blocks][num_kv_heads][16][head_dim]`` tensors."""
+        nb, hkv, bs, d = k.shape
+        if bs != BLOCK_SIZE or v.shape != k.shape or not k.is_contiguous() or not v.is_contiguous():
+            raise ValueError("pool tensors must be contiguous [num_blocks][num_kv_heads][16][head_dim]")
+        return cls(k, v, nb, hkv, d, hkv * BLOCK_SIZE * d)
+
+    @classmethod
+    def interleaved(cls, kv: torch.Tensor) -> "Pool":
+        """Pool from one ``[num_blocks][2][num_kv_heads][16][head_dim]`` tensor: K and V of a
+        block side by side, i.e. one page of block_size x heads x head_dim x 2 x dtype_bytes."""
+        nb, two, hkv, bs, d = kv.shape
+        if two != 2 or bs != BLOCK_SIZE or not kv.is_contiguous():
+            raise ValueError("expected contiguous [num_blocks][2][num_kv_heads][16][head_dim]")
+        return cls(kv[:, 0], kv[:, 1], nb, hkv, d, 2 * hkv * BLOCK_SIZE * d)
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.k.dtype
+
+    def c_struct(self) -> KvbPool:
+        if self.k.dtype not in _DT:
+            raise ValueError(f"unsupported pool dtype {self.k.dtype}")
+        return KvbPool(self.k.data_ptr(), self.v.data_ptr(), self.block_stride, self.num_blocks,
+                       BLOCK_SIZE, self.num_kv_heads, self.head_dim, _DT[self.k.dtype])
+
+
+def version() -> str:
+    return _lib.load().kvb_version().decode()
+
+
+def write_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+             stream=None) -> None:
+    """kvb_write_kv: scatter ``k_new/v_new [T][Hkv][d]`` into pool slots ``slot_mapping`` (int64)."""
+    lib = _lib.load()
+    ps = pool.c_struct()
+    _lib.check("kvb_write_kv", lib.kvb_write_kv(
+        ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(slot_mapping.numel()),
+        _stream(stream)))
+
+
+def paged_prefill_workspace_size(batch: int, num_q_heads: int, head_dim: int, total_q: int,
+                                 max_prefix_len: int) -> int:
+    return int(_lib.load().kvb_paged_prefill_workspace_size(batch, num_q_heads, head_dim, total_q,
+                                                            max_prefix_len))
+
+
+def paged_decode_workspace_size(batch: int, num_kv_heads: int, num_q_heads: int, head_dim: int,
+                                max_context_len: int, split_blocks: int = 0) -> int:
+    return int(_lib.load().kvb_paged_decode_workspace_size(batch, num_kv_heads, num_q_heads, head_dim,
+                                                           max_context_len, split_blocks))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                  cu_q_lens: torch.Tensor, prefix_lens: torch.Tensor, block_tables: torch.Tensor,
+                  scale: float, max_q_len: int, max_prefix_len: int,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """kvb_paged_prefill.  ``q [T][Hq][d]``, ``k_new/v_new [T][Hkv][d]``, ``cu_q_lens`` int32
+    [B+1], ``prefix_lens`` int32 [B], ``block_tables`` int32 [B][stride]."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    batch = int(prefix_lens.numel())
+    T, hq, d = q.shape
+    need = paged_prefill_workspace_size(batch, hq, d, T, max_prefix_len)
+    workspace = _workspace(need, q.device, workspace)
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_prefill", lib.kvb_paged_prefill(
+        ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(cu_q_lens),
+        _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch, hq, T,
+        int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def paged_decode(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
+                 block_tables: torch.Tensor, scale: float, max_context_len: int,
+                 split_blocks: int = 0, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvb_paged_decode.  ``q [B][Hq][d]``, ``context_lens`` int32 [B] (including the current
+    token), ``block_tables`` int32 [B][stride]."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    B, hq, d = q.shape
+    need = paged_decode_workspace_size(B, pool.num_kv_heads, hq, d, max_context_len, split_blocks)
+    workspace = _workspace(need, q.device, workspace)
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_decode", lib.kvb_paged_decode(
+        ctypes.byref(ps), _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
+        int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def gather_kv(pool: Pool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+              cu_seq_lens: torch.Tensor, max_len: int, k_out: torch.Tensor, v_out: torch.Tensor,
+              stream=None) -> None:
+    """kvb_gather_kv (indexing check): logical tokens of every sequence, contiguous."""
+    lib = _lib.load()
+    ps = pool.c_struct()
+    _lib.check("kvb_gather_kv", lib.kvb_gather_kv(
+        ctypes.byref(ps), _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
+        _ptr(cu_seq_lens), _ptr(k_out), _ptr(v_out), int(seq_lens.numel()), int(max_len),
+        _stream(stream)))

@@ -1,0 +1,152 @@
+// C ABI: host-side validation (before any HIP call), launch planning and dispatch.
+#include <math.h>
+#include <stdint.h>
+#include "kvb.h"
+#include "kvb_launch.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvb_status check_pool(const kvb_pool* p) {
+  if (!p) return KVB_ERR_NULL;
+  if (!p->k || !p->v) return KVB_ERR_NULL;
+  if (p->dtype != KVB_FP16 && p->dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
+  if (p->block_size != 16) return KVB_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 96 && p->head_dim != 128) return KVB_ERR_UNSUPPORTED;
+  if (p->num_kv_heads <= 0 || p->num_blocks <= 0) return KVB_ERR_INVALID;
+  if (p->block_stride < (int64_t)p->num_kv_heads * 16 * p->head_dim) return KVB_ERR_INVALID;
+  if (p->block_stride % 8 != 0) return KVB_ERR_INVALID;
+  if (!aligned16(p->k) || !aligned16(p->v)) return KVB_ERR_INVALID;
+  return KVB_OK;
+}
+
+kvb_status check_scale(float scale) {
+  if (!isfinite(scale) || scale < 0.f) return KVB_ERR_INVALID;
+  return KVB_OK;
+}
+
+kvb_status launch_status(hipError_t e) { return e == hipSuccess ? KVB_OK : KVB_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvb_status_str(kvb_status s) {
+  switch (s) {
+    case KVB_OK: return "ok";
+    case KVB_ERR_NULL: return "null pointer";
+    case KVB_ERR_INVALID: return "invalid argument";
+    case KVB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVB_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVB_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* kvb_version(void) { return "0.1.0"; }
+
+kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (num_tokens < 0) return KVB_ERR_INVALID;
+  if (num_tokens == 0) return KVB_OK;
+  if (!k_new || !v_new || !slot_mapping) return KVB_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_mapping & 7u)) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_write_kv(*pool, k_new, v_new, slot_mapping, num_tokens,
+                                            (hipStream_t)stream));
+}
+
+size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t total_q, int32_t max_prefix_len) {
+  (void)batch; (void)num_q_heads; (void)head_dim; (void)total_q; (void)max_prefix_len;
+  return 0;
+}
+
+kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
+                             const void* v_new, void* out, const int32_t* cu_q_lens,
+                             const int32_t* prefix_lens, const int32_t* block_tables,
+                             int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                             int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_prefix_len < 0 || num_q_heads <= 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0 || total_q == 0) return KVB_OK;
+  if (!q || !k_new || !v_new || !out || !cu_q_lens || !prefix_lens || !block_tables)
+    return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+      ((uintptr_t)cu_q_lens & 3u) || ((uintptr_t)prefix_lens & 3u) || ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (max_q_len > total_q) return KVB_ERR_INVALID;
+  if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
+  const size_t need = kvb_paged_prefill_workspace_size(batch, num_q_heads, pool->head_dim, total_q,
+                                                       max_prefix_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
+  if (max_q_len == 0) return KVB_OK;
+  return launch_status(kvb::launch_prefill(*pool, q, k_new, v_new, out, cu_q_lens, prefix_lens,
+                                           block_tables, block_table_stride, batch, num_q_heads,
+                                           total_q, max_q_len, max_prefix_len, scale,
+                                           (hipStream_t)stream));
+}
+
+size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t max_context_len,
+                                       int32_t split_blocks) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
+      max_context_len <= 0 || split_blocks < 0)
+    return 0;
+  int sb = 0, ns = 0;
+  kvb::decode_plan(batch, num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
+  return (size_t)kvb::decode_ws_bytes(batch, num_q_heads, head_dim, ns);
+}
+
+kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
+                            const int32_t* context_lens, const int32_t* block_tables,
+                            int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, int32_t split_blocks, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || split_blocks < 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0) return KVB_OK;
+  if (!q || !out || !context_lens || !block_tables) return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
+    return KVB_ERR_INVALID;
+  int sb = 0, ns = 0;
+  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
+  const size_t need = (size_t)kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_decode(*pool, q, out, context_lens, block_tables,
+                                          block_table_stride, batch, num_q_heads, max_context_len,
+                                          sb, ns, scale, workspace, (hipStream_t)stream));
+}
+
+kvb_status kvb_gather_kv(const kvb_pool* pool, const int32_t* block_tables,
+                         int32_t block_table_stride, const int32_t* seq_lens,
+                         const int32_t* cu_seq_lens, void* k_out, void* v_out, int32_t batch,
+                         int32_t max_len, void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || max_len < 0) return KVB_ERR_INVALID;
+  if (batch == 0 || max_len == 0) return KVB_OK;
+  if (!block_tables || !seq_lens || !cu_seq_lens || !k_out || !v_out) return KVB_ERR_NULL;
+  if (!aligned16(k_out) || !aligned16(v_out)) return KVB_ERR_INVALID;
+  if (block_table_stride < (max_len + 15) / 16) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_gather_kv(*pool, block_tables, block_table_stride, seq_lens,
+                                             cu_seq_lens, k_out, v_out, batch, max_len,
+                                             (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side helpers shared by the gfx950 kernels: 16-bit element types,
+// vector types for MFMA operands, cross-lane reductions and the XCD-aware
+// work-group remap.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvb {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kBlock = 16;        // tokens per physical block
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, work-groups dealt round-robin
+
+// Element type tags.  Storage is always the raw 16-bit payload.
+struct F16 {
+  static constexpr int id = 0;
+  __device__ static inline float to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+  __device__ static inline uint16_t from_f32(float f) {   // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+  // 32x32x16 MFMA with 16-bit operands passed as 8 x 16-bit lanes.
+  __device__ static inline f32x16 mfma32(s16x8 a, s16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  // a.x*b.x + a.y*b.y + c (fp32 accumulate)
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
+                                  c, false);
+  }
+};
+
+struct BF16 {
+  static constexpr int id = 1;
+  __device__ static inline float to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+  __device__ static inline uint16_t from_f32(float f) {   // round to nearest even
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+  }
+  __device__ static inline f32x16 mfma32(s16x8 a, s16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+};
+
+// Low / high 16-bit halves of a packed pair, as fp32.
+template <typename T> __device__ inline float lo_f32(uint32_t w) { return T::to_f32((uint16_t)(w & 0xffffu)); }
+template <typename T> __device__ inline float hi_f32(uint32_t w) { return T::to_f32((uint16_t)(w >> 16)); }
+template <> __device__ inline float lo_f32<BF16>(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+template <> __device__ inline float hi_f32<BF16>(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+template <typename T> __device__ inline uint32_t pack2(float a, float b) {
+  return (uint32_t)T::from_f32(a) | ((uint32_t)T::from_f32(b) << 16);
+}
+
+// DPP quad permutations (within groups of 4 lanes): lane ^ 1 and lane ^ 2.
+__device__ inline float quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
+__device__ inline float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// XCD-aware remap: hardware deals consecutive work-group ids round-robin over the
+// XCDs; give each XCD a contiguous range of logical ids so neighbouring logical
+// work (same sequence / KV head) shares that XCD's L2.  `padded` is a multiple of 8.
+__device__ inline int xcd_logical_id(int hw_id, int padded) {
+  int per = padded / kNumXcd;
+  return (hw_id % kNumXcd) * per + hw_id / kNumXcd;
+}
+
+}  // namespace kvb

@@ -1,0 +1,35 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI after validation).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "kvb.h"
+
+namespace kvb {
+
+hipError_t launch_write_kv(const kvb_pool& p, const void* kn, const void* vn, const int64_t* slots,
+                           int num_tokens, hipStream_t s);
+hipError_t launch_gather_kv(const kvb_pool& p, const int32_t* bt, int bt_stride,
+                            const int32_t* seq_lens, const int32_t* cu, void* ko, void* vo,
+                            int batch, int max_len, hipStream_t s);
+
+// Decode: split planning and workspace layout (floats: partial outputs, then (max, sum) pairs).
+int decode_heads_per_wg(int G);
+void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, int* split_blocks,
+                 int* nsplit);
+inline int64_t decode_ws_o_floats(int batch, int hq, int d, int nsplit) {
+  return (int64_t)batch * hq * nsplit * d;
+}
+inline int64_t decode_ws_bytes(int batch, int hq, int d, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return (decode_ws_o_floats(batch, hq, d, nsplit) + (int64_t)batch * hq * nsplit * 2) * 4;
+}
+hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
+                         const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
+                         int ns, float scale, void* ws, hipStream_t s);
+
+hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
+                          const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
+                          int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
+                          float scale, hipStream_t s);
+
+}  // namespace kvb

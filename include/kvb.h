@@ -1,0 +1,149 @@
+/*
+ * kvb.h — C ABI of the paged prefix-reuse attention library (libkvb.so, gfx950).
+ *
+ * The problem these calls solve is stated across three web pages:
+ *   - kvboost 0.6.0 (PyPI project page), "CPU paged attention": K/V live in a fixed,
+ *     pre-allocated pool of 16-token physical blocks; shared prefixes share blocks
+ *     copy-on-write.
+ *   - kvstream 0.1.0 (PyPI project page), "Why KVStream?" feature table and "Request
+ *     lifecycle": pages allocated one slot per generated token; a prefix hit forks the
+ *     cached block table copy-on-write; "Configuration": one page holds
+ *     block_size x heads x head_dim x 2 x dtype_bytes.
+ *   - kvboost 0.6.0, "How it works" step 5: the cached prefix and the live suffix go
+ *     through one forward pass; "Flash Attention (CUDA)": fp16/bf16, head dims
+ *     64/96/128, any sequence length, causal masking that skips future K/V tiles.
+ *
+ * Conventions shared by every call
+ *   - Every pointer marked (device) is a device address on the current HIP device;
+ *     (host) pointers are read during the call only.  The caller owns every buffer.
+ *     The library allocates nothing, never synchronises, never reads device memory
+ *     on the host and keeps no state: calls are thread-safe and asynchronous on
+ *     `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before any HIP call.  A failed check
+ *     returns KVB_ERR_NULL / KVB_ERR_INVALID / KVB_ERR_UNSUPPORTED /
+ *     KVB_ERR_WORKSPACE and launches nothing.  A failed launch returns KVB_ERR_LAUNCH.
+ *   - Device pointers must be 16-byte aligned (KVB_ERR_INVALID otherwise).
+ *   - Device-side index contents are the caller's contract (no device-to-host read
+ *     checks them).  The kernels are nevertheless memory-safe against bad indices:
+ *     a slot or block id outside the pool is never dereferenced (a slot is then
+ *     skipped; a key in such a block is excluded from the softmax).
+ *   - Softmax scale: any finite value >= 0 (1/sqrt(head_dim) is the usual choice).
+ */
+#ifndef KVB_H
+#define KVB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVB_OK = 0,
+  KVB_ERR_NULL = 1,         /* a required pointer is NULL                               */
+  KVB_ERR_INVALID = 2,      /* inconsistent sizes, negative counts, misalignment        */
+  KVB_ERR_UNSUPPORTED = 3,  /* head_dim not in {64,96,128}, block_size != 16, bad dtype */
+  KVB_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query returns */
+  KVB_ERR_LAUNCH = 5        /* the HIP runtime reported an error at launch              */
+} kvb_status;
+
+typedef enum { KVB_FP16 = 0, KVB_BF16 = 1 } kvb_dtype;
+
+/* The K/V block pool.  Layout of each of k and v (device):
+ *   element (block, kv_head, row, e) at  block*block_stride + (kv_head*16 + row)*head_dim + e
+ * so one (block, kv-head) tile is a contiguous 16 x head_dim run (4 KiB at head_dim 128 in
+ * 16-bit types).  block_stride (elements) >= num_kv_heads*16*head_dim and a multiple of 8;
+ * setting v = k + num_kv_heads*16*head_dim and block_stride = 2*num_kv_heads*16*head_dim
+ * interleaves K and V per block, which is exactly one page of the kvstream formula. */
+typedef struct {
+  void*    k;              /* (device) K pool                                  */
+  void*    v;              /* (device) V pool                                  */
+  int64_t  block_stride;   /* elements between consecutive physical blocks     */
+  int32_t  num_blocks;     /* physical blocks in the pool (> 0)                */
+  int32_t  block_size;     /* tokens per block; must be 16                     */
+  int32_t  num_kv_heads;   /* > 0                                              */
+  int32_t  head_dim;       /* 64, 96 or 128                                    */
+  int32_t  dtype;          /* kvb_dtype                                        */
+} kvb_pool;
+
+/* Slot scatter (kvstream 0.1.0, "Why KVStream?": streaming KV allocation, one slot per
+ * token).  For every t < num_tokens with 0 <= slot_mapping[t] < num_blocks*16:
+ *   pool.k[slot/16][h][slot%16][:] = k_new[t][h][:]  and the same for v, for every kv head h.
+ * k_new, v_new: (device) [num_tokens][num_kv_heads][head_dim] contiguous, pool dtype.
+ * slot_mapping: (device) int64 [num_tokens]; negative (or out-of-pool) slots are skipped.
+ * Two tokens mapped to one slot in one call leave an unspecified one of them there.
+ * num_tokens == 0 is a no-op. */
+kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* Paged prefill (kvboost 0.6.0, "How it works" steps 3 and 5; "Flash Attention (CUDA)").
+ * Sequence b owns chunk rows t in [cu_q_lens[b], cu_q_lens[b+1]); chunk row i = t -
+ * cu_q_lens[b] sits at position prefix_lens[b] + i and attends, for query head h, to
+ *   - the cached prefix keys j < prefix_lens[b], read from the pool through
+ *     block_tables[b*block_table_stride + j/16], row j%16, kv head h / (num_q_heads/num_kv_heads);
+ *   - the chunk's own keys 0..i, read from k_new/v_new rows cu_q_lens[b] + 0..i.
+ * out[t][h][:] = softmax(scale * q[t][h] . K^T) V, rounded to the pool dtype.
+ * q, out: (device) [total_q][num_q_heads][head_dim]; k_new, v_new: (device)
+ * [total_q][num_kv_heads][head_dim]; cu_q_lens: (device) int32 [batch+1], non-decreasing,
+ * cu_q_lens[0] = 0, cu_q_lens[batch] = total_q; prefix_lens: (device) int32 [batch] >= 0;
+ * block_tables: (device) int32 [batch][block_table_stride] with
+ * block_table_stride >= ceil(max_prefix_len/16).  max_q_len >= every chunk length and
+ * max_prefix_len >= every prefix length (host bounds used for the launch grid; a
+ * larger value only costs idle work-groups).  Only pool entries of the prefix are read,
+ * so kvb_write_kv of the same chunk may run before or after this call.
+ * workspace: (device) at least kvb_paged_prefill_workspace_size(...) bytes (may be NULL
+ * when that size is 0). */
+kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
+                             const void* v_new, void* out, const int32_t* cu_q_lens,
+                             const int32_t* prefix_lens, const int32_t* block_tables,
+                             int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                             int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged decode: one query per sequence over its whole context, which is already in the
+ * pool (kvstream 0.1.0, "Request lifecycle" step 2; kvboost 0.6.0, "CPU paged attention":
+ * only the decode loop changes).  The query of sequence b sits at position
+ * context_lens[b]-1 and sees keys 0..context_lens[b]-1 through its block table.  The work
+ * is split over groups of split_blocks blocks whose partial results (unnormalised output,
+ * running max, sum) are merged by log-sum-exp; split_blocks == 0 picks a size from the
+ * host bounds.  A context length <= 0 gives a zero output row.
+ * q, out: (device) [batch][num_q_heads][head_dim]; context_lens: (device) int32 [batch]
+ * <= max_context_len; block_tables: (device) int32 [batch][block_table_stride] with
+ * block_table_stride >= ceil(max_context_len/16).
+ * workspace: (device) at least kvb_paged_decode_workspace_size(...) bytes for the same
+ * batch, num_q_heads, head_dim, max_context_len and split_blocks. */
+kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
+                            const int32_t* context_lens, const int32_t* block_tables,
+                            int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                            int32_t max_context_len, int32_t split_blocks, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes in bytes (0 = none needed).  Pure host arithmetic. */
+size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t total_q, int32_t max_prefix_len);
+size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t max_context_len,
+                                       int32_t split_blocks);
+
+/* Test helper: gather through the block tables into a contiguous layout, bit-exact.
+ * For b < batch, j < seq_lens[b]:
+ *   k_out[cu_seq_lens[b] + j][h][:] = pool.k[block_tables[b*stride + j/16]][h][j%16][:]
+ * (same for v).  k_out, v_out: (device) [cu_seq_lens[batch]][num_kv_heads][head_dim];
+ * seq_lens, cu_seq_lens: (device) int32; max_len >= every seq_lens[b].  Rows of keys in
+ * blocks outside the pool are left untouched. */
+kvb_status kvb_gather_kv(const kvb_pool* pool, const int32_t* block_tables,
+                         int32_t block_table_stride, const int32_t* seq_lens,
+                         const int32_t* cu_seq_lens, void* k_out, void* v_out, int32_t batch,
+                         int32_t max_len, void* stream);
+
+/* Static string for a status code. */
+const char* kvb_status_str(kvb_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char* kvb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVB_H */

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every symbol include/kvb.h declares, and rejects bad
+arguments on the host before any HIP call.  CPU only: the fake device pointers used
+here are never dereferenced because validation fails first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_paged_prefix_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libkvb.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+OK, NULL, INVALID, UNSUP, WS = 0, 1, 2, 3, 4
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvb_[a-z_0-9]+)\s*\(", text)))
+
+
+def pool(**kw):
+    p = dict(k=FAKE, v=FAKE + 4096, block_stride=2 * 16 * 128, num_blocks=8, block_size=16,
+             num_kv_heads=2, head_dim=128, dtype=_lib.KVB_BF16)
+    p.update(kw)
+    return _lib.KvbPool(**p)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.kvb_status_str(0) == b"ok"
+    assert lib.kvb_status_str(4).startswith(b"workspace")
+    assert lib.kvb_version() == b"0.1.0"
+
+
+def write(lib, p, n=4, kn=FAKE, vn=FAKE, slots=FAKE):
+    return lib.kvb_write_kv(ctypes.byref(p), kn, vn, slots, n, None)
+
+
+def test_write_kv_validation(lib):
+    assert lib.kvb_write_kv(None, FAKE, FAKE, FAKE, 4, None) == NULL
+    assert write(lib, pool(k=None)) == NULL
+    assert write(lib, pool(block_size=32)) == UNSUP
+    assert write(lib, pool(head_dim=80)) == UNSUP
+    assert write(lib, pool(dtype=7)) == UNSUP
+    assert write(lib, pool(block_stride=100)) == INVALID
+    assert write(lib, pool(block_stride=2 * 16 * 128 + 4)) == INVALID
+    assert write(lib, pool(num_kv_heads=0)) == INVALID
+    assert write(lib, pool(k=FAKE + 2)) == INVALID
+    assert write(lib, pool(), n=-1) == INVALID
+    assert write(lib, pool(), kn=None) == NULL
+    assert write(lib, pool(), kn=FAKE + 8) == INVALID
+    assert write(lib, pool(), slots=FAKE + 4) == INVALID
+    assert write(lib, pool(), n=0) == OK          # nothing to do, no HIP call
+
+
+def prefill(lib, p, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, cu=FAKE, pl=FAKE, bt=FAKE, stride=4, batch=2,
+             hq=4, total=10, maxq=6, maxp=64, scale=0.1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kvb_paged_prefill(ctypes.byref(p), a["q"], a["kn"], a["vn"], a["out"], a["cu"],
+                                 a["pl"], a["bt"], a["stride"], a["batch"], a["hq"], a["total"],
+                                 a["maxq"], a["maxp"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation(lib):
+    p = pool()
+    assert prefill(lib, p, hq=3) == INVALID           # not a multiple of num_kv_heads
+    assert prefill(lib, p, hq=0) == INVALID
+    assert prefill(lib, p, batch=-1) == INVALID
+    assert prefill(lib, p, scale=float("nan")) == INVALID
+    assert prefill(lib, p, scale=-1.0) == INVALID
+    assert prefill(lib, p, q=None) == NULL
+    assert prefill(lib, p, bt=None) == NULL
+    assert prefill(lib, p, out=FAKE + 2) == INVALID
+    assert prefill(lib, p, cu=FAKE + 2) == INVALID
+    assert prefill(lib, p, maxq=11) == INVALID        # longer than total_q
+    assert prefill(lib, p, stride=3) == INVALID       # ceil(64/16) = 4 entries needed
+    assert prefill(lib, pool(head_dim=256)) == UNSUP
+    assert prefill(lib, p, batch=0) == OK
+    assert prefill(lib, p, total=0, maxq=0) == OK
+
+
+def decode(lib, p, **kw):
+    a = dict(q=FAKE, out=FAKE, ctx=FAKE, bt=FAKE, stride=256, batch=4, hq=8, maxc=4000, sb=0,
+             scale=0.1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kvb_paged_decode(ctypes.byref(p), a["q"], a["out"], a["ctx"], a["bt"], a["stride"],
+                                a["batch"], a["hq"], a["maxc"], a["sb"], a["scale"], a["ws"],
+                                a["wsb"], None)
+
+
+def test_decode_validation_and_workspace(lib):
+    p = pool()
+    need = lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 0)
+    assert need > 0
+    assert decode(lib, p) == WS                       # split decode needs a workspace
+    assert decode(lib, p, ws=FAKE, wsb=need - 1) == WS
+    assert decode(lib, p, ws=FAKE + 8, wsb=need) == INVALID
+    assert decode(lib, p, stride=249) == INVALID      # ceil(4000/16) = 250 entries needed
+    assert decode(lib, p, hq=5) == INVALID
+    assert decode(lib, p, sb=-2) == INVALID
+    assert decode(lib, p, q=None) == NULL
+    assert decode(lib, p, ctx=FAKE + 1) == INVALID
+    assert decode(lib, p, batch=0) == OK
+    # a split size covering the whole context needs no workspace
+    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256) == 0
+    # forced split sizes: (ceil(250/16) splits) x rows x (d + 2) floats
+    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 16 * 4 * 8 * (128 + 2) * 4
+
+
+def test_prefill_workspace_is_zero(lib):
+    assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 0
+
+
+def test_gather_validation(lib):
+    p = pool()
+    assert lib.kvb_gather_kv(ctypes.byref(p), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 2, 17, None) == INVALID
+    assert lib.kvb_gather_kv(ctypes.byref(p), None, 2, FAKE, FAKE, FAKE, FAKE, 2, 17, None) == NULL
+    assert lib.kvb_gather_kv(ctypes.byref(p), FAKE, 2, FAKE, FAKE, FAKE, FAKE, 0, 17, None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bit-exact for slot scatter and block-table gather; max abs error <= 1e-2 (fp16) /
+2e-2 (bf16) for attention outputs on N(0,1) inputs."""
+import numpy as np
+import pytest
+
+from workloads import make_custom, make_config
+from workloads.gen import NAN_BITS
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _util():
+    import gpu_util
+    return gpu_util
+
+
+# ------------------------------------------------------------------ scatter / gather
+
+@pytest.mark.parametrize("dt,d,hkv", [("bf16", 128, 8), ("fp16", 96, 2), ("bf16", 64, 1)])
+@pytest.mark.parametrize("layout", ["split", "interleaved"])
+def test_write_kv_bit_exact(dt, d, hkv, layout):
+    import oracle
+    u = _util()
+    w = make_custom(101, dt, hkv * 2, hkv, d, [37, 0, 16, 5], [20, 33, 1, 11], poison=True)
+    slots = w.slot_mapping.copy()
+    slots[3] = -1
+    slots[7] = -5
+    dev = u.Dev(w, layout)
+    dev.slots = u.idev(slots, torch.int64)
+    import attention_paged_prefix_amd as kvb
+    kvb.write_kv(dev.pool, dev.k_new, dev.v_new, dev.slots)
+    torch.cuda.synchronize()
+    ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, slots)
+    if layout == "interleaved":
+        got = u.to_bits(dev.kv)
+        gk, gv = got[:, 0], got[:, 1]
+    else:
+        gk, gv = u.to_bits(dev.k), u.to_bits(dev.v)
+    assert np.array_equal(gk, ek)      # NaN payloads compare as bits
+    assert np.array_equal(gv, ev)
+
+
+def test_gather_bit_exact_under_permutation():
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    w = make_custom(102, "bf16", 8, 4, 128, [70, 0, 16, 129, 3], kind="decode", poison=True)
+    dev = u.Dev(w)
+    lens = w.context_lens
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    n = int(cu[-1])
+    ko = torch.zeros((n, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    vo = torch.zeros_like(ko)
+    kvb.gather_kv(dev.pool, dev.bt, dev.ctx, u.idev(cu), int(lens.max()), ko, vo)
+    torch.cuda.synchronize()
+    import oracle
+    for b in range(len(lens)):
+        ek = oracle.gather_kv(w.k_pool, w.block_tables[b], int(lens[b]))
+        ev = oracle.gather_kv(w.v_pool, w.block_tables[b], int(lens[b]))
+        assert np.array_equal(u.to_bits(ko[cu[b]:cu[b + 1]]), ek)
+        assert np.array_equal(u.to_bits(vo[cu[b]:cu[b + 1]]), ev)
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    # seed, dtype, Hq, Hkv, d, prefix lens, chunk lens, sharing
+    (201, "fp16", 1, 1, 64, [32], [16], "none"),               # tiny shape
+    (202, "bf16", 16, 2, 128, [192] * 3, [40, 77, 130], "all"),  # shared prefix, G=8
+    (203, "fp16", 40, 8, 128, [300, 64], [70, 129], "none"),  # G=5, ragged tails
+    (204, "fp16", 32, 8, 96, [0, 17, 255, 1000], [1, 63, 65, 200], "pairs"),
+    (205, "bf16", 32, 8, 64, [5, 400, 0, 48], [300, 15, 129, 2], "pairs"),
+    (206, "bf16", 4, 4, 128, [0, 0], [200, 3], "none"),        # MHA, no prefix
+    (207, "fp16", 8, 1, 64, [1, 15, 16, 17], [7, 9, 16, 31], "none"),  # MQA, block edges
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
+def test_prefill_matches_oracle(case):
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
+    dev = u.Dev(w)
+    out = dev.prefill()
+    torch.cuda.synchronize()
+    got = u.to_bits(out)
+    ref = u.oracle_prefill(w)
+    import oracle
+    assert np.isfinite(oracle.decode_bits(got, dt)).all()
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+def test_prefill_tiny_config_and_row0_bit_exact():
+    u = _util()
+    w = make_config("tiny", poison=True)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.prefill())
+    ref = u.oracle_prefill(w)
+    assert u.max_err(got, ref, "fp16") <= 1e-2
+    # P = 0 chunk: row 0 sees only itself -> exactly v_new[0]
+    w0 = make_custom(208, "bf16", 8, 2, 128, [0, 0], [50, 1], poison=True)
+    d0 = u.Dev(w0)
+    g0 = u.to_bits(d0.prefill())
+    for h in range(8):
+        assert np.array_equal(g0[0, h], w0.v_new[0, h // 4])
+        assert np.array_equal(g0[50, h], w0.v_new[50, h // 4])
+
+
+def test_prefill_deterministic_and_permutation_invariant():
+    u = _util()
+    w = make_custom(209, "bf16", 16, 4, 128, [333, 64, 0], [100, 65, 31], poison=True)
+    dev = u.Dev(w)
+    a = u.to_bits(dev.prefill())
+    b = u.to_bits(dev.prefill())
+    assert np.array_equal(a, b)
+    # permute physical blocks, remap the tables: bitwise identical outputs
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(w.num_blocks)
+    kp = np.empty_like(w.k_pool); kp[perm] = w.k_pool
+    vp = np.empty_like(w.v_pool); vp[perm] = w.v_pool
+    w.k_pool, w.v_pool = kp, vp
+    w.block_tables = perm[w.block_tables].astype(np.int32)
+    c = u.to_bits(u.Dev(w).prefill())
+    assert np.array_equal(a, c)
+
+
+def test_prefill_untouched_canaries():
+    u = _util()
+    w = make_custom(210, "fp16", 8, 2, 64, [40, 7], [9, 30], poison=True)
+    dev = u.Dev(w)
+    T = w.total_q
+    buf = torch.full((T + 4, 8, 64), 7.0, dtype=torch.float16, device="cuda:0")
+    dev.prefill(out=buf[:T])
+    torch.cuda.synchronize()
+    tail = buf[T:].float().cpu().numpy()
+    assert (tail == 7.0).all()
+
+
+# ------------------------------------------------------------------ decode
+
+DECODE_CASES = [
+    (301, "bf16", 32, 8, 128, [517, 1, 16, 17, 4001, 2048]),
+    (302, "fp16", 8, 8, 64, [3, 64, 100]),
+    (303, "fp16", 40, 8, 96, [1000, 33]),
+    (304, "bf16", 16, 2, 128, [300, 2000, 15]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+@pytest.mark.parametrize("split", [0, 1, 4, 7])
+def test_decode_matches_oracle(case, split):
+    u = _util()
+    seed, dt, hq, hkv, d, ctx = case
+    w = make_custom(seed, dt, hq, hkv, d, ctx, kind="decode", share="all", poison=True)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.decode(split_blocks=split))
+    ref = u.oracle_decode(w)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+def test_decode_zero_context_gives_zero_row():
+    u = _util()
+    w = make_custom(305, "bf16", 8, 2, 128, [40, 5], kind="decode", poison=True)
+    w.context_lens = np.array([40, 0], np.int32)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.decode())
+    assert (got[1] == 0).all()
+    ref = u.oracle_decode(w)
+    assert u.max_err(got[:1], ref[:1], "bf16") <= 2e-2
+
+
+def test_decode_equals_one_row_prefill_within_tolerance():
+    u = _util()
+    w = make_custom(306, "fp16", 8, 2, 128, [77, 300], kind="decode", poison=True)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.decode(split_blocks=2))
+    ref = u.oracle_decode(w)
+    assert u.max_err(got, ref, "fp16") <= 1e-2
+    a = u.to_bits(dev.decode(split_blocks=2))
+    assert np.array_equal(a, got)          # run-to-run deterministic
