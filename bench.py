@@ -1,0 +1,366 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged prefix-reuse attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch:
+  kvb_write_kv (the chunk's K/V into its pool slots) -> kvb_paged_prefill (chunk over the
+  cached prefix + causal self part) -> kvb_write_kv (one decode token per sequence) ->
+  kvb_paged_decode (one query per sequence over its whole context).
+Default workload: 8 sequences sharing one 2048-token prefix (128 blocks), 256-token
+chunks, 16 query / 2 KV heads, head_dim 128, bf16, pool of 8192 16-token blocks.
+
+Prints ONE JSON line.  `value` is algorithmic TFLOP/s of the whole step (prefill plus
+decode attention FLOPs over the measured step time) with every input resident in HBM.
+The same run also times the paged-decode workload (64 sequences, contexts 512..4096,
+first 1024 tokens shared, 32/8 heads, d=128, bf16) and reports its KV GB/s.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config shared_prompt]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-prefill TFLOP/s & decode KV GB/s on 1 MI355X, % of MFMA/HBM peak"
+PEAK_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
+PEAK_GBPS = 8000.0       # MI355X HBM3E, published
+ESZ = 2
+
+
+# ----------------------------------------------------------------- algorithmic counts
+
+def prefill_flops(w) -> float:
+    """4*d per visible (query row, key, q-head) pair: QK^T and PV, 2 flops per MAC."""
+    C = w.q_lens.astype(np.float64)
+    P = w.prefix_lens.astype(np.float64)
+    pairs = w.num_q_heads * np.sum(C * P + C * (C + 1) / 2)
+    return 4.0 * w.head_dim * pairs
+
+
+def decode_flops(ctx, w) -> float:
+    return 4.0 * w.head_dim * w.num_q_heads * float(np.sum(ctx))
+
+
+def unique_kv_tokens(tables, lens) -> int:
+    """Tokens of distinct physical blocks touched (a shared block counts once)."""
+    best = {}
+    for b, n in enumerate(lens):
+        n = int(n)
+        for j in range((n + 15) // 16):
+            pb = int(tables[b][j])
+            best[pb] = max(best.get(pb, 0), min(16, n - 16 * j))
+    return sum(best.values())
+
+
+def decode_bytes(w, ctx, tables) -> float:
+    B = len(ctx)
+    kv = unique_kv_tokens(tables, ctx) * w.num_kv_heads * w.head_dim * 2 * ESZ
+    qo = 2 * B * w.num_q_heads * w.head_dim * ESZ
+    tab = sum((int(n) + 15) // 16 for n in ctx) * 4 + B * 4
+    return float(kv + qo + tab)
+
+
+def prefill_bytes(w) -> float:
+    T = w.total_q
+    qo = 2 * T * w.num_q_heads * w.head_dim * ESZ
+    kvn = 2 * T * w.num_kv_heads * w.head_dim * ESZ
+    kvp = unique_kv_tokens(w.block_tables, w.prefix_lens) * w.num_kv_heads * w.head_dim * 2 * ESZ
+    tab = sum((int(p) + 15) // 16 for p in w.prefix_lens) * 4 + (2 * w.batch + 1) * 4
+    return float(qo + kvn + kvp + tab)
+
+
+def write_kv_bytes(T, w) -> float:
+    return float(2 * 2 * T * w.num_kv_heads * w.head_dim * ESZ + 8 * T)
+
+
+# ----------------------------------------------------------------- helpers
+
+def _dev_bits(torch, bits, dtype):
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(tdt)
+
+
+def _idev(torch, a, dt=None):
+    dt = dt or torch.int32
+    return torch.as_tensor(np.ascontiguousarray(a)).to(dt).to("cuda:0")
+
+
+def read_traffic(kernel_key: str):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = fields.get("source_file")
+    if not src:
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+    if sha != fields.get("source_sha256_16"):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the same prefill workload: (sequence, head)
+    pairs in order until the time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    done_flops = 0.0
+    pairs = 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        C = int(w.q_lens[b])
+        P = int(w.prefix_lens[b])
+        for h in range(w.num_q_heads):
+            oracle.paged_prefill(w.k_pool, w.v_pool, w.q, w.k_new, w.v_new, w.cu_q_lens,
+                                 w.prefix_lens, w.block_tables, w.num_q_heads, w.scale, w.dtype,
+                                 select=[(b, h, np.arange(C))])
+            done_flops += 4.0 * w.head_dim * (C * P + C * (C + 1) / 2)
+            pairs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"paged prefill of {pairs} of {w.batch * w.num_q_heads} (sequence, query head) "
+                      f"pairs of the same workload, fp64 NumPy, {dt:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="shared_prompt",
+                    choices=["shared_prompt", "long_prefix", "ragged_d96", "ragged_d64", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the separate decode workload")
+    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy"], default="step",
+                    help="profiling aid: time only one part")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by sequence and KV head but no multi-GPU run is provided.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    import attention_paged_prefix_amd as kvb
+    from workloads import make_config
+
+    if args.only == "copy":
+        # calibration kernel for the HBM counters: a plain 1 GiB device copy
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+        bb = torch.empty_like(a)
+        for _ in range(args.steps):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 2, "copy_bytes_written": a.numel() * 2}))
+        return 0
+
+    w = make_config(args.config, with_decode=True)
+    dt = w.dtype
+    k = _dev_bits(torch, w.k_pool, dt)
+    v = _dev_bits(torch, w.v_pool, dt)
+    pool = kvb.Pool.from_tensors(k, v)
+    q = _dev_bits(torch, w.q, dt)
+    kn = _dev_bits(torch, w.k_new, dt)
+    vn = _dev_bits(torch, w.v_new, dt)
+    cu = _idev(torch, w.cu_q_lens)
+    pl = _idev(torch, w.prefix_lens)
+    bt = _idev(torch, w.block_tables)
+    slots = _idev(torch, w.slot_mapping, torch.int64)
+    dq = _dev_bits(torch, w.dec_q, dt)
+    dk = _dev_bits(torch, w.dec_k, dt)
+    dv = _dev_bits(torch, w.dec_v, dt)
+    dslots = _idev(torch, w.dec_slots, torch.int64)
+    dctx = _idev(torch, w.dec_context_lens)
+    out = torch.empty_like(q)
+    dout = torch.empty_like(dq)
+    max_q, max_p = int(w.q_lens.max()), int(w.prefix_lens.max())
+    max_ctx = int(w.dec_context_lens.max())
+    dws_n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx)
+    dws = torch.empty(max(dws_n, 16), dtype=torch.uint8, device="cuda:0")
+    T = w.total_q
+
+    def part(name):
+        if name == "write_kv":
+            kvb.write_kv(pool, kn, vn, slots)
+        elif name == "prefill":
+            kvb.paged_prefill(pool, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out)
+        elif name == "write_kv_dec":
+            kvb.write_kv(pool, dk, dv, dslots)
+        elif name == "decode":
+            kvb.paged_decode(pool, dq, dctx, bt, w.scale, max_ctx, out=dout, workspace=dws)
+
+    parts = ["write_kv", "prefill", "write_kv_dec", "decode"]
+    if args.only in ("prefill", "decode", "write_kv"):
+        parts = [args.only] if args.only != "decode" else ["write_kv", "write_kv_dec", "decode"]
+        if args.only == "decode":
+            for p_ in parts[:2]:
+                part(p_)
+            parts = ["decode"]
+
+    for _ in range(args.warmup):
+        for p_ in parts:
+            part(p_)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, p_ in enumerate(parts):
+            part(p_)
+            ev[s][i + 1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_part = {p_: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, p_ in enumerate(parts)}
+    ms_step = total_ms / args.steps
+
+    pf = prefill_flops(w)
+    df = decode_flops(w.dec_context_lens, w)
+    step_flops = (pf if "prefill" in parts else 0.0) + (df if "decode" in parts else 0.0)
+    kernels = {}
+    if "prefill" in per_part:
+        t = per_part["prefill"] * 1e-3
+        kernels["paged_prefill"] = {"ms": per_part["prefill"], "tflops": pf / t / 1e12,
+                                    "gbps": prefill_bytes(w) / t / 1e9,
+                                    "frac_mfma_peak": pf / t / 1e12 / PEAK_TFLOPS}
+    if "decode" in per_part:
+        t = per_part["decode"] * 1e-3
+        db = decode_bytes(w, w.dec_context_lens, w.block_tables)
+        kernels["paged_decode"] = {"ms": per_part["decode"], "gbps": db / t / 1e9,
+                                   "frac_hbm_peak": db / t / 1e9 / PEAK_GBPS}
+    for nm, cnt in (("write_kv", T), ("write_kv_dec", w.batch)):
+        if nm in per_part:
+            kernels[nm] = {"ms": per_part[nm], "gbps": write_kv_bytes(cnt, w) / (per_part[nm] * 1e-3) / 1e9}
+
+    res = {
+        "metric": METRIC,
+        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": {"shared_prompt": "shared-system-prompt paged prefill + decode step",
+                                "long_prefix": "long-prefix paged prefill + decode step",
+                                "ragged_d96": "ragged multi-turn mix d96 prefill + decode step",
+                                "ragged_d64": "ragged multi-turn mix d64 prefill + decode step",
+                                "tiny": "tiny paged prefill + decode step"}[args.config],
+                   "batch": w.batch, "prefix_tokens": int(w.prefix_lens.sum()),
+                   "chunk_tokens": int(w.q_lens.sum()), "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "num_blocks": w.num_blocks, "seed": w.seed, "parallelism": "single GPU"},
+        "kernels": kernels,
+    }
+    if "prefill" in per_part:
+        ach = kernels["paged_prefill"]["tflops"]
+        res["roofline"] = {"bound": "mfma", "kernel": "paged_prefill", "achieved": ach,
+                           "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_TFLOPS,
+                           "traffic": read_traffic(f"paged_prefill_{args.config}"),
+                           "algorithmic_flops_per_launch": pf,
+                           "algorithmic_bytes_per_launch": prefill_bytes(w)}
+
+    if not args.no_decode and args.only == "step":
+        res["decode_workload"] = bench_decode(torch, kvb, args)
+
+    if not args.no_cpu_baseline and args.only == "step":
+        res["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(res))
+    return 0
+
+
+def bench_decode(torch, kvb, args):
+    """The paged-decode workload: 64 sequences, contexts U{512..4096} (seed 3), first 1024
+    tokens shared, 32/8 heads, d=128, bf16, pool of 16384 blocks."""
+    from workloads import make_config
+    w = make_config("decode")
+    k = _dev_bits(torch, w.k_pool, w.dtype)
+    v = _dev_bits(torch, w.v_pool, w.dtype)
+    pool = kvb.Pool.from_tensors(k, v)
+    q = _dev_bits(torch, w.q, w.dtype)
+    ctx = _idev(torch, w.context_lens)
+    bt = _idev(torch, w.block_tables)
+    out = torch.empty_like(q)
+    max_ctx = int(w.context_lens.max())
+    n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+
+    def run():
+        kvb.paged_decode(pool, q, ctx, bt, w.scale, max_ctx, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 10)
+    warm, cold = [], []
+    for _ in range(steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(); run(); b.record()
+        warm.append((a, b))
+    for _ in range(steps):
+        flush.fill_(1)          # evict L2 / Infinity Cache between launches (outside the events)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(); run(); b.record()
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    tw = float(np.mean([a.elapsed_time(b) for a, b in warm]))
+    tc = float(np.mean([a.elapsed_time(b) for a, b in cold]))
+    by = decode_bytes(w, w.context_lens, w.block_tables)
+    logical = float(np.sum(w.context_lens)) * w.num_kv_heads * w.head_dim * 2 * ESZ
+    return {"workload": "paged decode, 64 sequences, contexts 512..4096, first 1024 tokens shared",
+            "algorithmic_bytes": by, "ms_back_to_back": tw, "ms_cold_cache": tc,
+            "gbps_back_to_back": by / (tw * 1e-3) / 1e9, "gbps_cold_cache": by / (tc * 1e-3) / 1e9,
+            "frac_hbm_peak_cold": by / (tc * 1e-3) / 1e9 / PEAK_GBPS,
+            "logical_kv_gbps_cold": logical / (tc * 1e-3) / 1e9,
+            "tflops_cold": decode_flops(w.context_lens, w) / (tc * 1e-3) / 1e12}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -135,11 +135,11 @@ def paged_prefill(k_pool, v_pool, q, k_new, v_new, cu_q_lens, prefix_lens, block
             g = h // G
             C = int(cu[b + 1] - cu[b])
             K, V = _sequence_kv(k_pool, v_pool, block_tables[b], int(P[b]),
-                                k_new[cu[b]:cu[b + 1], g:g + 1], v_new[cu[b]:cu[b + 1], g:g + 1], dtype)
+                                k_new[cu[b]:cu[b + 1]], v_new[cu[b]:cu[b + 1]], dtype)
             rows = np.asarray(rows, dtype=np.int64)
             assert np.all(rows < C)
             qr = decode_bits(q[cu[b] + rows, h], dtype)
-            o, lse = attend(qr, K[:, 0], V[:, 0], P[b] + rows, scale)
+            o, lse = attend(qr, K[:, g], V[:, g], P[b] + rows, scale)
             res[(b, h)] = (o, lse) if want_lse else o
         return res
     out = np.zeros((T, num_q_heads, d), dtype=np.float64)

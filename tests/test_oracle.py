@@ -344,3 +344,17 @@ def test_write_kv_matches_slot_semantics():
     # the skipped token's would-be slot is untouched
     s4 = int(w.slot_mapping[4])
     assert np.array_equal(kp[s4 // 16, :, s4 % 16], w.k_pool[s4 // 16, :, s4 % 16])
+
+
+def test_selected_rows_equal_full_result():
+    w = make_custom(42, "bf16", 8, 2, 32, [40, 0, 17], [9, 12, 3])
+    full = _prefill(w)
+    sel = [(0, 3, [0, 4, 8]), (1, 7, list(range(12))), (2, 0, [2])]
+    got = _prefill(w, select=sel)
+    for b, h, rows in sel:
+        np.testing.assert_allclose(got[(b, h)], full[w.cu_q_lens[b] + np.array(rows), h], rtol=0, atol=1e-14)
+    dec = make_custom(43, "fp16", 4, 2, 16, [33, 5, 70], kind="decode")
+    a = oracle.paged_decode(dec.k_pool, dec.v_pool, dec.q, dec.context_lens, dec.block_tables, dec.scale, "fp16")
+    b_ = oracle.paged_decode(dec.k_pool, dec.v_pool, dec.q, dec.context_lens, dec.block_tables, dec.scale, "fp16",
+                             seqs=[2])
+    np.testing.assert_allclose(a[2], b_[2], rtol=0, atol=1e-14)
