@@ -5,19 +5,24 @@
 // paged attention": only the decode loop changes; kvstream 0.1.0, "Request lifecycle"
 // step 2: one slot per generated token, so the current token is already in the pool).
 //
-// Design (HBM-bound: about G flops per byte of K/V):
-//  * One work-group (4 waves) per (sequence, KV head, head chunk of up to GC query
-//    heads, split of `split_blocks` blocks).  All GC heads of a KV group read each K/V
-//    block once.
-//  * A wave consumes one 16-token block per step.  Lane l owns key row l/4 of the block
-//    and the 16-byte chunks {l%4 + 4j} of that row: every load instruction of the wave
-//    reads 16 rows x 64 contiguous bytes, and the q.k partial sums reduce over the 4
-//    lanes of a quad with two DPP moves.
-//  * Each lane keeps its own online-softmax state (max, sum, unnormalised output) over
-//    the key rows it sees, with lazy rescaling: the reference max only moves when a
-//    score exceeds it by more than 2^8 in the exp2 domain, so exponentials stay <= 256
-//    and the rescale multiply is rarely taken.  The state of the 64 key slots of the
-//    work-group is merged once at the end of the split (the same log-sum-exp identity).
+// Design (HBM-bound: about G flops per byte of K/V, so the aim is bytes in flight and
+// few instructions per byte):
+//  * One work-group (4 waves) per (sequence, KV head, head chunk of up to 16 query
+//    heads, split of `split_blocks` blocks).  The query heads of one KV group share
+//    every K/V byte read.
+//  * A wave consumes two 16-token blocks (32 keys) per step and has the next step's
+//    K/V loads in flight while it works on the current one.
+//  * Scores S^T = K Q^T use v_mfma_f32_16x16x32 with K loaded straight from the pool
+//    into A-operand registers (each load instruction reads 64 contiguous bytes from
+//    each of the 16 rows of a block) and the queries as the B operand (columns beyond
+//    the group are zero).
+//  * O^T += V^T P^T also uses 16x16x32: the score accumulators already hold P^T in
+//    B-operand layout; V is written to a per-wave LDS slot in its natural row-major
+//    layout (fully coalesced 1 KiB loads) and read back transposed with
+//    ds_read_b64_tr_b16.
+//  * Online softmax in the exp2 domain with lazy rescaling: the reference max only
+//    moves when a score exceeds it by more than 2^8, so exponentials stay <= 256 and
+//    the output rescale is rarely executed.
 //  * A split covering the whole context writes the normalised output directly; other
 //    splits write (output, max, sum) partials that decode_merge combines.
 #include "kvb_device.h"
@@ -28,44 +33,57 @@ namespace kvb {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kMaxSplitBlocks = 256;
+constexpr int kDecHeads = 16;               // query heads per work-group (MFMA N)
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegBig = -1.0e30f;
 
-template <int D> struct KVRegs {
-  static constexpr int NJ = D / 32;         // 16-byte chunks per lane per K (or V) row
-  uint4 k[NJ];
-  uint4 v[NJ];
+template <int D> struct DecStep {
+  static constexpr int NKK = D / 32;        // QK MFMAs per block
+  static constexpr int VCH = D / 32;        // 16-byte V chunks per lane per block
+  uint4 k[2][NKK];
+  uint4 v[2][VCH];
 };
 
-template <typename T, int D, int GC>
-__global__ void __launch_bounds__(kDecThreads)
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecThreads, 2)
 decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                     int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
                     uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens,
                     const int32_t* __restrict__ bt, int bt_stride, int hq, int hkv, int nchunks,
                     int split_blocks, int nsplit, int max_ctx, float c_log2,
                     float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real) {
-  constexpr int NJ = D / 32;
+  constexpr int NKK = D / 32;
+  constexpr int NDB = D / 16;               // 16-row d blocks of O^T
+  constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+  constexpr int VCH = D / 32;
+  constexpr int VROW = D + 16;              // LDS row stride (elements): 8 banks apart per row
+  constexpr int SLOT = 32 * VROW;           // two blocks per wave
+
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kDecWaves * SLOT];
+  __shared__ int s_bt[kMaxSplitBlocks];
+  __shared__ float s_m[kDecWaves][kDecHeads];
+  __shared__ float s_l[kDecWaves][kDecHeads];
+  static_assert(kDecWaves * kDecHeads * D * 4 <= kDecWaves * SLOT * 2, "merge buffer reuses V slots");
+  float* s_o = reinterpret_cast<float*>(sV);  // [wave][head][D] after the main loop
+
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
-  // logical id -> (b, kvh, split, chunk), chunk fastest
   int r = lid;
   const int chunk = r % nchunks; r /= nchunks;
   const int split = r % nsplit; r /= nsplit;
   const int kvh = r % hkv;
   const int b = r / hkv;
   const int G = hq / hkv;
-  const int h0 = kvh * G + chunk * GC;
-  const int nh = min(GC, G - chunk * GC);
+  const int h0 = kvh * G + chunk * kDecHeads;
+  const int nh = min(kDecHeads, G - chunk * kDecHeads);
 
   int n = ctx_lens[b];
   n = min(n, min(max_ctx, bt_stride * kBlock));
   const int tid = threadIdx.x;
   if (n <= 0) {
-    if (split == 0) {
+    if (split == 0)
       for (int e = tid; e < nh * D; e += kDecThreads)
         out[((int64_t)b * hq + h0 + e / D) * D + (e % D)] = 0;
-    }
     return;
   }
   const int nblk = (n + kBlock - 1) / kBlock;
@@ -74,176 +92,177 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   const int blk_end = min(nblk, blk_begin + split_blocks);
   const bool single = nblk <= split_blocks;
 
-  __shared__ int s_bt[kMaxSplitBlocks];
-  __shared__ float s_m[kDecWaves][GC];
-  __shared__ float s_l[kDecWaves][GC];
-  __shared__ float s_acc[kDecWaves][GC][D];
-
   for (int i = tid; i < blk_end - blk_begin; i += kDecThreads) {
-    int pb = bt[(int64_t)b * bt_stride + blk_begin + i];
+    const int pb = bt[(int64_t)b * bt_stride + blk_begin + i];
     s_bt[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
   }
 
   const int lane = tid & 63, w = tid >> 6;
-  const int ks = lane >> 2;          // key row within a block
-  const int qd = lane & 3;           // chunk phase
+  const int c16 = lane & 15, g4 = lane >> 4;
 
-  // query chunks, packed 16-bit pairs
-  uint4 qv[GC][NJ];
+  // queries as the B operand: column c16 (head h0 + c16), d chunk 4*kk + g4
+  s16x8 qb[NKK];
 #pragma unroll
-  for (int h = 0; h < GC; ++h)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (h < nh)
-        qv[h][j] = *reinterpret_cast<const uint4*>(q + ((int64_t)b * hq + h0 + h) * D + 8 * (qd + 4 * j));
-      else
-        qv[h][j] = make_uint4(0, 0, 0, 0);
-    }
-
-  float m[GC], l[GC], acc[GC][NJ * 8];
-#pragma unroll
-  for (int h = 0; h < GC; ++h) {
-    m[h] = kNegBig;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < NJ * 8; ++e) acc[h][e] = 0.f;
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (c16 < nh)
+      qb[kk] = *reinterpret_cast<const s16x8*>(q + ((int64_t)b * hq + h0 + c16) * D + 8 * (4 * kk + g4));
+    else
+      qb[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
+
+  f32x4 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
   __syncthreads();
 
-  const int64_t head_off = (int64_t)(kvh * kBlock + ks) * D;
-  auto load = [&](int blk, KVRegs<D>& R) {
-    const int pb = s_bt[blk - blk_begin];
-    if (pb >= 0) {
-      const int64_t base = (int64_t)pb * block_stride + head_off;
+  const int64_t head_off = (int64_t)kvh * kBlock * D;
+  uint16_t* slot = sV + w * SLOT;
+
+  auto load = [&](int blk0, DecStep<D>& R) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        R.k[j] = *reinterpret_cast<const uint4*>(kp + base + 8 * (qd + 4 * j));
-        R.v[j] = *reinterpret_cast<const uint4*>(vp + base + 8 * (qd + 4 * j));
+    for (int hb = 0; hb < 2; ++hb) {
+      const int blk = blk0 + hb;
+      const int pb = blk < blk_end ? s_bt[blk - blk_begin] : -1;
+      if (pb >= 0) {
+        const uint16_t* kb = kp + (int64_t)pb * block_stride + head_off;
+        const uint16_t* vb = vp + (int64_t)pb * block_stride + head_off;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          R.k[hb][kk] = *reinterpret_cast<const uint4*>(kb + c16 * D + 8 * (4 * kk + g4));
+#pragma unroll
+        for (int j = 0; j < VCH; ++j)
+          R.v[hb][j] = *reinterpret_cast<const uint4*>(vb + 8 * (j * 64 + lane));
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) R.k[hb][kk] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) R.v[hb][j] = make_uint4(0, 0, 0, 0);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) { R.k[j] = make_uint4(0, 0, 0, 0); R.v[j] = make_uint4(0, 0, 0, 0); }
     }
   };
 
-  auto step = [&](int blk, const KVRegs<D>& R) {
-    const bool kvalid = (s_bt[blk - blk_begin] >= 0) && (blk * kBlock + ks < n);
-    float t[GC];
+  auto step = [&](int blk0, const DecStep<D>& R) {
+    // V of both blocks into this wave's LDS slot, natural [key][d] layout.  Rows past
+    // the context are zeroed: their probability is 0 but the pool may hold NaN there.
 #pragma unroll
-    for (int h = 0; h < GC; ++h) {
-      float s = 0.f;
+    for (int hb = 0; hb < 2; ++hb) {
+      const int kbase = (blk0 + hb) * kBlock;
+      const bool partial = kbase + kBlock > n;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        s = T::dot2(R.k[j].x, qv[h][j].x, s);
-        s = T::dot2(R.k[j].y, qv[h][j].y, s);
-        s = T::dot2(R.k[j].z, qv[h][j].z, s);
-        s = T::dot2(R.k[j].w, qv[h][j].w, s);
-      }
-      s += quad_xor1(s);
-      s += quad_xor2(s);
-      t[h] = kvalid ? s * c_log2 : -INFINITY;
-    }
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < GC; ++h) need |= t[h] > m[h] + kRescaleThreshold;
-    if (__any(need)) {
-#pragma unroll
-      for (int h = 0; h < GC; ++h) {
-        const float mn = fmaxf(m[h], t[h]);
-        const float alpha = fast_exp2(m[h] - mn);
-        m[h] = mn;
-        l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < NJ * 8; ++e) acc[h][e] *= alpha;
+      for (int j = 0; j < VCH; ++j) {
+        const int c = j * 64 + lane;
+        const int row = c / CPR, col = c - (c / CPR) * CPR;
+        uint4 val = R.v[hb][j];
+        if (partial && kbase + row >= n) val = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 8) = val;
       }
     }
-    float p[GC];
+    // S^T = K Q^T per block
+    f32x4 s[2];
 #pragma unroll
-    for (int h = 0; h < GC; ++h) {
-      p[h] = fast_exp2(t[h] - m[h]);
-      l[h] += p[h];
+    for (int hb = 0; hb < 2; ++hb) {
+      s[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        s[hb] = T::mfma16(__builtin_bit_cast(s16x8, R.k[hb][kk]), qb[kk], s[hb]);
     }
-    float vf[NJ * 8];
+    // scale + mask: lane holds keys 4*g4 + rr of each block for head column c16
+    float t[8];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint32_t wv[4] = {R.v[j].x, R.v[j].y, R.v[j].z, R.v[j].w};
+    for (int hb = 0; hb < 2; ++hb) {
+      const int blk = blk0 + hb;
+      const bool bvalid = blk < blk_end && s_bt[blk - blk_begin] >= 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[j * 8 + 2 * e] = kvalid ? lo_f32<T>(wv[e]) : 0.f;
-        vf[j * 8 + 2 * e + 1] = kvalid ? hi_f32<T>(wv[e]) : 0.f;
+      for (int rr = 0; rr < 4; ++rr) {
+        const bool ok = bvalid && (blk * kBlock + 4 * g4 + rr < n);
+        const float tv = ok ? s[hb][rr] * c_log2 : -INFINITY;
+        t[hb * 4 + rr] = tv;
+        mx = fmaxf(mx, tv);
       }
     }
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    if (__any(mx > m_run + kRescaleThreshold)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
 #pragma unroll
-    for (int h = 0; h < GC; ++h)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < NJ * 8; ++e) acc[h][e] = fmaf(p[h], vf[e], acc[h][e]);
+        for (int rr = 0; rr < 4; ++rr) o[db][rr] *= alpha;
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(t[2 * e] - m_run);
+      const float p1 = fast_exp2(t[2 * e + 1] - m_run);
+      l_run += p0 + p1;
+      pw[e] = pack2<T>(p0, p1);
+    }
+    const s16x8 pb8 = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    __builtin_amdgcn_wave_barrier();
+    // O^T += V^T P^T: A operand rows d = 16*db + c16, keys 4*g4.. of block 0 then block 1
+    const int src_row = 4 * g4 + (c16 >> 2);
+    const int src_col = 4 * (c16 & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const s16x4 lo = lds_read_tr16(slot + src_row * VROW + 16 * db + src_col);
+      const s16x4 hi = lds_read_tr16(slot + (16 + src_row) * VROW + 16 * db + src_col);
+      const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = T::mfma16(a, pb8, o[db]);
+    }
+    __builtin_amdgcn_wave_barrier();
   };
 
-  // Software pipeline: the next block's loads are in flight while this one is used.
-  int blk = blk_begin + w;
-  if (blk < blk_end) {
-    KVRegs<D> cur;
-    load(blk, cur);
-    for (; blk < blk_end; blk += kDecWaves) {
-      KVRegs<D> nxt;
-      const bool more = blk + kDecWaves < blk_end;
-      if (more) load(blk + kDecWaves, nxt);
-      step(blk, cur);
+  // each wave takes every fourth pair of blocks; next pair's loads in flight
+  int blk0 = blk_begin + 2 * w;
+  if (blk0 < blk_end) {
+    DecStep<D> cur;
+    load(blk0, cur);
+    for (; blk0 < blk_end; blk0 += 2 * kDecWaves) {
+      DecStep<D> nxt;
+      const bool more = blk0 + 2 * kDecWaves < blk_end;
+      if (more) load(blk0 + 2 * kDecWaves, nxt);
+      step(blk0, cur);
       if (more) cur = nxt;
     }
   }
 
-  // Merge the 16 key slots of this wave (lanes with equal l%4): xor over 4, 8, 16, 32.
+  // row sums over the four key groups of the wave
+  float lsum = l_run;
+  lsum += xor_lane(lsum, 16);
+  lsum += xor_lane(lsum, 32);
+  __syncthreads();                          // V slots are reused as the merge buffer
+  if (c16 < nh) {
 #pragma unroll
-  for (int h = 0; h < GC; ++h) {
-    float M = m[h];
-    M = fmaxf(M, xor_lane(M, 4));
-    M = fmaxf(M, xor_lane(M, 8));
-    M = fmaxf(M, xor_lane(M, 16));
-    M = fmaxf(M, xor_lane(M, 32));
-    const float sc = fast_exp2(m[h] - M);
-    float lh = l[h] * sc;
-    lh += xor_lane(lh, 4);
-    lh += xor_lane(lh, 8);
-    lh += xor_lane(lh, 16);
-    lh += xor_lane(lh, 32);
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int e = 0; e < NJ * 8; ++e) {
-      float a = acc[h][e] * sc;
-      a += xor_lane(a, 4);
-      a += xor_lane(a, 8);
-      a += xor_lane(a, 16);
-      a += xor_lane(a, 32);
-      acc[h][e] = a;
-    }
-    if (lane < 4) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s_acc[w][h][8 * (qd + 4 * j) + e] = acc[h][j * 8 + e];
-      if (lane == 0) { s_m[w][h] = M; s_l[w][h] = lh; }
-    }
+      for (int rr = 0; rr < 4; ++rr)
+        s_o[(w * kDecHeads + c16) * D + 16 * db + 4 * g4 + rr] = o[db][rr];
+    if (g4 == 0) { s_m[w][c16] = m_run; s_l[w][c16] = lsum; }
   }
   __syncthreads();
 
-  // Merge the 4 waves and write.
   for (int e = tid; e < nh * D; e += kDecThreads) {
     const int h = e / D, d = e - h * D;
     float M = s_m[0][h];
 #pragma unroll
     for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-    float o = 0.f, L = 0.f;
+    float ov = 0.f, L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float sc = fast_exp2(s_m[ww][h] - M);
-      o = fmaf(sc, s_acc[ww][h][d], o);
+      ov = fmaf(sc, s_o[(ww * kDecHeads + h) * D + d], ov);
       L = fmaf(sc, s_l[ww][h], L);
     }
     const int64_t row = (int64_t)b * hq + h0 + h;
     if (single) {
-      out[row * D + d] = T::from_f32(o / L);
+      out[row * D + d] = T::from_f32(ov / L);
     } else {
-      ws_o[(row * nsplit + split) * D + d] = o;
+      ws_o[(row * nsplit + split) * D + d] = ov;
       if (d == 0) {
         ws_ml[(row * nsplit + split) * 2 + 0] = M;
         ws_ml[(row * nsplit + split) * 2 + 1] = L;
@@ -252,7 +271,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   }
 }
 
-// One work-group of D threads per (sequence, query head); only sequences whose
+// One work-group of 128 threads per (sequence, query head); only sequences whose
 // context spans more than one split have partials to combine.
 template <typename T, int D>
 __global__ void __launch_bounds__(128)
@@ -281,25 +300,23 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   out[(int64_t)row * D + d] = T::from_f32(o / L);
 }
 
-int decode_heads_per_wg(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
+int decode_heads_per_wg(int G) { return G < kDecHeads ? G : kDecHeads; }
 
 void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, int* split_blocks,
                  int* nsplit) {
   const int G = hq / hkv;
-  const int gc = decode_heads_per_wg(G);
-  const int nchunks = (G + gc - 1) / gc;
+  const int nchunks = (G + kDecHeads - 1) / kDecHeads;
   const int max_blocks = max_ctx > 0 ? (max_ctx + kBlock - 1) / kBlock : 1;
   int sb = split_blocks_req;
   if (sb <= 0) {
     // aim for >= 2048 work-groups (8 per CU) without splits shorter than 16 blocks
     const long long units = (long long)batch * hkv * nchunks;
-    long long want = (2048 + units - 1) / units;
-    long long ns = want < 1 ? 1 : want;
-    long long max_ns = (max_blocks + 15) / 16;
+    long long ns = (2048 + units - 1) / units;
+    const long long max_ns = (max_blocks + 15) / 16;
     if (ns > max_ns) ns = max_ns;
     if (ns < 1) ns = 1;
     sb = (int)((max_blocks + ns - 1) / ns);
-    sb = (sb + 3) & ~3;
+    sb = (sb + 7) & ~7;                  // whole steps for the four waves
   }
   if (sb > kMaxSplitBlocks) sb = kMaxSplitBlocks;
   if (sb < 1) sb = 1;
@@ -307,17 +324,18 @@ void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, 
   *nsplit = (max_blocks + sb - 1) / sb;
 }
 
-template <typename T, int D, int GC>
+template <typename T, int D>
 static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
                                   const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx,
                                   int sb, int ns, float scale, float* ws_o, float* ws_ml,
                                   hipStream_t s) {
   const int G = hq / p.num_kv_heads;
-  const int nchunks = (G + GC - 1) / GC;
+  const int nchunks = (G + kDecHeads - 1) / kDecHeads;
   const long long real = (long long)batch * p.num_kv_heads * ns * nchunks;
+  if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   const float c = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, GC>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                      nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real);
@@ -328,18 +346,6 @@ static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, c
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_decode_d(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
-                                  const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx,
-                                  int sb, int ns, float scale, float* ws_o, float* ws_ml,
-                                  hipStream_t s) {
-  switch (decode_heads_per_wg(hq / p.num_kv_heads)) {
-    case 1: return launch_decode_t<T, D, 1>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
-    case 2: return launch_decode_t<T, D, 2>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
-    default: return launch_decode_t<T, D, 4>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
-  }
-}
-
 hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
                          const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
                          int ns, float scale, void* ws, hipStream_t s) {
@@ -347,12 +353,12 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
   float* ws_ml = ws_o + decode_ws_o_floats(batch, hq, p.head_dim, ns);
   const bool bf = p.dtype == KVB_BF16;
   switch (p.head_dim) {
-    case 64:  return bf ? launch_decode_d<BF16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
-                        : launch_decode_d<F16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
-    case 96:  return bf ? launch_decode_d<BF16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
-                        : launch_decode_d<F16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
-    default:  return bf ? launch_decode_d<BF16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
-                        : launch_decode_d<F16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
+    case 64:  return bf ? launch_decode_t<BF16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
+                        : launch_decode_t<F16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
+    case 96:  return bf ? launch_decode_t<BF16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
+                        : launch_decode_t<F16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
+    default:  return bf ? launch_decode_t<BF16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
+                        : launch_decode_t<F16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
   }
 }
 

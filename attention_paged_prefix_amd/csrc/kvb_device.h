@@ -31,6 +31,10 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  __device__ static inline f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
   // a.x*b.x + a.y*b.y + c (fp32 accumulate)
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
@@ -49,6 +53,9 @@ struct BF16 {
   __device__ static inline f32x16 mfma32(s16x8 a, s16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static inline f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
@@ -61,8 +68,28 @@ template <typename T> __device__ inline float hi_f32(uint32_t w) { return T::to_
 template <> __device__ inline float lo_f32<BF16>(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 template <> __device__ inline float hi_f32<BF16>(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-template <typename T> __device__ inline uint32_t pack2(float a, float b) {
-  return (uint32_t)T::from_f32(a) | ((uint32_t)T::from_f32(b) << 16);
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 values rounded (nearest even) into one packed 16-bit pair (v_cvt_pk_*_f32).
+template <typename T> __device__ inline uint32_t pack2(float a, float b);
+template <> __device__ inline uint32_t pack2<F16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, f16x2v));
+}
+template <> __device__ inline uint32_t pack2<BF16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane t
+// receives element t%4 of the 4 x 16-bit values addressed by lanes t/4, t/4+4, t/4+8 and
+// t/4+12 of its group, in that order.  With source lane s pointing at row (r0 + s/4),
+// columns (c0 + 4*(s%4)) .. +3 of a row-major 16-bit matrix, lane t receives column
+// c0 + t of rows r0 .. r0+3.
+__device__ inline s16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
 // DPP quad permutations (within groups of 4 lanes): lane ^ 1 and lane ^ 2.
