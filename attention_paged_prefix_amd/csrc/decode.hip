@@ -12,14 +12,13 @@
 //    every K/V byte read.
 //  * A wave consumes two 16-token blocks (32 keys) per step and has the next step's
 //    K/V loads in flight while it works on the current one.
-//  * Scores S^T = K Q^T use v_mfma_f32_16x16x32 with K loaded straight from the pool
-//    into A-operand registers (each load instruction reads 64 contiguous bytes from
-//    each of the 16 rows of a block) and the queries as the B operand (columns beyond
-//    the group are zero).
+//  * Every global load instruction reads 1 KiB contiguous (four rows of a block's
+//    16 x head_dim run).  K and V pass through a per-wave LDS slot in their natural
+//    row-major layout (padded rows, so the operand reads are bank-conflict free).
+//  * Scores S^T = K Q^T use v_mfma_f32_16x16x32 with K rows from LDS as the A operand
+//    and the queries as the B operand (columns beyond the group are zero).
 //  * O^T += V^T P^T also uses 16x16x32: the score accumulators already hold P^T in
-//    B-operand layout; V is written to a per-wave LDS slot in its natural row-major
-//    layout (fully coalesced 1 KiB loads) and read back transposed with
-//    ds_read_b64_tr_b16.
+//    B-operand layout, and V is read back transposed with ds_read_b64_tr_b16.
 //  * Online softmax in the exp2 domain with lazy rescaling: the reference max only
 //    moves when a score exceeds it by more than 2^8, so exponentials stay <= 256 and
 //    the output rescale is rarely executed.
@@ -38,10 +37,10 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr float kNegBig = -1.0e30f;
 
 template <int D> struct DecStep {
-  static constexpr int NKK = D / 32;        // QK MFMAs per block
-  static constexpr int VCH = D / 32;        // 16-byte V chunks per lane per block
-  uint4 k[2][NKK];
+  static constexpr int VCH = D / 32;        // 16-byte chunks per lane per block, K and V
+  uint4 k[2][VCH];
   uint4 v[2][VCH];
+  int rows[2];                              // valid key rows of each block (0..16)
 };
 
 template <typename T, int D>
@@ -56,23 +55,27 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   constexpr int NDB = D / 16;               // 16-row d blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
   constexpr int VCH = D / 32;
-  constexpr int VROW = D + 16;              // LDS row stride (elements): 8 banks apart per row
-  constexpr int SLOT = 32 * VROW;           // two blocks per wave
+  constexpr int VROW = D + 16;              // V row stride (elements): 8 banks apart per row
+  constexpr int KROW = D + 8;               // K row stride (elements): 4 banks apart per row
+  constexpr int SLOT = 32 * (VROW + KROW);  // two blocks of V then K per wave
 
   __shared__ __attribute__((aligned(16))) uint16_t sV[kDecWaves * SLOT];
   __shared__ int s_bt[kMaxSplitBlocks];
   __shared__ float s_m[kDecWaves][kDecHeads];
   __shared__ float s_l[kDecWaves][kDecHeads];
-  static_assert(kDecWaves * kDecHeads * D * 4 <= kDecWaves * SLOT * 2, "merge buffer reuses V slots");
+  static_assert(kDecWaves * kDecHeads * D * 4 <= kDecWaves * SLOT * 2, "merge buffer reuses the slots");
   float* s_o = reinterpret_cast<float*>(sV);  // [wave][head][D] after the main loop
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
+  // logical id -> (kvh, b, split, chunk), chunk fastest and KV head slowest: each XCD
+  // works on few KV heads, so prefix blocks shared by many sequences stay in its L2
+  const int batch = real / (nchunks * nsplit * hkv);
   int r = lid;
   const int chunk = r % nchunks; r /= nchunks;
   const int split = r % nsplit; r /= nsplit;
-  const int kvh = r % hkv;
-  const int b = r / hkv;
+  const int b = r % batch;
+  const int kvh = r / batch;
   const int G = hq / hkv;
   const int h0 = kvh * G + chunk * kDecHeads;
   const int nh = min(kDecHeads, G - chunk * kDecHeads);
@@ -97,7 +100,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     s_bt[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
   }
 
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = uniform(tid >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
 
   // queries as the B operand: column c16 (head h0 + c16), d chunk 4*kk + g4
@@ -117,66 +120,62 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   __syncthreads();
 
   const int64_t head_off = (int64_t)kvh * kBlock * D;
-  uint16_t* slot = sV + w * SLOT;
+  uint16_t* slot = sV + w * SLOT;           // V rows 0..31
+  uint16_t* kslot = slot + 32 * VROW;       // K rows 0..31
 
+  // Both blocks of a step through buffer resources sized to their valid rows: rows past
+  // the context, blocks past the split and blocks outside the pool read as zero and
+  // cost no memory traffic, and every load is issued unconditionally.
   auto load = [&](int blk0, DecStep<D>& R) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int blk = blk0 + hb;
-      const int pb = blk < blk_end ? s_bt[blk - blk_begin] : -1;
-      if (pb >= 0) {
-        const uint16_t* kb = kp + (int64_t)pb * block_stride + head_off;
-        const uint16_t* vb = vp + (int64_t)pb * block_stride + head_off;
+      const int pb = uniform(blk < blk_end ? s_bt[blk - blk_begin] : -1);
+      const int rows = pb >= 0 ? min(kBlock, n - blk * kBlock) : 0;
+      R.rows[hb] = rows;
+      const int64_t off = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + off, (uint32_t)(rows * D * 2));
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          R.k[hb][kk] = *reinterpret_cast<const uint4*>(kb + c16 * D + 8 * (4 * kk + g4));
-#pragma unroll
-        for (int j = 0; j < VCH; ++j)
-          R.v[hb][j] = *reinterpret_cast<const uint4*>(vb + 8 * (j * 64 + lane));
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) R.k[hb][kk] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) R.v[hb][j] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < VCH; ++j) {
+        R.k[hb][j] = buf_load16(rk, (uint32_t)(8 * (j * 64 + lane)) * 2);
+        R.v[hb][j] = buf_load16(rv, (uint32_t)(8 * (j * 64 + lane)) * 2);
       }
     }
   };
 
   auto step = [&](int blk0, const DecStep<D>& R) {
-    // V of both blocks into this wave's LDS slot, natural [key][d] layout.  Rows past
-    // the context are zeroed: their probability is 0 but the pool may hold NaN there.
+    // V of both blocks into this wave's LDS slot, natural [key][d] layout (rows past
+    // the context arrive as zeros, so NaN left in unused pool slots never reaches PV)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int kbase = (blk0 + hb) * kBlock;
-      const bool partial = kbase + kBlock > n;
+    for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int j = 0; j < VCH; ++j) {
         const int c = j * 64 + lane;
         const int row = c / CPR, col = c - (c / CPR) * CPR;
-        uint4 val = R.v[hb][j];
-        if (partial && kbase + row >= n) val = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 8) = val;
+        *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 8) = R.v[hb][j];
+        *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 8) = R.k[hb][j];
       }
-    }
-    // S^T = K Q^T per block
+    __builtin_amdgcn_wave_barrier();
+    // S^T = K Q^T per block: A operand = key row c16, d chunk 4*kk + g4
     f32x4 s[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       s[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[hb] = T::mfma16(__builtin_bit_cast(s16x8, R.k[hb][kk]), qb[kk], s[hb]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const s16x8 a = *reinterpret_cast<const s16x8*>(kslot + (hb * 16 + c16) * KROW + 8 * (4 * kk + g4));
+        s[hb] = T::mfma16(a, qb[kk], s[hb]);
+      }
     }
     // scale + mask: lane holds keys 4*g4 + rr of each block for head column c16
     float t[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int blk = blk0 + hb;
-      const bool bvalid = blk < blk_end && s_bt[blk - blk_begin] >= 0;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const bool ok = bvalid && (blk * kBlock + 4 * g4 + rr < n);
+        const bool ok = 4 * g4 + rr < R.rows[hb];
         const float tv = ok ? s[hb][rr] * c_log2 : -INFINITY;
         t[hb * 4 + rr] = tv;
         mx = fmaxf(mx, tv);
@@ -217,17 +216,23 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     __builtin_amdgcn_wave_barrier();
   };
 
-  // each wave takes every fourth pair of blocks; next pair's loads in flight
-  int blk0 = blk_begin + 2 * w;
-  if (blk0 < blk_end) {
-    DecStep<D> cur;
-    load(blk0, cur);
-    for (; blk0 < blk_end; blk0 += 2 * kDecWaves) {
-      DecStep<D> nxt;
-      const bool more = blk0 + 2 * kDecWaves < blk_end;
-      if (more) load(blk0 + 2 * kDecWaves, nxt);
-      step(blk0, cur);
-      if (more) cur = nxt;
+  // each wave takes every fourth pair of blocks; the next pair's loads are in flight
+  // while the current pair is used (past the end they are zero-size, i.e. free)
+  // Two named buffers in ping-pong so no register copy forces a wait on the loads
+  // that are still in flight.
+  const int nsteps = (blk_end - blk_begin - 2 * w + 2 * kDecWaves - 1) / (2 * kDecWaves);
+  if (nsteps > 0) {
+    constexpr int kStride = 2 * kDecWaves;
+    int blk0 = blk_begin + 2 * w;
+    DecStep<D> A, B;
+    load(blk0, A);
+    for (int it = 0; it < nsteps; it += 2) {
+      load(blk0 + kStride, B);
+      step(blk0, A);
+      if (it + 1 >= nsteps) break;
+      load(blk0 + 2 * kStride, A);
+      step(blk0 + kStride, B);
+      blk0 += 2 * kStride;
     }
   }
 

@@ -104,6 +104,21 @@ __device__ inline float xor_lane(float x, int mask) { return __shfl_xor(x, mask,
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resources (gfx9 family dword3).  Loads at byte offsets >= num_records
+// return zero without touching memory, which gives branch-free zero fill for masked
+// rows and keeps every load unconditional (so the compiler can count outstanding
+// loads exactly instead of waiting for all of them).
+constexpr int kBufDword3 = 0x00020000;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kBufDword3);
+}
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond any num_records used here
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // XCD-aware remap: hardware deals consecutive work-group ids round-robin over the
 // XCDs; give each XCD a contiguous range of logical ids so neighbouring logical
 // work (same sequence / KV head) shares that XCD's L2.  `padded` is a multiple of 8.

@@ -160,9 +160,10 @@ def main(argv=None):
     ap.add_argument("--config", default="shared_prompt",
                     choices=["shared_prompt", "long_prefix", "ragged_d96", "ragged_d64", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-blocks", type=int, default=0, help="decode split size (0 = auto)")
     ap.add_argument("--no-decode", action="store_true", help="skip the separate decode workload")
-    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy"], default="step",
-                    help="profiling aid: time only one part")
+    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy", "decode_workload"],
+                    default="step", help="profiling aid: time only one part")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -186,6 +187,10 @@ def main(argv=None):
             bb.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": a.numel() * 2, "copy_bytes_written": a.numel() * 2}))
+        return 0
+
+    if args.only == "decode_workload":
+        print(json.dumps(bench_decode(torch, kvb, args)))
         return 0
 
     w = make_config(args.config, with_decode=True)
@@ -326,12 +331,15 @@ def bench_decode(torch, kvb, args):
     bt = _idev(torch, w.block_tables)
     out = torch.empty_like(q)
     max_ctx = int(w.context_lens.max())
-    n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx)
+    sb = args.split_blocks
+    n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx, sb)
     ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    # Cache flush by READING 1 GiB (more than L2 + Infinity Cache): a write-based flush
+    # would leave dirty lines whose write-back then competes with the timed kernel.
+    flush = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
 
     def run():
-        kvb.paged_decode(pool, q, ctx, bt, w.scale, max_ctx, out=out, workspace=ws)
+        kvb.paged_decode(pool, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         run()
@@ -344,7 +352,7 @@ def bench_decode(torch, kvb, args):
         a.record(); run(); b.record()
         warm.append((a, b))
     for _ in range(steps):
-        flush.fill_(1)          # evict L2 / Infinity Cache between launches (outside the events)
+        flush.sum()             # evict L2 / Infinity Cache between launches (outside the events)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(); run(); b.record()
