@@ -11,20 +11,22 @@
 //    row v = i*G + g packs chunk row i and query head kvh*G + g, so the G query heads
 //    that share a KV head share every K/V tile staged in LDS (GQA packing; works for
 //    any G, including 5).
-//  * K/V tiles of 64 keys = four 16-token blocks.  A prefix tile gathers its four
-//    (block, kv-head) runs of 16 x head_dim through the block table; a self tile reads
-//    k_new/v_new.  The next tile is loaded into registers while the current one is
-//    used (register double buffering), then written to LDS.
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 (A = K from
-//    LDS, B = Q held in registers for the whole kernel).  Each lane then owns one query
-//    row, so the row max needs a single cross-lane step and the row sum none.
+//  * K/V tiles of 64 keys = four 16-token blocks.  Each block (or each 16-row group of
+//    the chunk's own K/V) is read through a buffer resource sized to its valid rows:
+//    one 16-byte load per thread, rows past the end read as zero with no memory
+//    traffic, and every load is unconditional so it overlaps the previous tile's math.
+//  * LDS is double buffered: tile t+1 is loaded into registers while tile t is used,
+//    then stored to the other buffer; one barrier per tile.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 (A = K rows
+//    from LDS, B = Q held in registers for the whole kernel).  Each lane then owns one
+//    query row, so the row max needs one cross-lane step and the row sum none.
 //  * The output is accumulated transposed, O^T += V^T P^T: the score accumulators are
-//    already laid out as the B operand, and V is stored in LDS transposed with keys
-//    permuted inside every 16-key group to match that layout (one 16-byte LDS read per
-//    A operand).
-//  * Online softmax in the exp2 domain with scale*log2(e) folded in.  Only tiles that
-//    cross the causal diagonal or the end of the keys are masked; tiles entirely in the
-//    future of every row of the work-group are never visited.
+//    already the B operand, and V stays in its natural row-major layout in LDS and is
+//    read transposed with ds_read_b64_tr_b16.
+//  * Online softmax in the exp2 domain with scale*log2(e) folded into one FMA; the
+//    running max only moves (and the output is only rescaled) when a score exceeds it
+//    by more than 2^8.  Only tiles crossing the causal diagonal or the end of the keys
+//    are masked; tiles entirely in the future of every row are never visited.
 #include "kvb_device.h"
 #include "kvb_launch.h"
 
@@ -34,12 +36,17 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kBM = 32 * kPfWaves;      // virtual rows per work-group
 constexpr int kKT = 64;                 // keys per tile
-constexpr int kVPad = 8;                // elements of padding per V^T row
 constexpr float kPfNegBig = -1.0e30f;
+constexpr float kPfRescale = 8.0f;      // log2 units
 
-// Position of key k (0..15) inside its 16-key group in the transposed V tile: lane half
-// h of the PV MFMA reads keys {4h..4h+3, 8+4h..8+4h+3} as 8 consecutive elements.
-__device__ inline int vt_group_pos(int q4) { return ((q4 & 1) << 3) | ((q4 >> 1) << 2); }
+template <int D> struct PfLayout {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int KS = D + 8;                  // K row stride: rows 4 banks apart
+  static constexpr int VS = D == 128 ? 160 : 96;    // V row stride: rows 16 banks apart
+  static constexpr int KBUF = kKT * KS;
+  static constexpr int VBUF = kKT * VS;
+  static constexpr int BUF = KBUF + VBUF;           // elements per LDS buffer
+};
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kPfThreads, 2)
@@ -48,34 +55,32 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
                uint16_t* __restrict__ out, const int32_t* __restrict__ cu,
                const int32_t* __restrict__ plen, const int32_t* __restrict__ bt, int bt_stride,
-               int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded, int real) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int NK = kKT * CPR / kPfThreads; // K chunks per thread per tile
-  constexpr int KS = D + 8;                  // K row stride in LDS (elements)
-  constexpr int VS = kKT + kVPad;            // V^T row stride in LDS (elements)
+               int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
+               int real) {
+  using L = PfLayout<D>;
+  constexpr int CPR = L::CPR, KS = L::KS, VS = L::VS;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
   constexpr int NDB = D / 32;                // 32-wide d blocks of the output
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
+  // logical id -> (kvh, b, tile), tile fastest and KV head slowest
   int r = lid;
   const int tile = r % max_tiles; r /= max_tiles;
-  const int kvh = r % hkv;
-  const int b = r / hkv;
+  const int b = r % batch;
+  const int kvh = r / batch;
   const int G = hq / hkv;
   const int cu_b = min(max(cu[b], 0), total_q);
   const int C = max(0, min(cu[b + 1], total_q) - cu_b);
   const int nrows = C * G;
   const int v0 = tile * kBM;
   if (v0 >= nrows) return;
-  int P = plen[b];
-  P = max(0, min(P, bt_stride * kBlock));
+  const int P = max(0, min(plen[b], bt_stride * kBlock));
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = uniform(tid >> 6);
   const int lr = lane & 31, hf = lane >> 5;
 
   // this lane's query row
@@ -107,97 +112,80 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_run = kPfNegBig, l_run = 0.f;
 
-  uint4 kreg[NK];
-  uint4 vreg[4];
-  const int vkg = tid & 15, vcc = tid >> 4;  // V loader: key group (4 keys), d chunk
+  // loader geometry: thread tid covers row tid/CPR, chunk tid%CPR of each 16-row group
+  const bool ld_on = tid < kBlock * CPR;
+  const int ld_row = ld_on ? tid / CPR : 0;
+  const int ld_col = ld_on ? tid - ld_row * CPR : 0;
   const int64_t bt_row = (int64_t)b * bt_stride;
   const int64_t head_off = (int64_t)kvh * kBlock * D;
+  const uint32_t pool_off = ld_on ? (uint32_t)(ld_row * D + ld_col * 8) * 2 : kOobOffset;
+  const uint32_t self_off = ld_on ? (uint32_t)(ld_row * hkv * D + ld_col * 8) * 2 : kOobOffset;
 
-  auto load_tile = [&](int t) {
+  // block ids of a prefix tile (uniform); -1 past the prefix
+  auto tile_blocks = [&](int t, int* ids) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = t * 4 + i;                       // block index within the prefix
+      int pb = -1;
+      if (t < n_pre && j * kBlock < P) {
+        pb = bt[bt_row + j];
+        pb = (pb >= 0 && pb < num_blocks) ? pb : -1;
+      }
+      ids[i] = pb;
+    }
+  };
+
+  uint4 kreg[4], vreg[4];
+  auto load_tile = [&](int t, const int* ids) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
-    const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
-    int blk4[4] = {-1, -1, -1, -1};
-    if (pre) {
+    const int count = t >= total ? 0 : (pre ? min(kKT, P - base) : min(kKT, self_n - base));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rows = max(0, min(kBlock, count - kBlock * i));
+      __amdgpu_buffer_rsrc_t rk, rv;
+      uint32_t off;
+      if (pre) {
+        const int pb = ids[i];
+        const int64_t o64 = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
+        const uint32_t nbytes = pb >= 0 ? (uint32_t)(rows * D * 2) : 0u;
+        rk = make_rsrc(kp + o64, nbytes);
+        rv = make_rsrc(vp + o64, nbytes);
+        off = pool_off;
+      } else {
+        const int row0 = min(cu_b + base + kBlock * i, total_q);
+        const int64_t o64 = ((int64_t)row0 * hkv + kvh) * D;
+        const uint32_t nbytes = rows > 0 ? (uint32_t)(((rows - 1) * hkv * D + D) * 2) : 0u;
+        rk = make_rsrc(kn + o64, nbytes);
+        rv = make_rsrc(vn + o64, nbytes);
+        off = self_off;
+      }
+      kreg[i] = buf_load16(rk, off);
+      vreg[i] = buf_load16(rv, off);
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    if (ld_on) {
+      uint16_t* sk = smem + buf * L::BUF;
+      uint16_t* sv = sk + L::KBUF;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i * kBlock < count) {
-          const int pb = bt[bt_row + (base >> 4) + i];
-          blk4[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < NK; ++jj) {
-      const int c = tid + kPfThreads * jj;
-      const int row = c / CPR, col = c - (c / CPR) * CPR;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (row < count) {
-        if (pre) {
-          const int pb = blk4[row >> 4];
-          if (pb >= 0)
-            val = *reinterpret_cast<const uint4*>(kp + (int64_t)pb * block_stride + head_off +
-                                                  (row & 15) * D + col * 8);
-        } else {
-          val = *reinterpret_cast<const uint4*>(kn + ((int64_t)(cu_b + base + row) * hkv + kvh) * D + col * 8);
-        }
-      }
-      kreg[jj] = val;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * vkg + e;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (vcc < CPR && row < count) {
-        if (pre) {
-          const int pb = blk4[row >> 4];
-          if (pb >= 0)
-            val = *reinterpret_cast<const uint4*>(vp + (int64_t)pb * block_stride + head_off +
-                                                  (row & 15) * D + vcc * 8);
-        } else {
-          val = *reinterpret_cast<const uint4*>(vn + ((int64_t)(cu_b + base + row) * hkv + kvh) * D + vcc * 8);
-        }
-      }
-      vreg[e] = val;
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int jj = 0; jj < NK; ++jj) {
-      const int c = tid + kPfThreads * jj;
-      const int row = c / CPR, col = c - (c / CPR) * CPR;
-      *reinterpret_cast<uint4*>(&sK[row * KS + col * 8]) = kreg[jj];
-    }
-    if (vcc < CPR) {
-      // keys 4*vkg .. 4*vkg+3, d = 8*vcc .. 8*vcc+7  ->  V^T rows d, 4 consecutive positions
-      const int pos = (vkg >> 2) * 16 + vt_group_pos(vkg & 3);
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-#pragma unroll
-      for (int pi = 0; pi < 4; ++pi) {
-        // element 2*pi (low halves) and 2*pi+1 (high halves)
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(w1[pi], w0[pi], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w3[pi], w2[pi], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w1[pi], w0[pi], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w3[pi], w2[pi], 0x07060302u);
-        *reinterpret_cast<uint2*>(&sV[(vcc * 8 + 2 * pi) * VS + pos]) = lo;
-        *reinterpret_cast<uint2*>(&sV[(vcc * 8 + 2 * pi + 1) * VS + pos]) = hi;
+        const int row = kBlock * i + ld_row;
+        *reinterpret_cast<uint4*>(sk + row * KS + ld_col * 8) = kreg[i];
+        *reinterpret_cast<uint4*>(sv + row * VS + ld_col * 8) = vreg[i];
       }
     }
   };
 
-  if (total > 0) load_tile(0);
-  for (int t = 0; t < total; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < total) load_tile(t + 1);
-    if (!wave_active) continue;
+  // tr-read source address of this lane inside a V tile: rows 4*hf + (l%16)/4 (+8),
+  // columns 16*((l/16)%2) + 4*(l%4) (+32 per d block, +16 rows per 16-key step)
+  const int tr_row = 4 * hf + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  auto compute = [&](int t, int buf) {
+    const uint16_t* sk = smem + buf * L::BUF;
+    const uint16_t* sv = sk + L::KBUF;
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
@@ -208,67 +196,78 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       s[mb] = f32x16{};
-      const uint16_t* krow = &sK[(32 * mb + lr) * KS + 8 * hf];
+      const uint16_t* krow = sk + (32 * mb + lr) * KS + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const s16x8 a = *reinterpret_cast<const s16x8*>(krow + 16 * kk);
-        s[mb] = T::mfma32(a, qreg[kk], s[mb]);
-      }
+      for (int kk = 0; kk < NKK; ++kk)
+        s[mb] = T::mfma32(*reinterpret_cast<const s16x8*>(krow + 16 * kk), qreg[kk], s[mb]);
     }
-
-    // scale, mask, row max
+    if (need_mask) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kl = 32 * mb + (rr >> 2) * 8 + hf * 4 + (rr & 3);
+          const bool ok = kl < count && (pre || base + kl <= i_row);
+          s[mb][rr] = ok ? s[mb][rr] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float tv = s[mb][rr] * c_log2;
-        if (need_mask) {
-          const int kl = 32 * mb + (rr >> 2) * 8 + hf * 4 + (rr & 3);
-          const bool ok = kl < count && (pre || base + kl <= i_row);
-          tv = ok ? tv : -INFINITY;
-        }
-        s[mb][rr] = tv;
-        mx = fmaxf(mx, tv);
-      }
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+    mx = fmaxf(mx, xor_lane(mx, 32)) * c_log2;
+    if (__any(mx > m_run + kPfRescale)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
+    }
     // probabilities, packed as the B operand of the PV product
     s16x8 pk[4];
-    float psum = 0.f;
 #pragma unroll
     for (int kp4 = 0; kp4 < 4; ++kp4) {
       const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
       uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(s[mb][r0 + 2 * e] - m_new);
-        const float p1 = fast_exp2(s[mb][r0 + 2 * e + 1] - m_new);
-        psum += p0 + p1;
+        const float p0 = fast_exp2(fmaf(s[mb][r0 + 2 * e], c_log2, -m_run));
+        const float p1 = fast_exp2(fmaf(s[mb][r0 + 2 * e + 1], c_log2, -m_run));
+        l_run += p0 + p1;
         pw[e] = pack2<T>(p0, p1);
       }
-      uint4 u = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      pk[kp4] = __builtin_bit_cast(s16x8, u);
+      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     }
-    l_run = l_run * alpha + psum;
+    // O^T += V^T P^T
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint16_t* vrow = &sV[(32 * db + lr) * VS + 8 * hf];
-#pragma unroll
       for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const s16x8 a = *reinterpret_cast<const s16x8*>(vrow + 16 * kp4);
+        const uint16_t* src = sv + (16 * kp4 + tr_row) * VS + 32 * db + tr_col;
+        const s16x4 lo = lds_read_tr16(src);
+        const s16x4 hi = lds_read_tr16(src + 8 * VS);
+        const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = T::mfma32(a, pk[kp4], o[db]);
       }
-    }
+  };
+
+  int ids_a[4], ids_b[4];   // block ids of the tile being loaded next
+  tile_blocks(0, ids_a);
+  tile_blocks(1, ids_b);
+  load_tile(0, ids_a);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < total; ++t) {
+    // ids_b holds tile t+1's blocks; fetch tile t+2's while t+1 is loading
+    load_tile(t + 1, ids_b);
+    tile_blocks(t + 2, ids_b);
+    if (wave_active) compute(t, t & 1);
+    store_tile((t + 1) & 1);
+    __syncthreads();
   }
 
   // epilogue: normalise and store (lane owns one query row, d in runs of 4)
@@ -299,12 +298,13 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   const long long real = (long long)batch * p.num_kv_heads * max_tiles;
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
-  const float c = scale * 1.4426950408889634f;
+  // scale 0 (all scores equal) is kept positive so masked -inf scores stay -inf
+  const float c = fmaxf(scale * 1.4426950408889634f, 1e-30f);
   hipLaunchKernelGGL((prefill_kernel<T, D>), dim3((unsigned)padded), dim3(kPfThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
-                     cu, plen, bt, bt_stride, hq, p.num_kv_heads, total_q, max_tiles, c, (int)padded,
-                     (int)real);
+                     cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
+                     (int)padded, (int)real);
   return hipGetLastError();
 }
 
