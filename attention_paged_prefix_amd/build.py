@@ -33,6 +33,15 @@ FLAGS = [
 ]
 
 
+# Attention kernels never produce NaN scores (masked keys use -inf), so their max
+# reductions need no NaN canonicalisation of every operand.  The host-side argument
+# checks (api.hip) are compiled without this flag.
+KERNEL_FLAGS = {
+    "prefill.hip": ["-fno-honor-nans"],
+    "decode.hip": ["-fno-honor-nans"],
+}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,7 +57,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + flags + KERNEL_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for cmd, _ in zip(cmds, ex.map(_run, cmds)):
             if verbose:

@@ -35,6 +35,7 @@ struct F16 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  static constexpr uint32_t kOnePair = 0x3C003C00u;   // (1.0, 1.0)
   // a.x*b.x + a.y*b.y + c (fp32 accumulate)
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b),
@@ -56,6 +57,7 @@ struct BF16 {
   __device__ static inline f32x4 mfma16(s16x8 a, s16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static constexpr uint32_t kOnePair = 0x3F803F80u;   // (1.0, 1.0)
   __device__ static inline float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
@@ -109,8 +111,15 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // rows and keeps every load unconditional (so the compiler can count outstanding
 // loads exactly instead of waiting for all of them).
 constexpr int kBufDword3 = 0x00020000;
+// The fields are forced into scalar registers (readfirstlane): callers pass wave-uniform
+// values, and a resource the compiler cannot prove uniform becomes a waterfall loop.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kBufDword3);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  void* p = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kBufDword3);
 }
 __device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));

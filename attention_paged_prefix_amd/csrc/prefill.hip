@@ -116,52 +116,49 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const bool ld_on = tid < kBlock * CPR;
   const int ld_row = ld_on ? tid / CPR : 0;
   const int ld_col = ld_on ? tid - ld_row * CPR : 0;
-  const int64_t bt_row = (int64_t)b * bt_stride;
+  const int32_t* bt_row = bt + (int64_t)b * bt_stride;
   const int64_t head_off = (int64_t)kvh * kBlock * D;
+  const uint16_t* kbase = kp + head_off;                          // + block * block_stride
+  const uint16_t* vbase = vp + head_off;
+  const uint16_t* knb = kn + ((int64_t)cu_b * hkv + kvh) * D;     // + row * hkv * D
+  const uint16_t* vnb = vn + ((int64_t)cu_b * hkv + kvh) * D;
   const uint32_t pool_off = ld_on ? (uint32_t)(ld_row * D + ld_col * 8) * 2 : kOobOffset;
   const uint32_t self_off = ld_on ? (uint32_t)(ld_row * hkv * D + ld_col * 8) * 2 : kOobOffset;
+  const uint32_t self_row_bytes = (uint32_t)(hkv * D * 2);
 
-  // block ids of a prefix tile (uniform); -1 past the prefix
+  // block ids of prefix tile t (uniform scalar loads); -1 past the prefix or out of pool
   auto tile_blocks = [&](int t, int* ids) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = t * 4 + i;                       // block index within the prefix
+      const int j = t * 4 + i;
       int pb = -1;
-      if (t < n_pre && j * kBlock < P) {
-        pb = bt[bt_row + j];
-        pb = (pb >= 0 && pb < num_blocks) ? pb : -1;
-      }
-      ids[i] = pb;
+      if (j * kBlock < P) pb = bt_row[j];
+      ids[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
     }
   };
 
+  // Tile t (prefix tiles first, then the chunk's own tiles) into registers.  Branch
+  // free: both sources are described by (base pointer, valid bytes, lane offset) and
+  // selected with uniform conditions; past the last tile every size is zero.
   uint4 kreg[4], vreg[4];
   auto load_tile = [&](int t, const int* ids) {
     const bool pre = t < n_pre;
-    const int base = pre ? t * kKT : (t - n_pre) * kKT;
-    const int count = t >= total ? 0 : (pre ? min(kKT, P - base) : min(kKT, self_n - base));
+    const int u = t - n_pre;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rows = max(0, min(kBlock, count - kBlock * i));
-      __amdgpu_buffer_rsrc_t rk, rv;
-      uint32_t off;
-      if (pre) {
-        const int pb = ids[i];
-        const int64_t o64 = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
-        const uint32_t nbytes = pb >= 0 ? (uint32_t)(rows * D * 2) : 0u;
-        rk = make_rsrc(kp + o64, nbytes);
-        rv = make_rsrc(vp + o64, nbytes);
-        off = pool_off;
-      } else {
-        const int row0 = min(cu_b + base + kBlock * i, total_q);
-        const int64_t o64 = ((int64_t)row0 * hkv + kvh) * D;
-        const uint32_t nbytes = rows > 0 ? (uint32_t)(((rows - 1) * hkv * D + D) * 2) : 0u;
-        rk = make_rsrc(kn + o64, nbytes);
-        rv = make_rsrc(vn + o64, nbytes);
-        off = self_off;
-      }
-      kreg[i] = buf_load16(rk, off);
-      vreg[i] = buf_load16(rv, off);
+      const int pb = ids[i];
+      const int rows_pre = max(0, min(kBlock, P - (t * kKT + kBlock * i)));
+      const int row0 = u * kKT + kBlock * i;
+      const int rows_self = max(0, min(kBlock, self_n - row0));
+      const int64_t pre_off = (int64_t)(pb >= 0 ? pb : 0) * block_stride;
+      const int64_t self_row = (int64_t)(pre ? 0 : min(row0, C)) * hkv * D;
+      const uint16_t* kb = pre ? kbase + pre_off : knb + self_row;
+      const uint16_t* vb = pre ? vbase + pre_off : vnb + self_row;
+      const uint32_t nb = pre ? (pb >= 0 ? (uint32_t)(rows_pre * D * 2) : 0u)
+                              : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
+      const uint32_t off = pre ? pool_off : self_off;
+      kreg[i] = buf_load16(make_rsrc(kb, nb), off);
+      vreg[i] = buf_load16(make_rsrc(vb, nb), off);
     }
   };
 
@@ -180,8 +177,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 
   // tr-read source address of this lane inside a V tile: rows 4*hf + (l%16)/4 (+8),
   // columns 16*((l/16)%2) + 4*(l%4) (+32 per d block, +16 rows per 16-key step)
-  const int tr_row = 4 * hf + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_base = (4 * hf + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int k_base = lr * KS + 8 * hf;
 
   auto compute = [&](int t, int buf) {
     const uint16_t* sk = smem + buf * L::BUF;
@@ -191,31 +188,28 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
     const bool need_mask = (count < kKT) || (!pre && base + kKT - 1 > i_first);
 
-    // S^T = K Q^T for two 32-key halves
-    f32x16 s[2];
+    // S^T = K Q^T for two 32-key halves; the two accumulation chains are interleaved
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-      const uint16_t* krow = sk + (32 * mb + lr) * KS + 8 * hf;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[mb] = T::mfma32(*reinterpret_cast<const s16x8*>(krow + 16 * kk), qreg[kk], s[mb]);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const s16x8 a0 = *reinterpret_cast<const s16x8*>(sk + k_base + 16 * kk);
+      const s16x8 a1 = *reinterpret_cast<const s16x8*>(sk + k_base + 32 * KS + 16 * kk);
+      s0 = T::mfma32(a0, qreg[kk], s0);
+      s1 = T::mfma32(a1, qreg[kk], s1);
     }
     if (need_mask) {
+      // key kl of the tile is visible to this lane's row iff kl < lim
+      const int lim = pre ? count : min(count, i_row - base + 1);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int kl = 32 * mb + (rr >> 2) * 8 + hf * 4 + (rr & 3);
-          const bool ok = kl < count && (pre || base + kl <= i_row);
-          s[mb][rr] = ok ? s[mb][rr] : -INFINITY;
-        }
+      for (int rr = 0; rr < 16; ++rr) {
+        const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
+        s0[rr] = kl < lim ? s0[rr] : -INFINITY;
+        s1[rr] = kl + 32 < lim ? s1[rr] : -INFINITY;
+      }
     }
-    float mx = -INFINITY;
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[mb][rr]);
+    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fmaxf(s0[rr], s1[rr]));
     mx = fmaxf(mx, xor_lane(mx, 32)) * c_log2;
     if (__any(mx > m_run + kPfRescale)) {
       const float mn = fmaxf(m_run, mx);
@@ -227,44 +221,50 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
     }
-    // probabilities, packed as the B operand of the PV product
+    // probabilities, packed as the B operand of the PV product; the row sum adds the
+    // rounded values (the ones PV uses) two at a time with a dot product against (1, 1)
     s16x8 pk[4];
+    float ls = l_run;
 #pragma unroll
     for (int kp4 = 0; kp4 < 4; ++kp4) {
-      const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+      const f32x16& sv4 = (kp4 >> 1) ? s1 : s0;
+      const int r0 = (kp4 & 1) * 8;
       uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(s[mb][r0 + 2 * e], c_log2, -m_run));
-        const float p1 = fast_exp2(fmaf(s[mb][r0 + 2 * e + 1], c_log2, -m_run));
-        l_run += p0 + p1;
+        const float p0 = fast_exp2(fmaf(sv4[r0 + 2 * e], c_log2, -m_run));
+        const float p1 = fast_exp2(fmaf(sv4[r0 + 2 * e + 1], c_log2, -m_run));
         pw[e] = pack2<T>(p0, p1);
+        ls = T::dot2(pw[e], T::kOnePair, ls);
       }
       pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     }
-    // O^T += V^T P^T
+    l_run = ls;
+    // O^T += V^T P^T; all eight transposed reads of a d block are issued before its MFMAs
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
+      s16x8 a[4];
 #pragma unroll
       for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const uint16_t* src = sv + (16 * kp4 + tr_row) * VS + 32 * db + tr_col;
+        const uint16_t* src = sv + tr_base + 16 * kp4 * VS + 32 * db;
         const s16x4 lo = lds_read_tr16(src);
         const s16x4 hi = lds_read_tr16(src + 8 * VS);
-        const s16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = T::mfma32(a, pk[kp4], o[db]);
+        a[kp4] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+#pragma unroll
+      for (int kp4 = 0; kp4 < 4; ++kp4) o[db] = T::mfma32(a[kp4], pk[kp4], o[db]);
+    }
   };
 
-  int ids_a[4], ids_b[4];   // block ids of the tile being loaded next
-  tile_blocks(0, ids_a);
-  tile_blocks(1, ids_b);
-  load_tile(0, ids_a);
+  int ids[4];
+  tile_blocks(0, ids);
+  load_tile(0, ids);
   store_tile(0);
+  tile_blocks(1, ids);
   __syncthreads();
   for (int t = 0; t < total; ++t) {
-    // ids_b holds tile t+1's blocks; fetch tile t+2's while t+1 is loading
-    load_tile(t + 1, ids_b);
-    tile_blocks(t + 2, ids_b);
+    load_tile(t + 1, ids);                  // in flight during this tile's math
+    tile_blocks(t + 2, ids);
     if (wave_active) compute(t, t & 1);
     store_tile((t + 1) & 1);
     __syncthreads();
