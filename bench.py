@@ -104,11 +104,13 @@ def read_traffic(kernel_key: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = fields.get("source_file")
-    if not src:
+    srcs = fields.get("source_files")
+    if not srcs:
         return None
-    sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
-    if sha != fields.get("source_sha256_16"):
+    h = hashlib.sha256()
+    for src in srcs.split(","):
+        h.update(open(os.path.join(ROOT, src.strip()), "rb").read())
+    if h.hexdigest()[:16] != fields.get("source_sha256_16"):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -117,8 +119,9 @@ def read_traffic(kernel_key: str):
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
-    """The fp64 oracle on a bounded sample of the same prefill workload: (sequence, head)
-    pairs in order until the time budget is spent."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same prefill workload:
+    whole (sequence, query head) problems in order, repeating the workload until about
+    `budget_s` seconds of host time have been spent."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -129,30 +132,68 @@ def cpu_baseline(w, budget_s: float = 12.0):
     done_flops = 0.0
     pairs = 0
     t0 = time.perf_counter()
-    for b in range(w.batch):
-        C = int(w.q_lens[b])
-        P = int(w.prefix_lens[b])
-        for h in range(w.num_q_heads):
-            oracle.paged_prefill(w.k_pool, w.v_pool, w.q, w.k_new, w.v_new, w.cu_q_lens,
-                                 w.prefix_lens, w.block_tables, w.num_q_heads, w.scale, w.dtype,
-                                 select=[(b, h, np.arange(C))])
-            done_flops += 4.0 * w.head_dim * (C * P + C * (C + 1) / 2)
-            pairs += 1
+    while time.perf_counter() - t0 < budget_s:
+        for b in range(w.batch):
+            C = int(w.q_lens[b])
+            P = int(w.prefix_lens[b])
+            for h in range(w.num_q_heads):
+                oracle.paged_prefill(w.k_pool, w.v_pool, w.q, w.k_new, w.v_new, w.cu_q_lens,
+                                     w.prefix_lens, w.block_tables, w.num_q_heads, w.scale, w.dtype,
+                                     select=[(b, h, np.arange(C))])
+                done_flops += 4.0 * w.head_dim * (C * P + C * (C + 1) / 2)
+                pairs += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
             if time.perf_counter() - t0 > budget_s:
                 break
-        if time.perf_counter() - t0 > budget_s:
-            break
     dt = time.perf_counter() - t0
     return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"paged prefill of {pairs} of {w.batch * w.num_q_heads} (sequence, query head) "
-                      f"pairs of the same workload, fp64 NumPy, {dt:.1f} s",
+            "sample": f"{pairs} (sequence, query head) problems of the same prefill workload "
+                      f"({w.batch * w.num_q_heads} per pass), fp64 NumPy, {dt:.1f} s",
             "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------- rocprofv3 summaries
+
+def summarize_rocprof(path: str, kernel: str) -> str:
+    """Text summary of rocprofv3 CSV output under `path` for kernels whose name contains
+    `kernel`: average duration from a kernel trace, per-dispatch averages of counters."""
+    import csv
+    import glob
+    lines = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*_kernel_stats.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if kernel in r["Name"]:
+                lines.append(f"kernel: {r['Name'][:120]}")
+                lines.append(f"calls: {r['Calls']}")
+                lines.append(f"avg_ns: {float(r['AverageNs']):.1f}")
+                lines.append(f"min_ns: {float(r['MinNs']):.1f}")
+                lines.append(f"max_ns: {float(r['MaxNs']):.1f}")
+    for f in sorted(glob.glob(os.path.join(path, "**", "*_counter_collection.csv"), recursive=True)):
+        per = {}
+        for r in csv.DictReader(open(f)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if per:
+            names = sorted({k for d in per.values() for k in d})
+            lines.append(f"dispatches: {len(per)}")
+            for n in names:
+                vals = [d.get(n, 0.0) for d in per.values()]
+                lines.append(f"{n}_per_dispatch: {sum(vals) / len(vals):.6g}")
+    return "\n".join(lines)
 
 
 # ----------------------------------------------------------------- main
 
 def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "--summarize-rocprof":
+        # python bench.py --summarize-rocprof DIR KERNEL_SUBSTRING
+        print(summarize_rocprof(argv[1], argv[2]))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -309,7 +350,11 @@ def main(argv=None):
                            "algorithmic_bytes_per_launch": prefill_bytes(w)}
 
     if not args.no_decode and args.only == "step":
-        res["decode_workload"] = bench_decode(torch, kvb, args)
+        dw = bench_decode(torch, kvb, args)
+        dw["roofline"] = {"bound": "hbm", "kernel": "paged_decode", "achieved": dw["gbps_cold_cache"],
+                          "peak": PEAK_GBPS, "unit": "GB/s", "frac": dw["gbps_cold_cache"] / PEAK_GBPS,
+                          "traffic": read_traffic("paged_decode_decode_workload")}
+        res["decode_workload"] = dw
 
     if not args.no_cpu_baseline and args.only == "step":
         res["cpu_baseline"] = cpu_baseline(w)
