@@ -128,6 +128,13 @@ constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond any num_records used he
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at
+// lds + 16*L (the LDS base must be wave-uniform).  Out-of-range lanes write zeros.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, (int)byte_off, 0, 0, 0);
+}
+
 // XCD-aware remap: hardware deals consecutive work-group ids round-robin over the
 // XCDs; give each XCD a contiguous range of logical ids so neighbouring logical
 // work (same sequence / KV head) shares that XCD's L2.  `padded` is a multiple of 8.

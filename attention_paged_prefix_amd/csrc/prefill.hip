@@ -32,24 +32,54 @@
 
 namespace kvb {
 
-constexpr int kPfWaves = 4;
+constexpr int kRowWaves = 4;             // waves along the rows (32 rows each)
+constexpr int kPfWaves = 2 * kRowWaves;  // two key halves
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kBM = 32 * kPfWaves;      // virtual rows per work-group
-constexpr int kKT = 64;                 // keys per tile
+constexpr int kRowBlocks = 1;            // 32-row MFMA blocks per wave
+constexpr int kBM = 32 * kRowBlocks * kRowWaves;  // virtual rows per work-group
+constexpr int kKT = 64;                  // keys per tile
 constexpr float kPfNegBig = -1.0e30f;
-constexpr float kPfRescale = 8.0f;      // log2 units
+constexpr float kPfRescale = 8.0f;       // log2 units
 
+// LDS tile = K rows then V rows, 64 x D each, unpadded.  Tiles are written by
+// LDS-direct buffer loads (16 bytes per lane, lanes contiguous), so rows cannot be
+// padded; instead the 16-byte chunks of a row are permuted so that the two read
+// patterns are bank-conflict free:
+//   K: the MFMA A operand reads one chunk from 16 consecutive rows per 16 lanes;
+//   V: the transpose read reads four 32-byte row pieces (4 rows x 4 chunks) per 32 lanes.
+// The permutation of a row depends only on row bits that are the same for every row a
+// given lane reads, so read addresses are precomputed per lane.
 template <int D> struct PfLayout {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int KS = D + 8;                  // K row stride: rows 4 banks apart
-  static constexpr int VS = D == 128 ? 160 : 96;    // V row stride: rows 16 banks apart
-  static constexpr int KBUF = kKT * KS;
-  static constexpr int VBUF = kKT * VS;
-  static constexpr int BUF = KBUF + VBUF;           // elements per LDS buffer
+  static constexpr int TILE = 2 * kKT * D;          // elements: K then V
+  __device__ static int posK(int r, int c) {
+    if constexpr (D == 128) return c ^ (r & 15);
+    else if constexpr (D == 96) return (c + ((r >> 2) & 3)) % 12;
+    else return c ^ ((r >> 1) & 7);
+  }
+  __device__ static int invK(int r, int p) {
+    if constexpr (D == 128) return p ^ (r & 15);
+    else if constexpr (D == 96) return (p + 12 - ((r >> 2) & 3)) % 12;
+    else return p ^ ((r >> 1) & 7);
+  }
+  __device__ static int posV(int r, int c) {
+    if constexpr (D == 128) return ((((c >> 2) + r) & 3) << 2) | (c & 3);
+    else if constexpr (D == 96) return (c + ((r >> 2) & 3)) % 12;
+    else return ((((c >> 2) + (r >> 1)) & 1) << 2) | (c & 3);
+  }
+  __device__ static int invV(int r, int p) {
+    if constexpr (D == 128) return ((((p >> 2) - r) & 3) << 2) | (p & 3);
+    else if constexpr (D == 96) return (p + 12 - ((r >> 2) & 3)) % 12;
+    else return ((((p >> 2) - (r >> 1)) & 1) << 2) | (p & 3);
+  }
 };
 
+// Work-group = 8 waves (two per SIMD).  Wave w handles the 32 virtual rows
+// 32*(w & 3) .. +31 of the work-group's 128 and the key tiles t with t % 2 == (w >> 2):
+// the two waves of a row group split the keys and merge their (output, max, sum)
+// through LDS at the end.  A stage holds two tiles; stages are double buffered in LDS.
 template <typename T, int D>
-__global__ void __launch_bounds__(kPfThreads, 2)
+__global__ void __launch_bounds__(kPfThreads, 1)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
@@ -58,11 +88,13 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
                int real) {
   using L = PfLayout<D>;
-  constexpr int CPR = L::CPR, KS = L::KS, VS = L::VS;
+  constexpr int CPR = L::CPR;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
   constexpr int NDB = D / 32;                // 32-wide d blocks of the output
+  constexpr int NLD = CPR / 4;               // 1 KiB load instructions per 16-row block
+  constexpr int VOFF = kKT * D;              // V rows follow K rows in a tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * L::TILE];  // [key half][stage]
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -82,23 +114,26 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
   const int lr = lane & 31, hf = lane >> 5;
+  const int rw = w & (kRowWaves - 1), kh = w / kRowWaves;   // row group, key half
 
-  // this lane's query row
-  const int v = v0 + 32 * w + lr;
-  const bool rvalid = v < nrows;
-  const int i_row = rvalid ? v / G : C;
-  const int g_row = rvalid ? v - (v / G) * G : 0;
-  const bool wave_active = v0 + 32 * w < nrows;
-
-  s16x8 qreg[NKK];
-  {
-    const uint16_t* qrow = q + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D + 8 * hf;
+  // this lane's two query rows
+  int i_row[kRowBlocks], g_row[kRowBlocks];
+  bool rvalid[kRowBlocks];
+  s16x8 qreg[kRowBlocks][NKK];
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const int v = v0 + 32 * kRowBlocks * rw + 32 * j + lr;
+    rvalid[j] = v < nrows;
+    i_row[j] = rvalid[j] ? v / G : C;
+    g_row[j] = rvalid[j] ? v - (v / G) * G : 0;
+    const uint16_t* qrow = q + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (rvalid) qreg[kk] = *reinterpret_cast<const s16x8*>(qrow + 16 * kk);
-      else qreg[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (rvalid[j]) qreg[j][kk] = *reinterpret_cast<const s16x8*>(qrow + 16 * kk);
+      else qreg[j][kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  const bool wave_active = v0 + 32 * kRowBlocks * rw < nrows;
 
   const int last_row = min(nrows, v0 + kBM) - 1;
   const int self_n = last_row / G + 1;       // chunk keys needed by this work-group
@@ -106,185 +141,252 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int n_pre = (P + kKT - 1) / kKT;
   const int n_self = (self_n + kKT - 1) / kKT;
   const int total = n_pre + n_self;
+  const int nstage = (total + 1) / 2;
 
-  f32x16 o[NDB];
+  f32x16 o[kRowBlocks][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m_run = kPfNegBig, l_run = 0.f;
+  for (int j = 0; j < kRowBlocks; ++j)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[j][i] = f32x16{};
+  float m_run[kRowBlocks], l_run[kRowBlocks];
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) { m_run[j] = kPfNegBig; l_run[j] = 0.f; }
 
-  // loader geometry: thread tid covers row tid/CPR, chunk tid%CPR of each 16-row group
-  const bool ld_on = tid < kBlock * CPR;
-  const int ld_row = ld_on ? tid / CPR : 0;
-  const int ld_col = ld_on ? tid - ld_row * CPR : 0;
+  // ---- loader: waves 0-3 stage the even tile of a stage, waves 4-7 the odd one; within
+  // a tile wave (w & 3) loads block (w & 3).  Instruction m of a block fills LDS chunks
+  // 64m..64m+63 of that block; lane L's chunk holds row (64m+L)/CPR, logical chunk
+  // inv(row, (64m+L)%CPR).
+  const int ld_tile = w / kRowWaves, ld_blk = w & (kRowWaves - 1);
+  uint32_t offK_pool[NLD], offV_pool[NLD], offK_self[NLD], offV_self[NLD];
+#pragma unroll
+  for (int m = 0; m < NLD; ++m) {
+    const int pos = 64 * m + lane;
+    const int rb = pos / CPR, cp = pos - (pos / CPR) * CPR;
+    const int ck = L::invK(rb, cp), cv = L::invV(rb, cp);
+    offK_pool[m] = (uint32_t)(rb * D + ck * 8) * 2;
+    offV_pool[m] = (uint32_t)(rb * D + cv * 8) * 2;
+    offK_self[m] = (uint32_t)(rb * hkv * D + ck * 8) * 2;
+    offV_self[m] = (uint32_t)(rb * hkv * D + cv * 8) * 2;
+  }
   const int32_t* bt_row = bt + (int64_t)b * bt_stride;
   const int64_t head_off = (int64_t)kvh * kBlock * D;
   const uint16_t* kbase = kp + head_off;                          // + block * block_stride
   const uint16_t* vbase = vp + head_off;
   const uint16_t* knb = kn + ((int64_t)cu_b * hkv + kvh) * D;     // + row * hkv * D
   const uint16_t* vnb = vn + ((int64_t)cu_b * hkv + kvh) * D;
-  const uint32_t pool_off = ld_on ? (uint32_t)(ld_row * D + ld_col * 8) * 2 : kOobOffset;
-  const uint32_t self_off = ld_on ? (uint32_t)(ld_row * hkv * D + ld_col * 8) * 2 : kOobOffset;
   const uint32_t self_row_bytes = (uint32_t)(hkv * D * 2);
 
-  // block ids of prefix tile t (uniform scalar loads); -1 past the prefix or out of pool
+  // block id of this wave's block of prefix tile t (uniform scalar load)
   auto tile_blocks = [&](int t, int* ids) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = t * 4 + i;
-      int pb = -1;
-      if (j * kBlock < P) pb = bt_row[j];
-      ids[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
-    }
+    const int jb = t * 4 + ld_blk;
+    int pb = -1;
+    if (t < n_pre && jb * kBlock < P) pb = bt_row[jb];
+    ids[0] = (pb >= 0 && pb < num_blocks) ? pb : -1;
   };
 
-  // Tile t (prefix tiles first, then the chunk's own tiles) into registers.  Branch
-  // free: both sources are described by (base pointer, valid bytes, lane offset) and
-  // selected with uniform conditions; past the last tile every size is zero.
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int t, const int* ids) {
+  // Tile t (prefix tiles first, then the chunk's own tiles) straight into LDS buffer
+  // (ld_tile, stage).  Sources are (base, valid bytes, lane offset) selected with uniform
+  // conditions; rows past the end read as zero; past the last tile every size is zero.
+  auto load_tile = [&](int t, const int* ids, int stage) {
     const bool pre = t < n_pre;
-    const int u = t - n_pre;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pb = ids[i];
+    const int tu = t - n_pre;
+    uint16_t* dst = smem + (ld_tile * 2 + stage) * L::TILE;
+    {
+      const int i = ld_blk;
+      const int pb = ids[0];
       const int rows_pre = max(0, min(kBlock, P - (t * kKT + kBlock * i)));
-      const int row0 = u * kKT + kBlock * i;
-      const int rows_self = max(0, min(kBlock, self_n - row0));
+      const int row0 = tu * kKT + kBlock * i;
+      const int rows_self = t < total ? max(0, min(kBlock, self_n - row0)) : 0;
       const int64_t pre_off = (int64_t)(pb >= 0 ? pb : 0) * block_stride;
-      const int64_t self_row = (int64_t)(pre ? 0 : min(row0, C)) * hkv * D;
+      const int64_t self_row = (int64_t)(pre ? 0 : min(max(row0, 0), C)) * hkv * D;
       const uint16_t* kb = pre ? kbase + pre_off : knb + self_row;
       const uint16_t* vb = pre ? vbase + pre_off : vnb + self_row;
       const uint32_t nb = pre ? (pb >= 0 ? (uint32_t)(rows_pre * D * 2) : 0u)
                               : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
-      const uint32_t off = pre ? pool_off : self_off;
-      kreg[i] = buf_load16(make_rsrc(kb, nb), off);
-      vreg[i] = buf_load16(make_rsrc(vb, nb), off);
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    if (ld_on) {
-      uint16_t* sk = smem + buf * L::BUF;
-      uint16_t* sv = sk + L::KBUF;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nb), rv = make_rsrc(vb, nb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = kBlock * i + ld_row;
-        *reinterpret_cast<uint4*>(sk + row * KS + ld_col * 8) = kreg[i];
-        *reinterpret_cast<uint4*>(sv + row * VS + ld_col * 8) = vreg[i];
+      for (int m = 0; m < NLD; ++m) {
+        uint16_t* dk = dst + (kBlock * i * CPR + 64 * m) * 8;
+        buf_load16_lds(rk, pre ? offK_pool[m] : offK_self[m], dk);
+        buf_load16_lds(rv, pre ? offV_pool[m] : offV_self[m], dk + VOFF);
       }
     }
   };
 
-  // tr-read source address of this lane inside a V tile: rows 4*hf + (l%16)/4 (+8),
-  // columns 16*((l/16)%2) + 4*(l%4) (+32 per d block, +16 rows per 16-key step)
-  const int tr_base = (4 * hf + ((lane & 15) >> 2)) * VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int k_base = lr * KS + 8 * hf;
+  // ---- per-lane LDS read addresses (elements, relative to a tile)
+  // K operand of row block mb: row 32*mb + lr, logical chunk 2*kk + hf (mb adds 32 rows)
+  int kaddr[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = (lr * CPR + L::posK(lr, 2 * kk + hf)) * 8;
+  // V transpose-read source: rows 16*kp4 + 4*hf + (l%16)/4 (+8 for the high half),
+  // columns 32*db + 16*((l/16)%2) + 4*(l%4), i.e. chunk 4*db + 2*((l/16)%2) + (l%4)/2
+  int vaddr[NDB][2];
+  {
+    const int s4 = (lane & 15) >> 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 4 * hf + s4 + 8 * hi;
+        const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        vaddr[db][hi] = VOFF + (row * CPR + L::posV(row, c)) * 8 + 4 * (lane & 1);
+      }
+  }
 
-  auto compute = [&](int t, int buf) {
-    const uint16_t* sk = smem + buf * L::BUF;
-    const uint16_t* sv = sk + L::KBUF;
+  auto compute = [&](int t, const uint16_t* sk) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
     const bool need_mask = (count < kKT) || (!pre && base + kKT - 1 > i_first);
 
-    // S^T = K Q^T for two 32-key halves; the two accumulation chains are interleaved
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // S^T = K Q^T: each K operand read feeds both row blocks
+    f32x16 s[kRowBlocks][2];
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; ++j) { s[j][0] = f32x16{}; s[j][1] = f32x16{}; }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const s16x8 a0 = *reinterpret_cast<const s16x8*>(sk + k_base + 16 * kk);
-      const s16x8 a1 = *reinterpret_cast<const s16x8*>(sk + k_base + 32 * KS + 16 * kk);
-      s0 = T::mfma32(a0, qreg[kk], s0);
-      s1 = T::mfma32(a1, qreg[kk], s1);
+      const s16x8 a0 = *reinterpret_cast<const s16x8*>(sk + kaddr[kk]);
+      const s16x8 a1 = *reinterpret_cast<const s16x8*>(sk + kaddr[kk] + 32 * D);
+#pragma unroll
+      for (int j = 0; j < kRowBlocks; ++j) {
+        s[j][0] = T::mfma32(a0, qreg[j][kk], s[j][0]);
+        s[j][1] = T::mfma32(a1, qreg[j][kk], s[j][1]);
+      }
     }
     if (need_mask) {
-      // key kl of the tile is visible to this lane's row iff kl < lim
-      const int lim = pre ? count : min(count, i_row - base + 1);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
-        s0[rr] = kl < lim ? s0[rr] : -INFINITY;
-        s1[rr] = kl + 32 < lim ? s1[rr] : -INFINITY;
+      for (int j = 0; j < kRowBlocks; ++j) {
+        // key kl of the tile is visible to this lane's row iff kl < lim
+        const int lim = pre ? count : min(count, i_row[j] - base + 1);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
+          s[j][0][rr] = kl < lim ? s[j][0][rr] : -INFINITY;
+          s[j][1][rr] = kl + 32 < lim ? s[j][1][rr] : -INFINITY;
+        }
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx[kRowBlocks];
+    bool need = false;
 #pragma unroll
-    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fmaxf(s0[rr], s1[rr]));
-    mx = fmaxf(mx, xor_lane(mx, 32)) * c_log2;
-    if (__any(mx > m_run + kPfRescale)) {
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
+    for (int j = 0; j < kRowBlocks; ++j) {
+      float m = fmaxf(s[j][0][0], s[j][1][0]);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
+      for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s[j][0][rr], s[j][1][rr]));
+      mx[j] = fmaxf(m, xor_lane(m, 32)) * c_log2;
+      need |= mx[j] > m_run[j] + kPfRescale;
     }
-    // probabilities, packed as the B operand of the PV product; the row sum adds the
+    if (__any(need)) {
+#pragma unroll
+      for (int j = 0; j < kRowBlocks; ++j) {
+        const float mn = fmaxf(m_run[j], mx[j]);
+        const float alpha = fast_exp2(m_run[j] - mn);
+        m_run[j] = mn;
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) o[j][db][rr] *= alpha;
+      }
+    }
+    // probabilities, packed as the B operand of the PV product; row sums add the
     // rounded values (the ones PV uses) two at a time with a dot product against (1, 1)
-    s16x8 pk[4];
-    float ls = l_run;
+    s16x8 pk[kRowBlocks][4];
 #pragma unroll
-    for (int kp4 = 0; kp4 < 4; ++kp4) {
-      const f32x16& sv4 = (kp4 >> 1) ? s1 : s0;
-      const int r0 = (kp4 & 1) * 8;
-      uint32_t pw[4];
+    for (int j = 0; j < kRowBlocks; ++j) {
+      float ls = l_run[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(sv4[r0 + 2 * e], c_log2, -m_run));
-        const float p1 = fast_exp2(fmaf(sv4[r0 + 2 * e + 1], c_log2, -m_run));
-        pw[e] = pack2<T>(p0, p1);
-        ls = T::dot2(pw[e], T::kOnePair, ls);
+      for (int kp4 = 0; kp4 < 4; ++kp4) {
+        const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[j][mb][r0 + 2 * e], c_log2, -m_run[j]));
+          const float p1 = fast_exp2(fmaf(s[j][mb][r0 + 2 * e + 1], c_log2, -m_run[j]));
+          pw[e] = pack2<T>(p0, p1);
+          ls = T::dot2(pw[e], T::kOnePair, ls);
+        }
+        pk[j][kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
       }
-      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      l_run[j] = ls;
     }
-    l_run = ls;
-    // O^T += V^T P^T; all eight transposed reads of a d block are issued before its MFMAs
+    // O^T += V^T P^T: each transposed V operand read feeds both row blocks
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       s16x8 a[4];
 #pragma unroll
       for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const uint16_t* src = sv + tr_base + 16 * kp4 * VS + 32 * db;
-        const s16x4 lo = lds_read_tr16(src);
-        const s16x4 hi = lds_read_tr16(src + 8 * VS);
+        const s16x4 lo = lds_read_tr16(sk + vaddr[db][0] + 16 * kp4 * D);
+        const s16x4 hi = lds_read_tr16(sk + vaddr[db][1] + 16 * kp4 * D);
         a[kp4] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int kp4 = 0; kp4 < 4; ++kp4) o[db] = T::mfma32(a[kp4], pk[kp4], o[db]);
+      for (int j = 0; j < kRowBlocks; ++j)
+#pragma unroll
+        for (int kp4 = 0; kp4 < 4; ++kp4) o[j][db] = T::mfma32(a[kp4], pk[j][kp4], o[j][db]);
     }
   };
 
-  int ids[4];
-  tile_blocks(0, ids);
-  load_tile(0, ids);
-  store_tile(0);
-  tile_blocks(1, ids);
+  int ids[1];
+  tile_blocks(ld_tile, ids);
+  load_tile(ld_tile, ids, 0);
+  tile_blocks(2 + ld_tile, ids);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < total; ++t) {
-    load_tile(t + 1, ids);                  // in flight during this tile's math
-    tile_blocks(t + 2, ids);
-    if (wave_active) compute(t, t & 1);
-    store_tile((t + 1) & 1);
+  for (int st = 0; st < nstage; ++st) {
+    load_tile(2 * st + 2 + ld_tile, ids, (st + 1) & 1);   // next stage, lands during this one
+    tile_blocks(2 * st + 4 + ld_tile, ids);
+    const int t = 2 * st + kh;
+    if (wave_active && t < total) compute(t, smem + (kh * 2 + (st & 1)) * L::TILE);
+    __builtin_amdgcn_s_waitcnt(0);          // this wave's LDS-direct loads have landed
     __syncthreads();
   }
 
-  // epilogue: normalise and store (lane owns one query row, d in runs of 4)
-  const float l_tot = l_run + xor_lane(l_run, 32);
-  if (!rvalid) return;
-  const float inv = 1.0f / l_tot;
-  uint16_t* orow = out + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D;
+  // Merge the two key halves of each row group through LDS (the stage buffers are free):
+  // key-half 1 waves publish (output, max, sum); key-half 0 waves combine and store.
+  float* mbuf = reinterpret_cast<float*>(smem);
+  constexpr int OPW = kRowBlocks * NDB * 16;       // output floats per lane
+  static_assert((2 * (OPW + 2 * kRowBlocks) * 64) * 4 <= 4 * L::TILE * 2, "merge buffer fits");
+  float* my = mbuf + rw * (OPW + 2 * kRowBlocks) * 64;
+  if (kh == 1) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int j = 0; j < kRowBlocks; ++j) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * db + r4 * 8 + hf * 4;
-      uint2 u;
-      u.x = pack2<T>(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
-      u.y = pack2<T>(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d) = u;
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) my[((j * NDB + db) * 16 + rr) * 64 + lane] = o[j][db][rr];
+      my[(OPW + 2 * j) * 64 + lane] = m_run[j];
+      my[(OPW + 2 * j + 1) * 64 + lane] = l_run[j];
     }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int j = 0; j < kRowBlocks; ++j) {
+    const float m1 = my[(OPW + 2 * j) * 64 + lane];
+    const float l1 = my[(OPW + 2 * j + 1) * 64 + lane];
+    const float M = fmaxf(m_run[j], m1);
+    const float a0 = fast_exp2(m_run[j] - M), a1 = fast_exp2(m1 - M);
+    float lt = l_run[j] * a0 + l1 * a1;
+    lt += xor_lane(lt, 32);
+    if (!rvalid[j]) continue;
+    const float inv0 = a0 / lt, inv1 = a1 / lt;
+    uint16_t* orow = out + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + r4 * 8 + hf * 4;
+        float vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vals[e] = o[j][db][4 * r4 + e] * inv0 + my[((j * NDB + db) * 16 + 4 * r4 + e) * 64 + lane] * inv1;
+        uint2 uu;
+        uu.x = pack2<T>(vals[0], vals[1]);
+        uu.y = pack2<T>(vals[2], vals[3]);
+        *reinterpret_cast<uint2*>(orow + d) = uu;
+      }
+  }
 }
 
 template <typename T, int D>
