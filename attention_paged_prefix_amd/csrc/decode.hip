@@ -184,6 +184,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
     if (__any(mx > m_run + kRescaleThreshold)) {
+      keep_branch();
       const float mn = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - mn);
       m_run = mn;

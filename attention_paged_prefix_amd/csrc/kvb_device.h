@@ -89,7 +89,11 @@ template <> __device__ inline uint32_t pack2<BF16>(float a, float b) {
 // t/4+12 of its group, in that order.  With source lane s pointing at row (r0 + s/4),
 // columns (c0 + 4*(s%4)) .. +3 of a row-major 16-bit matrix, lane t receives column
 // c0 + t of rows r0 .. r0+3.
-__device__ inline s16x4 lds_read_tr16(const uint16_t* p) {
+// The restrict-qualified pointer gives the read alias-scope information once inlined.
+// Without it the compiler waits for every outstanding LDS-direct buffer load before the
+// read, including loads into a different LDS buffer; callers that read memory filled by
+// LDS-direct loads must therefore wait for those loads themselves (s_waitcnt + barrier).
+__device__ __attribute__((always_inline)) inline s16x4 lds_read_tr16(const uint16_t* __restrict__ p) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
@@ -127,6 +131,10 @@ __device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) 
 constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond any num_records used here
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Placed inside a rarely taken branch so the compiler keeps the branch instead of
+// speculating the block into selects that would then run on every iteration.
+__device__ inline void keep_branch() { asm volatile("" ::: "memory"); }
 
 // 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at
 // lds + 16*L (the LDS base must be wave-uniform).  Out-of-range lanes write zeros.

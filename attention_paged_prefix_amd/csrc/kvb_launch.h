@@ -6,6 +6,20 @@
 
 namespace kvb {
 
+// Compute units of the current device (queried once per device, then cached).
+inline int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_write_kv(const kvb_pool& p, const void* kn, const void* vn, const int64_t* slots,
                            int num_tokens, hipStream_t s);
 hipError_t launch_gather_kv(const kvb_pool& p, const int32_t* bt, int bt_stride,

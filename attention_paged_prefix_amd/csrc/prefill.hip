@@ -33,8 +33,6 @@
 namespace kvb {
 
 constexpr int kRowWaves = 4;             // waves along the rows (32 rows each)
-constexpr int kPfWaves = 2 * kRowWaves;  // two key halves
-constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kRowBlocks = 1;            // 32-row MFMA blocks per wave
 constexpr int kBM = 32 * kRowBlocks * kRowWaves;  // virtual rows per work-group
 constexpr int kKT = 64;                  // keys per tile
@@ -74,12 +72,15 @@ template <int D> struct PfLayout {
   }
 };
 
-// Work-group = 8 waves (two per SIMD).  Wave w handles the 32 virtual rows
-// 32*(w & 3) .. +31 of the work-group's 128 and the key tiles t with t % 2 == (w >> 2):
-// the two waves of a row group split the keys and merge their (output, max, sum)
-// through LDS at the end.  A stage holds two tiles; stages are double buffered in LDS.
-template <typename T, int D>
-__global__ void __launch_bounds__(kPfThreads, 1)
+// Work-group = 4 * KS waves.  Wave w handles the 32 virtual rows 32*(w & 3) .. +31 of
+// the work-group's 128 and the key tiles t with t % KS == (w >> 2).  With KS = 2 (small
+// grids: 8 waves, one work-group per CU) the two waves of a row group split the keys
+// and merge their (output, max, sum) through LDS at the end; with KS = 1 (large grids)
+// two independent 4-wave work-groups share a CU and drift out of phase, so one group's
+// softmax overlaps the other's MFMAs.  A stage holds KS tiles; stages are double
+// buffered in LDS.
+template <typename T, int D, int KS>
+__global__ void __launch_bounds__(256 * KS, 2 / KS)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
@@ -94,7 +95,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr int NLD = CPR / 4;               // 1 KiB load instructions per 16-row block
   constexpr int VOFF = kKT * D;              // V rows follow K rows in a tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * L::TILE];  // [key half][stage]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KS * L::TILE];  // [key part][stage]
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -114,7 +115,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
   const int lr = lane & 31, hf = lane >> 5;
-  const int rw = w & (kRowWaves - 1), kh = w / kRowWaves;   // row group, key half
+  const int rw = w & (kRowWaves - 1), kh = w / kRowWaves;   // row group, key part
 
   // this lane's two query rows
   int i_row[kRowBlocks], g_row[kRowBlocks];
@@ -141,7 +142,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int n_pre = (P + kKT - 1) / kKT;
   const int n_self = (self_n + kKT - 1) / kKT;
   const int total = n_pre + n_self;
-  const int nstage = (total + 1) / 2;
+  const int nstage = (total + KS - 1) / KS;
 
   f32x16 o[kRowBlocks][NDB];
 #pragma unroll
@@ -152,21 +153,21 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 #pragma unroll
   for (int j = 0; j < kRowBlocks; ++j) { m_run[j] = kPfNegBig; l_run[j] = 0.f; }
 
-  // ---- loader: waves 0-3 stage the even tile of a stage, waves 4-7 the odd one; within
-  // a tile wave (w & 3) loads block (w & 3).  Instruction m of a block fills LDS chunks
+  // ---- loader: waves 4k..4k+3 stage tile k of a stage; within a tile wave (w & 3)
+  // loads block (w & 3).  Instruction m of a block fills LDS chunks
   // 64m..64m+63 of that block; lane L's chunk holds row (64m+L)/CPR, logical chunk
   // inv(row, (64m+L)%CPR).
   const int ld_tile = w / kRowWaves, ld_blk = w & (kRowWaves - 1);
-  uint32_t offK_pool[NLD], offV_pool[NLD], offK_self[NLD], offV_self[NLD];
+  // byte offset of lane's chunk = row * (source row pitch) + column bytes; the pitch is
+  // D*2 in the pool and hkv*D*2 in the chunk's own K/V, chosen per tile (uniform)
+  uint32_t ld_row[NLD], ld_colK[NLD], ld_colV[NLD];
 #pragma unroll
   for (int m = 0; m < NLD; ++m) {
     const int pos = 64 * m + lane;
     const int rb = pos / CPR, cp = pos - (pos / CPR) * CPR;
-    const int ck = L::invK(rb, cp), cv = L::invV(rb, cp);
-    offK_pool[m] = (uint32_t)(rb * D + ck * 8) * 2;
-    offV_pool[m] = (uint32_t)(rb * D + cv * 8) * 2;
-    offK_self[m] = (uint32_t)(rb * hkv * D + ck * 8) * 2;
-    offV_self[m] = (uint32_t)(rb * hkv * D + cv * 8) * 2;
+    ld_row[m] = (uint32_t)rb;
+    ld_colK[m] = (uint32_t)L::invK(rb, cp) * 16;
+    ld_colV[m] = (uint32_t)L::invV(rb, cp) * 16;
   }
   const int32_t* bt_row = bt + (int64_t)b * bt_stride;
   const int64_t head_off = (int64_t)kvh * kBlock * D;
@@ -204,11 +205,13 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       const uint32_t nb = pre ? (pb >= 0 ? (uint32_t)(rows_pre * D * 2) : 0u)
                               : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nb), rv = make_rsrc(vb, nb);
+      const uint32_t pitch = uniform(pre ? D * 2 : (int)self_row_bytes);
 #pragma unroll
       for (int m = 0; m < NLD; ++m) {
         uint16_t* dk = dst + (kBlock * i * CPR + 64 * m) * 8;
-        buf_load16_lds(rk, pre ? offK_pool[m] : offK_self[m], dk);
-        buf_load16_lds(rv, pre ? offV_pool[m] : offV_self[m], dk + VOFF);
+        const uint32_t rowoff = ld_row[m] * pitch;
+        buf_load16_lds(rk, rowoff + ld_colK[m], dk);
+        buf_load16_lds(rv, rowoff + ld_colV[m], dk + VOFF);
       }
     }
   };
@@ -254,6 +257,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       }
     }
     if (need_mask) {
+      keep_branch();
 #pragma unroll
       for (int j = 0; j < kRowBlocks; ++j) {
         // key kl of the tile is visible to this lane's row iff kl < lim
@@ -277,6 +281,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       need |= mx[j] > m_run[j] + kPfRescale;
     }
     if (__any(need)) {
+      keep_branch();
 #pragma unroll
       for (int j = 0; j < kRowBlocks; ++j) {
         const float mn = fmaxf(m_run[j], mx[j]);
@@ -330,13 +335,13 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   int ids[1];
   tile_blocks(ld_tile, ids);
   load_tile(ld_tile, ids, 0);
-  tile_blocks(2 + ld_tile, ids);
+  tile_blocks(KS + ld_tile, ids);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int st = 0; st < nstage; ++st) {
-    load_tile(2 * st + 2 + ld_tile, ids, (st + 1) & 1);   // next stage, lands during this one
-    tile_blocks(2 * st + 4 + ld_tile, ids);
-    const int t = 2 * st + kh;
+    load_tile(KS * st + KS + ld_tile, ids, (st + 1) & 1);   // next stage, lands during this one
+    tile_blocks(KS * st + 2 * KS + ld_tile, ids);
+    const int t = KS * st + kh;
     if (wave_active && t < total) compute(t, smem + (kh * 2 + (st & 1)) * L::TILE);
     __builtin_amdgcn_s_waitcnt(0);          // this wave's LDS-direct loads have landed
     __syncthreads();
@@ -346,8 +351,30 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // key-half 1 waves publish (output, max, sum); key-half 0 waves combine and store.
   float* mbuf = reinterpret_cast<float*>(smem);
   constexpr int OPW = kRowBlocks * NDB * 16;       // output floats per lane
-  static_assert((2 * (OPW + 2 * kRowBlocks) * 64) * 4 <= 4 * L::TILE * 2, "merge buffer fits");
+  static_assert(KS == 1 || (kRowWaves * (OPW + 2 * kRowBlocks) * 64) * 4 <= 2 * KS * L::TILE * 2,
+                "merge buffer fits");
   float* my = mbuf + rw * (OPW + 2 * kRowBlocks) * 64;
+  if (KS == 1) {
+#pragma unroll
+    for (int j = 0; j < kRowBlocks; ++j) {
+      float lt = l_run[j];
+      lt += xor_lane(lt, 32);
+      if (!rvalid[j]) continue;
+      const float inv = 1.0f / lt;
+      uint16_t* orow = out + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * db + r4 * 8 + hf * 4;
+          uint2 uu;
+          uu.x = pack2<T>(o[j][db][4 * r4 + 0] * inv, o[j][db][4 * r4 + 1] * inv);
+          uu.y = pack2<T>(o[j][db][4 * r4 + 2] * inv, o[j][db][4 * r4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = uu;
+        }
+    }
+    return;
+  }
   if (kh == 1) {
 #pragma unroll
     for (int j = 0; j < kRowBlocks; ++j) {
@@ -402,11 +429,21 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   // scale 0 (all scores equal) is kept positive so masked -inf scores stay -inf
   const float c = fmaxf(scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((prefill_kernel<T, D>), dim3((unsigned)padded), dim3(kPfThreads), 0, s,
-                     (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
-                     (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
-                     cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                     (int)padded, (int)real);
+  // Up to two work-groups per CU fit: with fewer work-groups than 2 x CUs the keys are
+  // split inside each work-group instead, so every SIMD still runs two waves.
+  const bool split = real < 2LL * device_cu_count();
+  if (split)
+    hipLaunchKernelGGL((prefill_kernel<T, D, 2>), dim3((unsigned)padded), dim3(512), 0, s,
+                       (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
+                       (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
+                       cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
+                       (int)padded, (int)real);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, D, 1>), dim3((unsigned)padded), dim3(256), 0, s,
+                       (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
+                       (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
+                       cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
+                       (int)padded, (int)real);
   return hipGetLastError();
 }
 

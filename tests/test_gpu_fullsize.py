@@ -1,0 +1,82 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the benchmark
+times (default split plan for decode), on sampled outputs the oracle computes one row
+at a time: first and last rows, rows on tile and block edges, and a few random rows,
+for query heads at GQA group edges."""
+import numpy as np
+import pytest
+
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _util():
+    import gpu_util
+    return gpu_util
+
+
+def _rows(C, rng):
+    cand = {0, 1, 15, 16, 31, 32, 63, 64, 127, 128, C // 2, C - 2, C - 1}
+    cand |= set(int(x) for x in rng.integers(0, C, size=4))
+    return sorted(r for r in cand if 0 <= r < C)
+
+
+def _heads(hq, hkv, rng):
+    G = hq // hkv
+    cand = {0, G - 1, G, hq - 1, int(rng.integers(0, hq))}
+    return sorted(h for h in cand if 0 <= h < hq)
+
+
+@pytest.mark.parametrize("name", ["shared_prompt", "long_prefix", "ragged_d96", "ragged_d64"])
+def test_prefill_full_size_sampled(name):
+    u = _util()
+    w = make_config(name, poison=True)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.prefill())
+    torch.cuda.synchronize()
+    import oracle
+    vals = oracle.decode_bits(got, w.dtype)
+    assert np.isfinite(vals).all()
+    rng = np.random.default_rng(99)
+    B = w.batch
+    seqs = sorted(set([0, B - 1] + [int(x) for x in rng.integers(0, B, size=min(B, 4))]))
+    select = []
+    for b in seqs:
+        C = int(w.q_lens[b])
+        if C == 0:
+            continue
+        rows = _rows(C, rng)
+        for h in _heads(w.num_q_heads, w.num_kv_heads, rng):
+            select.append((b, h, rows))
+    ref = oracle.paged_prefill(w.k_pool, w.v_pool, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens,
+                               w.block_tables, w.num_q_heads, w.scale, w.dtype, select=select)
+    worst = 0.0
+    for (b, h, rows) in select:
+        g = vals[w.cu_q_lens[b] + np.asarray(rows), h]
+        worst = max(worst, float(np.max(np.abs(g - ref[(b, h)]))))
+    assert worst <= u.TOL[w.dtype], f"max abs err {worst}"
+
+
+def test_decode_full_size_sampled():
+    u = _util()
+    w = make_config("decode", poison=True)
+    dev = u.Dev(w)
+    got = u.to_bits(dev.decode(split_blocks=0))
+    torch.cuda.synchronize()
+    import oracle
+    vals = oracle.decode_bits(got, w.dtype)
+    assert np.isfinite(vals).all()
+    rng = np.random.default_rng(98)
+    seqs = sorted(set([0, w.batch - 1] + [int(x) for x in rng.integers(0, w.batch, size=10)]))
+    ref = oracle.paged_decode(w.k_pool, w.v_pool, w.q, w.context_lens, w.block_tables, w.scale,
+                              w.dtype, seqs=seqs)
+    err = float(np.max(np.abs(vals[seqs] - ref[seqs])))
+    assert err <= u.TOL[w.dtype], f"max abs err {err}"

@@ -101,6 +101,29 @@ def test_prefill_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+# Grids of at least two work-groups per compute unit take the kernel variant without
+# the in-group key split; these shapes are large enough for that on any device here.
+LARGE_GRID_CASES = [
+    (211, "bf16", 32, 8, 128, [100, 700, 0, 2000], [520, 600, 700, 300], "pairs"),
+    (212, "fp16", 32, 8, 96, [1500, 33, 0, 640], [700, 640, 511, 257], "none"),
+    (213, "bf16", 32, 8, 64, [64, 64, 900, 17], [700, 690, 650, 700], "all"),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_GRID_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+def test_prefill_large_grid_matches_oracle(case):
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    G = hq // hkv
+    groups = len(P) * hkv * ((max(C) * G + 127) // 128)
+    assert groups >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
+    got = u.to_bits(u.Dev(w).prefill())
+    ref = u.oracle_prefill(w)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
 def test_prefill_tiny_config_and_row0_bit_exact():
     u = _util()
     w = make_config("tiny", poison=True)
