@@ -17,6 +17,7 @@ kvb_status check_pool(const kvb_pool* p) {
   if (p->num_kv_heads <= 0 || p->num_blocks <= 0) return KVB_ERR_INVALID;
   if (p->block_stride < (int64_t)p->num_kv_heads * 16 * p->head_dim) return KVB_ERR_INVALID;
   if (p->block_stride % 8 != 0) return KVB_ERR_INVALID;
+  if (p->block_stride > 0x7fffffffLL) return KVB_ERR_INVALID;   // kernels take it as 32 bits
   if (!aligned16(p->k) || !aligned16(p->v)) return KVB_ERR_INVALID;
   return KVB_OK;
 }

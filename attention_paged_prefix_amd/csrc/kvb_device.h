@@ -108,6 +108,34 @@ __device__ inline float quad_xor2(float x) {
 
 __device__ inline float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Both halves of a wave exchanged (lane l <-> lane l^32) with gfx950's v_permlane32_swap,
+// which swaps lanes 32..63 of its first operand with lanes 0..31 of its second.  With x in
+// both operands, the pair then holds (x[l], x[l^32]) in some order in every lane, so
+// max/sum of the pair is the reduction over the two halves.  Written as (non-volatile)
+// inline assembly: the compiler folds the intrinsic's two results into one when both
+// inputs are the same value.  The s_nop covers the VALU-write -> permlane-read hazard.
+__device__ inline void half_swap(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline float halves_max(float x) {
+  float a, b;
+  half_swap(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float halves_sum(float x) {
+  float a, b;
+  half_swap(x, a, b);
+  return a + b;
+}
+
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmem = 0x010;
+constexpr int kSchedDsRead = 0x100;
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer resources (gfx9 family dword3).  Loads at byte offsets >= num_records
@@ -129,6 +157,10 @@ __device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond any num_records used here
+// One dword into a vector register (the same value in every lane for a uniform offset).
+__device__ inline uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
+}
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

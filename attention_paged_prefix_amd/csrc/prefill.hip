@@ -33,8 +33,7 @@
 namespace kvb {
 
 constexpr int kRowWaves = 4;             // waves along the rows (32 rows each)
-constexpr int kRowBlocks = 1;            // 32-row MFMA blocks per wave
-constexpr int kBM = 32 * kRowBlocks * kRowWaves;  // virtual rows per work-group
+constexpr int kBM = 32 * kRowWaves;      // virtual rows per work-group
 constexpr int kKT = 64;                  // keys per tile
 constexpr float kPfNegBig = -1.0e30f;
 constexpr float kPfRescale = 8.0f;       // log2 units
@@ -73,12 +72,17 @@ template <int D> struct PfLayout {
 };
 
 // Work-group = 4 * KS waves.  Wave w handles the 32 virtual rows 32*(w & 3) .. +31 of
-// the work-group's 128 and the key tiles t with t % KS == (w >> 2).  With KS = 2 (small
-// grids: 8 waves, one work-group per CU) the two waves of a row group split the keys
-// and merge their (output, max, sum) through LDS at the end; with KS = 1 (large grids)
-// two independent 4-wave work-groups share a CU and drift out of phase, so one group's
-// softmax overlaps the other's MFMAs.  A stage holds KS tiles; stages are double
-// buffered in LDS.
+// the work-group's 128 and the key tiles t with t % KS == (w >> 2) ("key part").  With
+// KS = 2 (small grids: 8 waves, one work-group per CU) the two waves of a row group split
+// the keys and merge their (output, max, sum) through LDS at the end; with KS = 1 (large
+// grids) two independent 4-wave work-groups share a CU.
+//
+// Step j of a key part covers its tile KS*j + part.  The loop is software pipelined
+// inside each wave: step j issues the S MFMAs of tile j+1 while the VALU turns tile j's
+// scores into probabilities, then the PV MFMAs of tile j while the VALU takes tile j+1's
+// row max and scales its scores.  K is therefore staged one tile ahead of V: LDS holds
+// two K buffers and two V buffers per key part; step j loads K of tile j+2 and V of tile
+// j+1, and one barrier per step publishes them.
 template <typename T, int D, int KS>
 __global__ void __launch_bounds__(256 * KS, 2 / KS)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -93,9 +97,12 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
   constexpr int NDB = D / 32;                // 32-wide d blocks of the output
   constexpr int NLD = CPR / 4;               // 1 KiB load instructions per 16-row block
-  constexpr int VOFF = kKT * D;              // V rows follow K rows in a tile
+  constexpr int HT = kKT * D;                // elements of one K (or V) tile
+  constexpr int NQK = 2 * NKK;               // S MFMAs per tile (= K operand reads)
+  constexpr int NPV = 4 * NDB;               // PV MFMAs per tile (2 V reads each)
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KS * L::TILE];  // [key part][stage]
+  // [key part][parity][K | V][64 x D]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT];
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -117,24 +124,21 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int lr = lane & 31, hf = lane >> 5;
   const int rw = w & (kRowWaves - 1), kh = w / kRowWaves;   // row group, key part
 
-  // this lane's two query rows
-  int i_row[kRowBlocks], g_row[kRowBlocks];
-  bool rvalid[kRowBlocks];
-  s16x8 qreg[kRowBlocks][NKK];
-#pragma unroll
-  for (int j = 0; j < kRowBlocks; ++j) {
-    const int v = v0 + 32 * kRowBlocks * rw + 32 * j + lr;
-    rvalid[j] = v < nrows;
-    i_row[j] = rvalid[j] ? v / G : C;
-    g_row[j] = rvalid[j] ? v - (v / G) * G : 0;
-    const uint16_t* qrow = q + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D + 8 * hf;
+  // this lane's query row (virtual row v = i*G + g)
+  const int vrow = v0 + 32 * rw + lr;
+  const bool rvalid = vrow < nrows;
+  const int i_row = rvalid ? vrow / G : C;
+  const int g_row = rvalid ? vrow - (vrow / G) * G : 0;
+  s16x8 qreg[NKK];
+  {
+    const uint16_t* qrow = q + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (rvalid[j]) qreg[j][kk] = *reinterpret_cast<const s16x8*>(qrow + 16 * kk);
-      else qreg[j][kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (rvalid) qreg[kk] = *reinterpret_cast<const s16x8*>(qrow + 16 * kk);
+      else qreg[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  const bool wave_active = v0 + 32 * kRowBlocks * rw < nrows;
+  const bool wave_active = v0 + 32 * rw < nrows;
 
   const int last_row = min(nrows, v0 + kBM) - 1;
   const int self_n = last_row / G + 1;       // chunk keys needed by this work-group
@@ -144,22 +148,17 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int total = n_pre + n_self;
   const int nstage = (total + KS - 1) / KS;
 
-  f32x16 o[kRowBlocks][NDB];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int j = 0; j < kRowBlocks; ++j)
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) o[j][i] = f32x16{};
-  float m_run[kRowBlocks], l_run[kRowBlocks];
-#pragma unroll
-  for (int j = 0; j < kRowBlocks; ++j) { m_run[j] = kPfNegBig; l_run[j] = 0.f; }
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m_run = kPfNegBig, l_run = 0.f;
 
-  // ---- loader: waves 4k..4k+3 stage tile k of a stage; within a tile wave (w & 3)
-  // loads block (w & 3).  Instruction m of a block fills LDS chunks
-  // 64m..64m+63 of that block; lane L's chunk holds row (64m+L)/CPR, logical chunk
-  // inv(row, (64m+L)%CPR).
-  const int ld_tile = w / kRowWaves, ld_blk = w & (kRowWaves - 1);
-  // byte offset of lane's chunk = row * (source row pitch) + column bytes; the pitch is
-  // D*2 in the pool and hkv*D*2 in the chunk's own K/V, chosen per tile (uniform)
+  // ---- loader: the 4 waves of key part kh stage that part's tiles; wave (w & 3) loads
+  // block (w & 3) of a tile.  Instruction m of a block fills LDS chunks 64m..64m+63 of
+  // that block; lane L's chunk holds row (64m+L)/CPR, logical chunk inv(row, (64m+L)%CPR).
+  // Byte offset = row * (source row pitch) + column bytes; the pitch is D*2 in the pool
+  // and hkv*D*2 in the chunk's own K/V, chosen per tile.
+  const int ld_blk = w & (kRowWaves - 1);
   uint32_t ld_row[NLD], ld_colK[NLD], ld_colV[NLD];
 #pragma unroll
   for (int m = 0; m < NLD; ++m) {
@@ -170,6 +169,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     ld_colV[m] = (uint32_t)L::invV(rb, cp) * 16;
   }
   const int32_t* bt_row = bt + (int64_t)b * bt_stride;
+  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt_row, (uint32_t)min(bt_stride, 1 << 28) * 4u);
   const int64_t head_off = (int64_t)kvh * kBlock * D;
   const uint16_t* kbase = kp + head_off;                          // + block * block_stride
   const uint16_t* vbase = vp + head_off;
@@ -177,47 +177,57 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const uint16_t* vnb = vn + ((int64_t)cu_b * hkv + kvh) * D;
   const uint32_t self_row_bytes = (uint32_t)(hkv * D * 2);
 
-  // block id of this wave's block of prefix tile t (uniform scalar load)
-  auto tile_blocks = [&](int t, int* ids) {
+  uint16_t* const kbuf0 = smem + (kh * 4 + 0) * HT;   // parity 0 K, then V, parity 1 K, V
+  auto kbuf = [&](int par) { return kbuf0 + par * 2 * HT; };
+  auto vbuf = [&](int par) { return kbuf0 + par * 2 * HT + HT; };
+
+  // raw block-table entry for this wave's block of tile t (vector load; 0 when t has no
+  // prefix block here, validity is decided again where the id is used)
+  auto fetch_id = [&](int t) -> uint32_t {
     const int jb = t * 4 + ld_blk;
-    int pb = -1;
-    if (t < n_pre && jb * kBlock < P) pb = bt_row[jb];
-    ids[0] = (pb >= 0 && pb < num_blocks) ? pb : -1;
+    const bool ok = t < n_pre && jb * kBlock < P;
+    return buf_load4(bt_rsrc, ok ? (uint32_t)jb * 4u : kOobOffset);
   };
-
-  // Tile t (prefix tiles first, then the chunk's own tiles) straight into LDS buffer
-  // (ld_tile, stage).  Sources are (base, valid bytes, lane offset) selected with uniform
-  // conditions; rows past the end read as zero; past the last tile every size is zero.
-  auto load_tile = [&](int t, const int* ids, int stage) {
+  // Source of this wave's 16-row block of tile t (prefix tiles first, then the chunk's
+  // own tiles), K or V part: a buffer resource sized to the valid rows (rows past the end
+  // read as zero; past the last tile every size is zero), the row pitch and the LDS
+  // destination.  Everything is a scalar select, so the loop carries no branches here.
+  struct LdDesc {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t pitch;
+    uint16_t* dst;
+  };
+  const uint32_t bs32 = (uint32_t)block_stride;
+  auto make_desc = [&](int t, int pb, uint16_t* dst, const uint16_t* pool_base,
+                       const uint16_t* self_base) -> LdDesc {
     const bool pre = t < n_pre;
-    const int tu = t - n_pre;
-    uint16_t* dst = smem + (ld_tile * 2 + stage) * L::TILE;
-    {
-      const int i = ld_blk;
-      const int pb = ids[0];
-      const int rows_pre = max(0, min(kBlock, P - (t * kKT + kBlock * i)));
-      const int row0 = tu * kKT + kBlock * i;
-      const int rows_self = t < total ? max(0, min(kBlock, self_n - row0)) : 0;
-      const int64_t pre_off = (int64_t)(pb >= 0 ? pb : 0) * block_stride;
-      const int64_t self_row = (int64_t)(pre ? 0 : min(max(row0, 0), C)) * hkv * D;
-      const uint16_t* kb = pre ? kbase + pre_off : knb + self_row;
-      const uint16_t* vb = pre ? vbase + pre_off : vnb + self_row;
-      const uint32_t nb = pre ? (pb >= 0 ? (uint32_t)(rows_pre * D * 2) : 0u)
-                              : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nb), rv = make_rsrc(vb, nb);
-      const uint32_t pitch = uniform(pre ? D * 2 : (int)self_row_bytes);
+    const int jb = t * 4 + ld_blk;
+    const bool pvalid = pre && jb * kBlock < P && (uint32_t)pb < (uint32_t)num_blocks;
+    const int rows_pre = max(0, min(kBlock, P - jb * kBlock));
+    const int row0 = (t - n_pre) * kKT + kBlock * ld_blk;
+    const int rows_self = (!pre && t < total) ? max(0, min(kBlock, self_n - row0)) : 0;
+    const uint32_t mul_a = pre ? (pvalid ? (uint32_t)pb : 0u) : (uint32_t)min(max(row0, 0), C);
+    const uint32_t mul_b = pre ? bs32 : (uint32_t)(hkv * D);
+    const uint16_t* src = (pre ? pool_base : self_base) + (uint64_t)mul_a * mul_b;
+    const uint32_t nb = pre ? (pvalid ? (uint32_t)(rows_pre * D * 2) : 0u)
+                            : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
+    LdDesc d;
+    d.rs = make_rsrc(src, nb);
+    d.pitch = (uint32_t)uniform(pre ? D * 2 : (int)self_row_bytes);
+    d.dst = dst + kBlock * ld_blk * CPR * 8;
+    return d;
+  };
+  // load instruction m (1 KiB) of a part
+  auto issue = [&](const LdDesc& d, const uint32_t* col, int m) {
+    buf_load16_lds(d.rs, ld_row[m] * d.pitch + col[m], d.dst + 64 * m * 8);
+  };
+  auto issue_all = [&](const LdDesc& d, const uint32_t* col) {
 #pragma unroll
-      for (int m = 0; m < NLD; ++m) {
-        uint16_t* dk = dst + (kBlock * i * CPR + 64 * m) * 8;
-        const uint32_t rowoff = ld_row[m] * pitch;
-        buf_load16_lds(rk, rowoff + ld_colK[m], dk);
-        buf_load16_lds(rv, rowoff + ld_colV[m], dk + VOFF);
-      }
-    }
+    for (int m = 0; m < NLD; ++m) issue(d, col, m);
   };
 
-  // ---- per-lane LDS read addresses (elements, relative to a tile)
-  // K operand of row block mb: row 32*mb + lr, logical chunk 2*kk + hf (mb adds 32 rows)
+  // ---- per-lane LDS read addresses (elements, relative to a K or V tile)
+  // K operand: row 32*half + lr, logical chunk 2*kk + hf
   int kaddr[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = (lr * CPR + L::posK(lr, 2 * kk + hf)) * 8;
@@ -232,188 +242,307 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       for (int hi = 0; hi < 2; ++hi) {
         const int row = 4 * hf + s4 + 8 * hi;
         const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-        vaddr[db][hi] = VOFF + (row * CPR + L::posV(row, c)) * 8 + 4 * (lane & 1);
+        vaddr[db][hi] = (row * CPR + L::posV(row, c)) * 8 + 4 * (lane & 1);
       }
   }
 
-  auto compute = [&](int t, const uint16_t* sk) {
+  // S^T = K Q^T for one tile: s[half] holds keys 32*half + (MFMA row), this lane's row
+  auto qk = [&](const uint16_t* kb, f32x16* s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const s16x8 a0 = *reinterpret_cast<const s16x8*>(kb + kaddr[kk]);
+      const s16x8 a1 = *reinterpret_cast<const s16x8*>(kb + kaddr[kk] + 32 * D);
+      s[0] = T::mfma32(a0, qreg[kk], s[0]);
+      s[1] = T::mfma32(a1, qreg[kk], s[1]);
+    }
+  };
+  // keys of tile t this lane's row may not see -> -inf (only tiles that need it)
+  auto tile_needs_mask = [&](int t) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
-    const bool need_mask = (count < kKT) || (!pre && base + kKT - 1 > i_first);
-
-    // S^T = K Q^T: each K operand read feeds both row blocks
-    f32x16 s[kRowBlocks][2];
+    return (count < kKT) || (!pre && base + kKT - 1 > i_first);
+  };
+  auto mask = [&](int t, f32x16* s) {
+    const bool pre = t < n_pre;
+    const int base = pre ? t * kKT : (t - n_pre) * kKT;
+    const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
+    const int lim = pre ? count : min(count, i_row - base + 1);
 #pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) { s[j][0] = f32x16{}; s[j][1] = f32x16{}; }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const s16x8 a0 = *reinterpret_cast<const s16x8*>(sk + kaddr[kk]);
-      const s16x8 a1 = *reinterpret_cast<const s16x8*>(sk + kaddr[kk] + 32 * D);
-#pragma unroll
-      for (int j = 0; j < kRowBlocks; ++j) {
-        s[j][0] = T::mfma32(a0, qreg[j][kk], s[j][0]);
-        s[j][1] = T::mfma32(a1, qreg[j][kk], s[j][1]);
-      }
-    }
-    if (need_mask) {
-      keep_branch();
-#pragma unroll
-      for (int j = 0; j < kRowBlocks; ++j) {
-        // key kl of the tile is visible to this lane's row iff kl < lim
-        const int lim = pre ? count : min(count, i_row[j] - base + 1);
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
-          s[j][0][rr] = kl < lim ? s[j][0][rr] : -INFINITY;
-          s[j][1][rr] = kl + 32 < lim ? s[j][1][rr] : -INFINITY;
-        }
-      }
-    }
-    float mx[kRowBlocks];
-    bool need = false;
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-      float m = fmaxf(s[j][0][0], s[j][1][0]);
-#pragma unroll
-      for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s[j][0][rr], s[j][1][rr]));
-      mx[j] = fmaxf(m, xor_lane(m, 32)) * c_log2;
-      need |= mx[j] > m_run[j] + kPfRescale;
-    }
-    if (__any(need)) {
-      keep_branch();
-#pragma unroll
-      for (int j = 0; j < kRowBlocks; ++j) {
-        const float mn = fmaxf(m_run[j], mx[j]);
-        const float alpha = fast_exp2(m_run[j] - mn);
-        m_run[j] = mn;
-        l_run[j] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) o[j][db][rr] *= alpha;
-      }
-    }
-    // probabilities, packed as the B operand of the PV product; row sums add the
-    // rounded values (the ones PV uses) two at a time with a dot product against (1, 1)
-    s16x8 pk[kRowBlocks][4];
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-      float ls = l_run[j];
-#pragma unroll
-      for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[j][mb][r0 + 2 * e], c_log2, -m_run[j]));
-          const float p1 = fast_exp2(fmaf(s[j][mb][r0 + 2 * e + 1], c_log2, -m_run[j]));
-          pw[e] = pack2<T>(p0, p1);
-          ls = T::dot2(pw[e], T::kOnePair, ls);
-        }
-        pk[j][kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      }
-      l_run[j] = ls;
-    }
-    // O^T += V^T P^T: each transposed V operand read feeds both row blocks
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      s16x8 a[4];
-#pragma unroll
-      for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const s16x4 lo = lds_read_tr16(sk + vaddr[db][0] + 16 * kp4 * D);
-        const s16x4 hi = lds_read_tr16(sk + vaddr[db][1] + 16 * kp4 * D);
-        a[kp4] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int j = 0; j < kRowBlocks; ++j)
-#pragma unroll
-        for (int kp4 = 0; kp4 < 4; ++kp4) o[j][db] = T::mfma32(a[kp4], pk[j][kp4], o[j][db]);
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
+      s[0][rr] = kl < lim ? s[0][rr] : -INFINITY;
+      s[1][rr] = kl + 32 < lim ? s[1][rr] : -INFINITY;
     }
   };
+  // Row max of a fresh score tile; the running max only moves (and the output is only
+  // rescaled) when a score exceeds it by more than 2^8.  Leaves the scores as
+  // s*c - m (exp2 arguments) and returns whether the output needs rescaling.
+  auto row_max = [&](f32x16* s, float& m_new) -> bool {
+    float m = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s[0][rr], s[1][rr]));
+    const float mx = halves_max(m) * c_log2;
+    const bool any = __any(mx > m_run + kPfRescale);
+    m_new = any ? fmaxf(m_run, mx) : m_run;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      s[0][rr] = fmaf(s[0][rr], c_log2, -m_new);
+      s[1][rr] = fmaf(s[1][rr], c_log2, -m_new);
+    }
+    return any;
+  };
+  auto rescale = [&](float m_new) {
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
+  };
+  // probabilities, packed as the B operand of the PV product; row sums add the rounded
+  // values (the ones PV uses) two at a time with a dot product against (1, 1)
+  auto probs = [&](const f32x16* x, s16x8* pk) {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kp4 = 0; kp4 < 4; ++kp4) {
+      const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = pack2<T>(fast_exp2(x[mb][r0 + 2 * e]), fast_exp2(x[mb][r0 + 2 * e + 1]));
+        if (e & 1) ls1 = T::dot2(pw[e], T::kOnePair, ls1);
+        else ls0 = T::dot2(pw[e], T::kOnePair, ls0);
+      }
+      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    }
+    l_run += ls0 + ls1;
+  };
+  // O^T += V^T P^T
+  auto pv = [&](const uint16_t* vb, const s16x8* pk) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kp4 = 0; kp4 < 4; ++kp4) {
+        const s16x4 lo = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
+        const s16x4 hi = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
+        o[db] = T::mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kp4], o[db]);
+      }
+  };
 
-  int ids[1];
-  tile_blocks(ld_tile, ids);
-  load_tile(ld_tile, ids, 0);
-  tile_blocks(KS + ld_tile, ids);
+  // ---- prologue: K and V of step 0, K of step 1; scores of step 0
+  int pb_next_v;                                    // block id of the next V tile
+  uint32_t id_raw;                                  // raw id of the next K tile (in flight)
+  {
+    const int t0 = kh, t1 = KS + kh;
+    const int jb0 = t0 * 4 + ld_blk, jb1 = t1 * 4 + ld_blk;
+    const int pb0 = (t0 < n_pre && jb0 * kBlock < P) ? bt_row[jb0] : -1;
+    const int pb1 = (t1 < n_pre && jb1 * kBlock < P) ? bt_row[jb1] : -1;
+    issue_all(make_desc(t0, pb0, kbuf(0), kbase, knb), ld_colK);
+    issue_all(make_desc(t0, pb0, vbuf(0), vbase, vnb), ld_colV);
+    issue_all(make_desc(t1, pb1, kbuf(1), kbase, knb), ld_colK);
+    pb_next_v = pb1;
+    id_raw = fetch_id(2 * KS + kh);
+  }
+  f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int st = 0; st < nstage; ++st) {
-    load_tile(KS * st + KS + ld_tile, ids, (st + 1) & 1);   // next stage, lands during this one
-    tile_blocks(KS * st + 2 * KS + ld_tile, ids);
-    const int t = KS * st + kh;
-    if (wave_active && t < total) compute(t, smem + (kh * 2 + (st & 1)) * L::TILE);
-    __builtin_amdgcn_s_waitcnt(0);          // this wave's LDS-direct loads have landed
+  if (wave_active) {
+    qk(kbuf(0), s_cur);
+    if (tile_needs_mask(kh)) mask(kh, s_cur);
+    float m_new;
+    row_max(s_cur, m_new);
+    m_run = m_new;
+  }
+  __syncthreads();                                  // K buffer 0 is reloaded in step 0
+
+  for (int j = 0; j + 1 < nstage; ++j) {
+    const int t_next = KS * (j + 1) + kh;           // scores computed in this step
+    // loads of this step: K of tile j+2 and V of tile j+1 (2*NLD == NKK instructions)
+    const int pb_k = uniform((int)id_raw);
+    const LdDesc dk = make_desc(KS * (j + 2) + kh, pb_k, kbuf(j & 1), kbase, knb);
+    const LdDesc dv = make_desc(t_next, pb_next_v, vbuf((j + 1) & 1), vbase, vnb);
+    pb_next_v = pb_k;
+    id_raw = fetch_id(KS * (j + 3) + kh);
+    if (!wave_active) {
+      issue_all(dk, ld_colK);
+      issue_all(dv, ld_colV);
+    } else {
+      // Hand-interleaved: each step of a phase is a scheduling region of its own, so
+      // operand reads issued there stay two MFMA steps ahead of their use and the VALU
+      // work of the other tile fills the MFMA shadow.
+      // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack).
+      const uint16_t* kb = kbuf((j + 1) & 1);
+      f32x16 s_nxt[2] = {f32x16{}, f32x16{}};
+      s16x8 ka[NKK][2];
+      uint32_t pw[16];
+#pragma unroll
+      for (int kk = 0; kk < 2 && kk < NKK; ++kk) {
+        ka[kk][0] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk]);
+        ka[kk][1] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk] + 32 * D);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        // one load per step: bunched at the step start, the loads of all waves queue at
+        // the memory pipeline and stall the issuing waves
+        static_assert(2 * NLD == NKK, "one load per S step");
+        if (kk < NLD) issue(dk, ld_colK, kk);
+        else issue(dv, ld_colV, kk - NLD);
+        if (kk + 2 < NKK) {
+          ka[kk + 2][0] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk + 2]);
+          ka[kk + 2][1] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk + 2] + 32 * D);
+        }
+        s_nxt[0] = T::mfma32(ka[kk][0], qreg[kk], s_nxt[0]);
+        s_nxt[1] = T::mfma32(ka[kk][1], qreg[kk], s_nxt[1]);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)            // pair e = (kp4 = e/4, element e%4)
+          if (e * NKK / 16 == kk) {
+            const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+            pw[e] = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s16x8 pk[4];
+#pragma unroll
+      for (int kp4 = 0; kp4 < 4; ++kp4)
+        pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[4 * kp4], pw[4 * kp4 + 1], pw[4 * kp4 + 2], pw[4 * kp4 + 3]));
+      // keep the probabilities in phase 1: otherwise they sink past the mask branch
+      asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]));
+      if (tile_needs_mask(t_next)) {
+        keep_branch();
+        mask(t_next, s_nxt);
+      }
+      // Phase 2: PV MFMAs of tile j; row sums of tile j, row max and exp2 arguments of
+      // tile j+1.  VALU work units: 0-3 partial maxima, 4 the wave-wide max and the new
+      // reference, 5-12 scaled scores (4 each), 13-16 row sums (4 dot products each).
+      const uint16_t* vb = vbuf(j & 1);
+      constexpr int NU = 17;
+      s16x4 va[NPV][2];
+      float pmax[4], m_new = m_run, ls[4];
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int db = i >> 2, kp4 = i & 3;
+        va[i][0] = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
+        va[i][1] = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
+      }
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 2 < NPV) {
+          const int db = (i + 2) >> 2, kp4 = (i + 2) & 3;
+          va[i + 2][0] = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
+          va[i + 2][1] = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
+        }
+        {
+          const int db = i >> 2, kp4 = i & 3;
+          o[db] = T::mfma32(__builtin_shufflevector(va[i][0], va[i][1], 0, 1, 2, 3, 4, 5, 6, 7), pk[kp4], o[db]);
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          if (u * NPV / NU != i) continue;
+          if (u < 4) {
+            const int h = u >> 1, r0 = (u & 1) * 8;
+            float m = fmaxf(s_nxt[h][r0], s_nxt[h][r0 + 1]);
+#pragma unroll
+            for (int rr = 2; rr < 8; ++rr) m = fmaxf(m, s_nxt[h][r0 + rr]);
+            pmax[u] = m;
+          } else if (u == 4) {
+            const float mx = halves_max(fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]))) * c_log2;
+            any = __any(mx > m_run + kPfRescale);
+            m_new = any ? fmaxf(m_run, mx) : m_run;
+          } else if (u < 13) {
+            const int h = (u - 5) >> 2, r0 = ((u - 5) & 3) * 4;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_new);
+          } else {
+            const int k0 = (u - 13) * 4;
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 + e], T::kOnePair, a);
+            ls[u - 13] = a;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));   // scaled scores stay in phase 2
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if (any) {
+        keep_branch();
+        rescale(m_new);
+      }
+      m_run = m_new;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
+    }
+    __builtin_amdgcn_s_waitcnt(0);                  // this wave's LDS-direct loads have landed
     __syncthreads();
   }
+  if (wave_active) {
+    s16x8 pk[4];
+    probs(s_cur, pk);
+    pv(vbuf((nstage - 1) & 1), pk);
+  }
 
-  // Merge the two key halves of each row group through LDS (the stage buffers are free):
-  // key-half 1 waves publish (output, max, sum); key-half 0 waves combine and store.
+  // Merge the two key parts of each row group through LDS (the tile buffers are free):
+  // key-part 1 waves publish (output, max, sum); key-part 0 waves combine and store.
   float* mbuf = reinterpret_cast<float*>(smem);
-  constexpr int OPW = kRowBlocks * NDB * 16;       // output floats per lane
-  static_assert(KS == 1 || (kRowWaves * (OPW + 2 * kRowBlocks) * 64) * 4 <= 2 * KS * L::TILE * 2,
-                "merge buffer fits");
-  float* my = mbuf + rw * (OPW + 2 * kRowBlocks) * 64;
+  constexpr int OPW = NDB * 16;                    // output floats per lane
+  static_assert(KS == 1 || (kRowWaves * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
+  float* my = mbuf + rw * (OPW + 2) * 64;
   if (KS == 1) {
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-      float lt = l_run[j];
-      lt += xor_lane(lt, 32);
-      if (!rvalid[j]) continue;
-      const float inv = 1.0f / lt;
-      uint16_t* orow = out + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = 32 * db + r4 * 8 + hf * 4;
-          uint2 uu;
-          uu.x = pack2<T>(o[j][db][4 * r4 + 0] * inv, o[j][db][4 * r4 + 1] * inv);
-          uu.y = pack2<T>(o[j][db][4 * r4 + 2] * inv, o[j][db][4 * r4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + d) = uu;
-        }
-    }
-    return;
-  }
-  if (kh == 1) {
-#pragma unroll
-    for (int j = 0; j < kRowBlocks; ++j) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) my[((j * NDB + db) * 16 + rr) * 64 + lane] = o[j][db][rr];
-      my[(OPW + 2 * j) * 64 + lane] = m_run[j];
-      my[(OPW + 2 * j + 1) * 64 + lane] = l_run[j];
-    }
-  }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int j = 0; j < kRowBlocks; ++j) {
-    const float m1 = my[(OPW + 2 * j) * 64 + lane];
-    const float l1 = my[(OPW + 2 * j + 1) * 64 + lane];
-    const float M = fmaxf(m_run[j], m1);
-    const float a0 = fast_exp2(m_run[j] - M), a1 = fast_exp2(m1 - M);
-    float lt = l_run[j] * a0 + l1 * a1;
-    lt += xor_lane(lt, 32);
-    if (!rvalid[j]) continue;
-    const float inv0 = a0 / lt, inv1 = a1 / lt;
-    uint16_t* orow = out + ((int64_t)(cu_b + i_row[j]) * hq + kvh * G + g_row[j]) * D;
+    float lt = halves_sum(l_run);
+    if (!rvalid) return;
+    const float inv = 1.0f / lt;
+    uint16_t* orow = out + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d = 32 * db + r4 * 8 + hf * 4;
-        float vals[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vals[e] = o[j][db][4 * r4 + e] * inv0 + my[((j * NDB + db) * 16 + 4 * r4 + e) * 64 + lane] * inv1;
         uint2 uu;
-        uu.x = pack2<T>(vals[0], vals[1]);
-        uu.y = pack2<T>(vals[2], vals[3]);
+        uu.x = pack2<T>(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
+        uu.y = pack2<T>(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
         *reinterpret_cast<uint2*>(orow + d) = uu;
       }
+    return;
   }
+  __syncthreads();                                  // every wave is done with the tiles
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) my[(db * 16 + rr) * 64 + lane] = o[db][rr];
+    my[OPW * 64 + lane] = m_run;
+    my[(OPW + 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = my[OPW * 64 + lane];
+  const float l1 = my[(OPW + 1) * 64 + lane];
+  const float M = fmaxf(m_run, m1);
+  const float a0 = fast_exp2(m_run - M), a1 = fast_exp2(m1 - M);
+  const float lt = halves_sum(l_run * a0 + l1 * a1);
+  if (!rvalid) return;
+  const float inv0 = a0 / lt, inv1 = a1 / lt;
+  uint16_t* orow = out + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + r4 * 8 + hf * 4;
+      float vals[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vals[e] = o[db][4 * r4 + e] * inv0 + my[(db * 16 + 4 * r4 + e) * 64 + lane] * inv1;
+      uint2 uu;
+      uu.x = pack2<T>(vals[0], vals[1]);
+      uu.y = pack2<T>(vals[2], vals[3]);
+      *reinterpret_cast<uint2*>(orow + d) = uu;
+    }
 }
 
 template <typename T, int D>

@@ -53,7 +53,8 @@ typedef enum { KVB_FP16 = 0, KVB_BF16 = 1 } kvb_dtype;
 /* The K/V block pool.  Layout of each of k and v (device):
  *   element (block, kv_head, row, e) at  block*block_stride + (kv_head*16 + row)*head_dim + e
  * so one (block, kv-head) tile is a contiguous 16 x head_dim run (4 KiB at head_dim 128 in
- * 16-bit types).  block_stride (elements) >= num_kv_heads*16*head_dim and a multiple of 8;
+ * 16-bit types).  block_stride (elements) >= num_kv_heads*16*head_dim, a multiple of 8 and
+ * below 2^31 (the byte offset of a block, block*block_stride*2, may exceed 32 bits);
  * setting v = k + num_kv_heads*16*head_dim and block_stride = 2*num_kv_heads*16*head_dim
  * interleaves K and V per block, which is exactly one page of the kvstream formula. */
 typedef struct {

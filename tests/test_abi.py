@@ -62,6 +62,7 @@ def test_write_kv_validation(lib):
     assert write(lib, pool(dtype=7)) == UNSUP
     assert write(lib, pool(block_stride=100)) == INVALID
     assert write(lib, pool(block_stride=2 * 16 * 128 + 4)) == INVALID
+    assert write(lib, pool(block_stride=1 << 31)) == INVALID
     assert write(lib, pool(num_kv_heads=0)) == INVALID
     assert write(lib, pool(k=FAKE + 2)) == INVALID
     assert write(lib, pool(), n=-1) == INVALID
