@@ -27,6 +27,8 @@
 //    running max only moves (and the output is only rescaled) when a score exceeds it
 //    by more than 2^8.  Only tiles crossing the causal diagonal or the end of the keys
 //    are masked; tiles entirely in the future of every row are never visited.
+#include <type_traits>
+
 #include "kvb_device.h"
 #include "kvb_launch.h"
 
@@ -98,8 +100,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr int NDB = D / 32;                // 32-wide d blocks of the output
   constexpr int NLD = CPR / 4;               // 1 KiB load instructions per 16-row block
   constexpr int HT = kKT * D;                // elements of one K (or V) tile
-  constexpr int NQK = 2 * NKK;               // S MFMAs per tile (= K operand reads)
+  constexpr uint32_t HTB = HT * 2;           // bytes of one K (or V) tile
   constexpr int NPV = 4 * NDB;               // PV MFMAs per tile (2 V reads each)
+  static_assert(2 * NLD == NKK, "one load per S step");
 
   // [key part][parity][K | V][64 x D]
   __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT];
@@ -122,7 +125,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
   const int lr = lane & 31, hf = lane >> 5;
-  const int rw = w & (kRowWaves - 1), kh = w / kRowWaves;   // row group, key part
+  const int rw = w & (kRowWaves - 1);                       // row group
+  const int kh = KS == 1 ? 0 : w / kRowWaves;                // key part
 
   // this lane's query row (virtual row v = i*G + g)
   const int vrow = v0 + 32 * rw + lr;
@@ -153,11 +157,17 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m_run = kPfNegBig, l_run = 0.f;
 
+  // ---- LDS: key part kh owns 4 tile buffers (bytes): K parity 0, V parity 0, K parity 1,
+  // V parity 1.  All read and write addresses are a per-lane register plus a constant.
+  char* const lds = reinterpret_cast<char*>(smem);
+  const uint32_t part_base = (uint32_t)(kh * 4 * HTB);
+  constexpr uint32_t kOffK0 = 0, kOffV0 = HTB, kOffK1 = 2 * HTB, kOffV1 = 3 * HTB;
+
   // ---- loader: the 4 waves of key part kh stage that part's tiles; wave (w & 3) loads
   // block (w & 3) of a tile.  Instruction m of a block fills LDS chunks 64m..64m+63 of
   // that block; lane L's chunk holds row (64m+L)/CPR, logical chunk inv(row, (64m+L)%CPR).
   // Byte offset = row * (source row pitch) + column bytes; the pitch is D*2 in the pool
-  // and hkv*D*2 in the chunk's own K/V, chosen per tile.
+  // and hkv*D*2 in the chunk's own K/V.
   const int ld_blk = w & (kRowWaves - 1);
   uint32_t ld_row[NLD], ld_colK[NLD], ld_colV[NLD];
 #pragma unroll
@@ -168,72 +178,88 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     ld_colK[m] = (uint32_t)L::invK(rb, cp) * 16;
     ld_colV[m] = (uint32_t)L::invV(rb, cp) * 16;
   }
+  const uint32_t ld_dst = part_base + (uint32_t)(kBlock * ld_blk * CPR * 16);
   const int32_t* bt_row = bt + (int64_t)b * bt_stride;
-  const __amdgpu_buffer_rsrc_t bt_rsrc = make_rsrc(bt_row, (uint32_t)min(bt_stride, 1 << 28) * 4u);
   const int64_t head_off = (int64_t)kvh * kBlock * D;
   const uint16_t* kbase = kp + head_off;                          // + block * block_stride
   const uint16_t* vbase = vp + head_off;
   const uint16_t* knb = kn + ((int64_t)cu_b * hkv + kvh) * D;     // + row * hkv * D
   const uint16_t* vnb = vn + ((int64_t)cu_b * hkv + kvh) * D;
   const uint32_t self_row_bytes = (uint32_t)(hkv * D * 2);
-
-  uint16_t* const kbuf0 = smem + (kh * 4 + 0) * HT;   // parity 0 K, then V, parity 1 K, V
-  auto kbuf = [&](int par) { return kbuf0 + par * 2 * HT; };
-  auto vbuf = [&](int par) { return kbuf0 + par * 2 * HT + HT; };
-
-  // raw block-table entry for this wave's block of tile t (vector load; 0 when t has no
-  // prefix block here, validity is decided again where the id is used)
-  auto fetch_id = [&](int t) -> uint32_t {
-    const int jb = t * 4 + ld_blk;
-    const bool ok = t < n_pre && jb * kBlock < P;
-    return buf_load4(bt_rsrc, ok ? (uint32_t)jb * 4u : kOobOffset);
-  };
-  // Source of this wave's 16-row block of tile t (prefix tiles first, then the chunk's
-  // own tiles), K or V part: a buffer resource sized to the valid rows (rows past the end
-  // read as zero; past the last tile every size is zero), the row pitch and the LDS
-  // destination.  Everything is a scalar select, so the loop carries no branches here.
-  struct LdDesc {
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t pitch;
-    uint16_t* dst;
-  };
   const uint32_t bs32 = (uint32_t)block_stride;
-  auto make_desc = [&](int t, int pb, uint16_t* dst, const uint16_t* pool_base,
-                       const uint16_t* self_base) -> LdDesc {
+
+  // tiles of the chunk itself crossing the causal diagonal, or the end of the keys, need
+  // per-row masking (uniform per work-group)
+  auto tile_needs_mask = [&](int t) {
+    const bool pre = t < n_pre;
+    const int base = pre ? t * kKT : (t - n_pre) * kKT;
+    const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
+    return (count < kKT) || (!pre && base + kKT - 1 > i_first);
+  };
+
+  // Descriptor table of this wave's tile sequence: lane i describes the wave's block of
+  // tile KS*(u0+i)+kh (u = step index): K and V source addresses and valid bytes (rows
+  // past the end read as zero; past the last tile the size is zero), plus wave-wide bit
+  // masks of "prefix tile" and "needs masking".  Filled 64 tiles at a time with one
+  // gathered block-table read; a step then only reads lanes out of it.
+  uint32_t tk_lo, tk_hi, tv_lo, tv_hi, t_nb;
+  uint64_t pre_bits, mask_bits;
+  int u0 = 0;
+  auto refill = [&](int u_first) {
+    const int t = KS * (u_first + lane) + kh;
     const bool pre = t < n_pre;
     const int jb = t * 4 + ld_blk;
-    const bool pvalid = pre && jb * kBlock < P && (uint32_t)pb < (uint32_t)num_blocks;
+    const bool inpre = pre && jb * kBlock < P;
+    const int pb = inpre ? bt_row[jb] : -1;
+    const bool pvalid = inpre && (uint32_t)pb < (uint32_t)num_blocks;
     const int rows_pre = max(0, min(kBlock, P - jb * kBlock));
     const int row0 = (t - n_pre) * kKT + kBlock * ld_blk;
     const int rows_self = (!pre && t < total) ? max(0, min(kBlock, self_n - row0)) : 0;
-    const uint32_t mul_a = pre ? (pvalid ? (uint32_t)pb : 0u) : (uint32_t)min(max(row0, 0), C);
-    const uint32_t mul_b = pre ? bs32 : (uint32_t)(hkv * D);
-    const uint16_t* src = (pre ? pool_base : self_base) + (uint64_t)mul_a * mul_b;
-    const uint32_t nb = pre ? (pvalid ? (uint32_t)(rows_pre * D * 2) : 0u)
-                            : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
+    const uint64_t off = pre ? (uint64_t)(pvalid ? (uint32_t)pb : 0u) * bs32
+                             : (uint64_t)(uint32_t)min(max(row0, 0), C) * (uint32_t)(hkv * D);
+    const uint64_t ak = (uint64_t)(pre ? kbase : knb) + 2 * off;
+    const uint64_t av = (uint64_t)(pre ? vbase : vnb) + 2 * off;
+    tk_lo = (uint32_t)ak;
+    tk_hi = (uint32_t)(ak >> 32);
+    tv_lo = (uint32_t)av;
+    tv_hi = (uint32_t)(av >> 32);
+    t_nb = pre ? (pvalid ? (uint32_t)(rows_pre * D * 2) : 0u)
+               : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
+    pre_bits = __ballot(pre);
+    mask_bits = __ballot(tile_needs_mask(t));
+  };
+  struct LdDesc {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t pitch;
+    uint32_t dst;                                   // LDS byte address of the block
+  };
+  auto desc = [&](int li, bool is_v, uint32_t buf_off) -> LdDesc {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(is_v ? tv_lo : tk_lo), li);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(is_v ? tv_hi : tk_hi), li);
+    const int nb = __builtin_amdgcn_readlane((int)t_nb, li);
     LdDesc d;
-    d.rs = make_rsrc(src, nb);
-    d.pitch = (uint32_t)uniform(pre ? D * 2 : (int)self_row_bytes);
-    d.dst = dst + kBlock * ld_blk * CPR * 8;
+    d.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, nb, kBufDword3);
+    d.pitch = ((pre_bits >> li) & 1) ? (uint32_t)(D * 2) : self_row_bytes;
+    d.dst = ld_dst + buf_off;
     return d;
   };
   // load instruction m (1 KiB) of a part
   auto issue = [&](const LdDesc& d, const uint32_t* col, int m) {
-    buf_load16_lds(d.rs, ld_row[m] * d.pitch + col[m], d.dst + 64 * m * 8);
+    buf_load16_lds(d.rs, ld_row[m] * d.pitch + col[m], lds + d.dst + 64 * 16 * m);
   };
   auto issue_all = [&](const LdDesc& d, const uint32_t* col) {
 #pragma unroll
     for (int m = 0; m < NLD; ++m) issue(d, col, m);
   };
 
-  // ---- per-lane LDS read addresses (elements, relative to a K or V tile)
+  // ---- per-lane LDS read addresses (bytes, including this key part's base)
   // K operand: row 32*half + lr, logical chunk 2*kk + hf
-  int kaddr[NKK];
+  uint32_t kaddr[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = (lr * CPR + L::posK(lr, 2 * kk + hf)) * 8;
+  for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = part_base + (uint32_t)(lr * CPR + L::posK(lr, 2 * kk + hf)) * 16;
   // V transpose-read source: rows 16*kp4 + 4*hf + (l%16)/4 (+8 for the high half),
   // columns 32*db + 16*((l/16)%2) + 4*(l%4), i.e. chunk 4*db + 2*((l/16)%2) + (l%4)/2
-  int vaddr[NDB][2];
+  uint32_t vaddr[NDB][2];
   {
     const int s4 = (lane & 15) >> 2;
 #pragma unroll
@@ -242,29 +268,19 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       for (int hi = 0; hi < 2; ++hi) {
         const int row = 4 * hf + s4 + 8 * hi;
         const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-        vaddr[db][hi] = (row * CPR + L::posV(row, c)) * 8 + 4 * (lane & 1);
+        vaddr[db][hi] = part_base + (uint32_t)((row * CPR + L::posV(row, c)) * 16 + 8 * (lane & 1));
       }
   }
+  auto k_operand = [&](uint32_t off, int kk, int half) {
+    return *reinterpret_cast<const s16x8*>(lds + (kaddr[kk] + off + (uint32_t)(half * 32 * D * 2)));
+  };
+  auto v_operand = [&](uint32_t off, int db, int kp4) {
+    const s16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(lds + (vaddr[db][0] + off + (uint32_t)(kp4 * 16 * D * 2))));
+    const s16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(lds + (vaddr[db][1] + off + (uint32_t)(kp4 * 16 * D * 2))));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
-  // S^T = K Q^T for one tile: s[half] holds keys 32*half + (MFMA row), this lane's row
-  auto qk = [&](const uint16_t* kb, f32x16* s) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const s16x8 a0 = *reinterpret_cast<const s16x8*>(kb + kaddr[kk]);
-      const s16x8 a1 = *reinterpret_cast<const s16x8*>(kb + kaddr[kk] + 32 * D);
-      s[0] = T::mfma32(a0, qreg[kk], s[0]);
-      s[1] = T::mfma32(a1, qreg[kk], s[1]);
-    }
-  };
-  // keys of tile t this lane's row may not see -> -inf (only tiles that need it)
-  auto tile_needs_mask = [&](int t) {
-    const bool pre = t < n_pre;
-    const int base = pre ? t * kKT : (t - n_pre) * kKT;
-    const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
-    return (count < kKT) || (!pre && base + kKT - 1 > i_first);
-  };
+  // keys of tile t this lane's row may not see -> -inf
   auto mask = [&](int t, f32x16* s) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
@@ -276,23 +292,6 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       s[0][rr] = kl < lim ? s[0][rr] : -INFINITY;
       s[1][rr] = kl + 32 < lim ? s[1][rr] : -INFINITY;
     }
-  };
-  // Row max of a fresh score tile; the running max only moves (and the output is only
-  // rescaled) when a score exceeds it by more than 2^8.  Leaves the scores as
-  // s*c - m (exp2 arguments) and returns whether the output needs rescaling.
-  auto row_max = [&](f32x16* s, float& m_new) -> bool {
-    float m = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-    for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s[0][rr], s[1][rr]));
-    const float mx = halves_max(m) * c_log2;
-    const bool any = __any(mx > m_run + kPfRescale);
-    m_new = any ? fmaxf(m_run, mx) : m_run;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      s[0][rr] = fmaf(s[0][rr], c_log2, -m_new);
-      s[1][rr] = fmaf(s[1][rr], c_log2, -m_new);
-    }
-    return any;
   };
   auto rescale = [&](float m_new) {
     const float alpha = fast_exp2(m_run - m_new);
@@ -320,171 +319,176 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     }
     l_run += ls0 + ls1;
   };
-  // O^T += V^T P^T
-  auto pv = [&](const uint16_t* vb, const s16x8* pk) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int kp4 = 0; kp4 < 4; ++kp4) {
-        const s16x4 lo = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
-        const s16x4 hi = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
-        o[db] = T::mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pk[kp4], o[db]);
-      }
-  };
 
   // ---- prologue: K and V of step 0, K of step 1; scores of step 0
-  int pb_next_v;                                    // block id of the next V tile
-  uint32_t id_raw;                                  // raw id of the next K tile (in flight)
-  {
-    const int t0 = kh, t1 = KS + kh;
-    const int jb0 = t0 * 4 + ld_blk, jb1 = t1 * 4 + ld_blk;
-    const int pb0 = (t0 < n_pre && jb0 * kBlock < P) ? bt_row[jb0] : -1;
-    const int pb1 = (t1 < n_pre && jb1 * kBlock < P) ? bt_row[jb1] : -1;
-    issue_all(make_desc(t0, pb0, kbuf(0), kbase, knb), ld_colK);
-    issue_all(make_desc(t0, pb0, vbuf(0), vbase, vnb), ld_colV);
-    issue_all(make_desc(t1, pb1, kbuf(1), kbase, knb), ld_colK);
-    pb_next_v = pb1;
-    id_raw = fetch_id(2 * KS + kh);
-  }
+  refill(0);
+  issue_all(desc(0, false, kOffK0), ld_colK);
+  issue_all(desc(0, true, kOffV0), ld_colV);
+  issue_all(desc(1, false, kOffK1), ld_colK);
   f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (wave_active) {
-    qk(kbuf(0), s_cur);
-    if (tile_needs_mask(kh)) mask(kh, s_cur);
-    float m_new;
-    row_max(s_cur, m_new);
-    m_run = m_new;
+    s_cur[0] = f32x16{};
+    s_cur[1] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      s_cur[0] = T::mfma32(k_operand(kOffK0, kk, 0), qreg[kk], s_cur[0]);
+      s_cur[1] = T::mfma32(k_operand(kOffK0, kk, 1), qreg[kk], s_cur[1]);
+    }
+    if (mask_bits & 1) mask(kh, s_cur);
+    float m = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s_cur[0][rr], s_cur[1][rr]));
+    // the first tile always sets the reference (m_run starts far below any score)
+    m_run = fmaxf(m_run, halves_max(m) * c_log2);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      s_cur[0][rr] = fmaf(s_cur[0][rr], c_log2, -m_run);
+      s_cur[1][rr] = fmaf(s_cur[1][rr], c_log2, -m_run);
+    }
   }
   __syncthreads();                                  // K buffer 0 is reloaded in step 0
 
-  for (int j = 0; j + 1 < nstage; ++j) {
-    const int t_next = KS * (j + 1) + kh;           // scores computed in this step
-    // loads of this step: K of tile j+2 and V of tile j+1 (2*NLD == NKK instructions)
-    const int pb_k = uniform((int)id_raw);
-    const LdDesc dk = make_desc(KS * (j + 2) + kh, pb_k, kbuf(j & 1), kbase, knb);
-    const LdDesc dv = make_desc(t_next, pb_next_v, vbuf((j + 1) & 1), vbase, vnb);
-    pb_next_v = pb_k;
-    id_raw = fetch_id(KS * (j + 3) + kh);
+  // ---- step j: loads K of tile j+2 into K buffer (j&1) and V of tile j+1 into V buffer
+  // ((j+1)&1); S MFMAs of tile j+1 from K buffer ((j+1)&1); PV MFMAs of tile j from V
+  // buffer (j&1).  The buffer parity is a compile-time constant (the loop is unrolled by
+  // two), so every LDS address is a register plus an immediate.
+  auto step = [&](int j, auto par_c) {
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr uint32_t offK_ld = PAR ? kOffK1 : kOffK0, offV_ld = PAR ? kOffV0 : kOffV1;
+    constexpr uint32_t offK_rd = PAR ? kOffK0 : kOffK1, offV_rd = PAR ? kOffV1 : kOffV0;
+    if (j + 2 - u0 >= 64) {                         // next 64 tiles of the sequence
+      keep_branch();
+      u0 = j + 1;
+      refill(u0);
+    }
+    const int lk = j + 2 - u0, lv = j + 1 - u0;
+    const LdDesc dk = desc(lk, false, offK_ld);
+    const LdDesc dv = desc(lv, true, offV_ld);
+    const bool need_mask = (mask_bits >> lv) & 1;
     if (!wave_active) {
       issue_all(dk, ld_colK);
       issue_all(dv, ld_colV);
-    } else {
-      // Hand-interleaved: each step of a phase is a scheduling region of its own, so
-      // operand reads issued there stay two MFMA steps ahead of their use and the VALU
-      // work of the other tile fills the MFMA shadow.
-      // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack).
-      const uint16_t* kb = kbuf((j + 1) & 1);
-      f32x16 s_nxt[2] = {f32x16{}, f32x16{}};
-      s16x8 ka[NKK][2];
-      uint32_t pw[16];
-#pragma unroll
-      for (int kk = 0; kk < 2 && kk < NKK; ++kk) {
-        ka[kk][0] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk]);
-        ka[kk][1] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk] + 32 * D);
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        // one load per step: bunched at the step start, the loads of all waves queue at
-        // the memory pipeline and stall the issuing waves
-        static_assert(2 * NLD == NKK, "one load per S step");
-        if (kk < NLD) issue(dk, ld_colK, kk);
-        else issue(dv, ld_colV, kk - NLD);
-        if (kk + 2 < NKK) {
-          ka[kk + 2][0] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk + 2]);
-          ka[kk + 2][1] = *reinterpret_cast<const s16x8*>(kb + kaddr[kk + 2] + 32 * D);
-        }
-        s_nxt[0] = T::mfma32(ka[kk][0], qreg[kk], s_nxt[0]);
-        s_nxt[1] = T::mfma32(ka[kk][1], qreg[kk], s_nxt[1]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)            // pair e = (kp4 = e/4, element e%4)
-          if (e * NKK / 16 == kk) {
-            const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
-            pw[e] = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
-          }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      s16x8 pk[4];
-#pragma unroll
-      for (int kp4 = 0; kp4 < 4; ++kp4)
-        pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[4 * kp4], pw[4 * kp4 + 1], pw[4 * kp4 + 2], pw[4 * kp4 + 3]));
-      // keep the probabilities in phase 1: otherwise they sink past the mask branch
-      asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]));
-      if (tile_needs_mask(t_next)) {
-        keep_branch();
-        mask(t_next, s_nxt);
-      }
-      // Phase 2: PV MFMAs of tile j; row sums of tile j, row max and exp2 arguments of
-      // tile j+1.  VALU work units: 0-3 partial maxima, 4 the wave-wide max and the new
-      // reference, 5-12 scaled scores (4 each), 13-16 row sums (4 dot products each).
-      const uint16_t* vb = vbuf(j & 1);
-      constexpr int NU = 17;
-      s16x4 va[NPV][2];
-      float pmax[4], m_new = m_run, ls[4];
-      bool any = false;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int db = i >> 2, kp4 = i & 3;
-        va[i][0] = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
-        va[i][1] = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
-      }
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + 2 < NPV) {
-          const int db = (i + 2) >> 2, kp4 = (i + 2) & 3;
-          va[i + 2][0] = lds_read_tr16(vb + vaddr[db][0] + 16 * kp4 * D);
-          va[i + 2][1] = lds_read_tr16(vb + vaddr[db][1] + 16 * kp4 * D);
-        }
-        {
-          const int db = i >> 2, kp4 = i & 3;
-          o[db] = T::mfma32(__builtin_shufflevector(va[i][0], va[i][1], 0, 1, 2, 3, 4, 5, 6, 7), pk[kp4], o[db]);
-        }
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          if (u * NPV / NU != i) continue;
-          if (u < 4) {
-            const int h = u >> 1, r0 = (u & 1) * 8;
-            float m = fmaxf(s_nxt[h][r0], s_nxt[h][r0 + 1]);
-#pragma unroll
-            for (int rr = 2; rr < 8; ++rr) m = fmaxf(m, s_nxt[h][r0 + rr]);
-            pmax[u] = m;
-          } else if (u == 4) {
-            const float mx = halves_max(fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]))) * c_log2;
-            any = __any(mx > m_run + kPfRescale);
-            m_new = any ? fmaxf(m_run, mx) : m_run;
-          } else if (u < 13) {
-            const int h = (u - 5) >> 2, r0 = ((u - 5) & 3) * 4;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_new);
-          } else {
-            const int k0 = (u - 13) * 4;
-            float a = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 + e], T::kOnePair, a);
-            ls[u - 13] = a;
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));   // scaled scores stay in phase 2
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-      if (any) {
-        keep_branch();
-        rescale(m_new);
-      }
-      m_run = m_new;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
+      return;
     }
+    // Hand-interleaved: each step of a phase is a scheduling region of its own, so
+    // operand reads issued there stay two MFMA steps ahead of their use and the VALU
+    // work of the other tile fills the MFMA shadow.
+    // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack), loads.
+    f32x16 s_nxt[2] = {f32x16{}, f32x16{}};
+    s16x8 ka[NKK][2];
+    uint32_t pw[16];
+#pragma unroll
+    for (int kk = 0; kk < 2 && kk < NKK; ++kk) {
+      ka[kk][0] = k_operand(offK_rd, kk, 0);
+      ka[kk][1] = k_operand(offK_rd, kk, 1);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      // one load per step: bunched at the step start, the loads of all waves queue at
+      // the memory pipeline and stall the issuing waves
+      if (kk < NLD) issue(dk, ld_colK, kk);
+      else issue(dv, ld_colV, kk - NLD);
+      if (kk + 2 < NKK) {
+        ka[kk + 2][0] = k_operand(offK_rd, kk + 2, 0);
+        ka[kk + 2][1] = k_operand(offK_rd, kk + 2, 1);
+      }
+      s_nxt[0] = T::mfma32(ka[kk][0], qreg[kk], s_nxt[0]);
+      s_nxt[1] = T::mfma32(ka[kk][1], qreg[kk], s_nxt[1]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)                // pair e = (kp4 = e/4, element e%4)
+        if (e * NKK / 16 == kk) {
+          const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+          pw[e] = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s16x8 pk[4];
+#pragma unroll
+    for (int kp4 = 0; kp4 < 4; ++kp4)
+      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[4 * kp4], pw[4 * kp4 + 1], pw[4 * kp4 + 2], pw[4 * kp4 + 3]));
+    // keep the probabilities in phase 1: otherwise they sink past the mask branch
+    asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]));
+    if (need_mask) {
+      keep_branch();
+      mask(KS * (j + 1) + kh, s_nxt);
+    }
+    // Phase 2: PV MFMAs of tile j; row sums of tile j, row max and exp2 arguments of
+    // tile j+1.  VALU work units: 0-3 partial maxima, 4 the wave-wide max and the new
+    // reference, 5-12 scaled scores (4 each), 13-16 row sums (4 dot products each).
+    constexpr int NU = 17;
+    s16x8 va[NPV];
+    float pmax[4], m_new = m_run, ls[4];
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) va[i] = v_operand(offV_rd, i >> 2, i & 3);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 2 < NPV) va[i + 2] = v_operand(offV_rd, (i + 2) >> 2, (i + 2) & 3);
+      o[i >> 2] = T::mfma32(va[i], pk[i & 3], o[i >> 2]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (u * NPV / NU != i) continue;
+        if (u < 4) {
+          const int h = u >> 1, r0 = (u & 1) * 8;
+          float m = fmaxf(s_nxt[h][r0], s_nxt[h][r0 + 1]);
+#pragma unroll
+          for (int rr = 2; rr < 8; ++rr) m = fmaxf(m, s_nxt[h][r0 + rr]);
+          pmax[u] = m;
+        } else if (u == 4) {
+          const float mx = halves_max(fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]))) * c_log2;
+          any = __any(mx > m_run + kPfRescale);
+          m_new = any ? fmaxf(m_run, mx) : m_run;
+        } else if (u < 13) {
+          const int h = (u - 5) >> 2, r0 = ((u - 5) & 3) * 4;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_new);
+        } else {
+          const int k0 = (u - 13) * 4;
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 + e], T::kOnePair, a);
+          ls[u - 13] = a;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));   // scaled scores stay in phase 2
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if (any) {
+      keep_branch();
+      rescale(m_new);
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
+  };
+  auto sync = [&]() {
     __builtin_amdgcn_s_waitcnt(0);                  // this wave's LDS-direct loads have landed
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 < nstage; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    sync();
+    step(j + 1, std::integral_constant<int, 1>{});
+    sync();
   }
+  if (j + 1 < nstage) {
+    step(j, std::integral_constant<int, 0>{});
+    sync();
+    ++j;
+  }
+  // last tile: probabilities and PV (V buffer parity of the last step)
   if (wave_active) {
     s16x8 pk[4];
     probs(s_cur, pk);
-    pv(vbuf((nstage - 1) & 1), pk);
+    const uint32_t off = (j & 1) ? kOffV1 : kOffV0;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) o[i >> 2] = T::mfma32(v_operand(off, i >> 2, i & 3), pk[i & 3], o[i >> 2]);
   }
 
   // Merge the two key parts of each row group through LDS (the tile buffers are free):

@@ -82,6 +82,7 @@ PREFILL_CASES = [
     (205, "bf16", 32, 8, 64, [5, 400, 0, 48], [300, 15, 129, 2], "pairs"),
     (206, "bf16", 4, 4, 128, [0, 0], [200, 3], "none"),        # MHA, no prefix
     (207, "fp16", 8, 1, 64, [1, 15, 16, 17], [7, 9, 16, 31], "none"),  # MQA, block edges
+    (214, "bf16", 8, 2, 128, [9000, 8300], [70, 33], "pairs"),  # > 128 tiles: key-split waves refill
 ]
 
 
@@ -107,6 +108,8 @@ LARGE_GRID_CASES = [
     (211, "bf16", 32, 8, 128, [100, 700, 0, 2000], [520, 600, 700, 300], "pairs"),
     (212, "fp16", 32, 8, 96, [1500, 33, 0, 640], [700, 640, 511, 257], "none"),
     (213, "bf16", 32, 8, 64, [64, 64, 900, 17], [700, 690, 650, 700], "all"),
+    # more than 64 key tiles per wave: the per-wave tile descriptors are refilled
+    (215, "fp16", 32, 8, 128, [4500, 4100, 4700, 4350], [512, 500, 480, 511], "pairs"),
 ]
 
 
