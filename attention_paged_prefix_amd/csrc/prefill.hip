@@ -483,13 +483,26 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     ++j;
   }
   // last tile: probabilities and PV (V buffer parity of the last step)
-  if (wave_active) {
+  auto last = [&](auto par_c) {
+    constexpr uint32_t off = decltype(par_c)::value ? kOffV1 : kOffV0;
     s16x8 pk[4];
     probs(s_cur, pk);
-    const uint32_t off = (j & 1) ? kOffV1 : kOffV0;
 #pragma unroll
     for (int i = 0; i < NPV; ++i) o[i >> 2] = T::mfma32(v_operand(off, i >> 2, i & 3), pk[i & 3], o[i >> 2]);
+  };
+  if (wave_active) {
+    if (j & 1) last(std::integral_constant<int, 1>{});
+    else last(std::integral_constant<int, 0>{});
   }
+
+  // Output row of this lane, recomputed from an opaque copy of the thread id so that the
+  // pre-loop values need not stay live (in registers) across the main loop.
+  int tid_e = threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int vrow_e = v0 + 32 * rw + (tid_e & 31);
+  const bool rvalid_e = vrow_e < nrows;
+  const int i_e = vrow_e / G;
+  uint16_t* const orow = out + ((int64_t)(cu_b + i_e) * hq + kvh * G + (vrow_e - i_e * G)) * D;
 
   // Merge the two key parts of each row group through LDS (the tile buffers are free):
   // key-part 1 waves publish (output, max, sum); key-part 0 waves combine and store.
@@ -499,9 +512,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   float* my = mbuf + rw * (OPW + 2) * 64;
   if (KS == 1) {
     float lt = halves_sum(l_run);
-    if (!rvalid) return;
+    if (!rvalid_e) return;
     const float inv = 1.0f / lt;
-    uint16_t* orow = out + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -530,9 +542,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const float M = fmaxf(m_run, m1);
   const float a0 = fast_exp2(m_run - M), a1 = fast_exp2(m1 - M);
   const float lt = halves_sum(l_run * a0 + l1 * a1);
-  if (!rvalid) return;
+  if (!rvalid_e) return;
   const float inv0 = a0 / lt, inv1 = a1 / lt;
-  uint16_t* orow = out + ((int64_t)(cu_b + i_row) * hq + kvh * G + g_row) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
