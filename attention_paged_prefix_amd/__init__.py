@@ -23,8 +23,9 @@ from . import _lib
 from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool  # noqa: F401
 
 __all__ = [
-    "Pool", "write_kv", "paged_prefill", "paged_decode", "gather_kv",
-    "paged_prefill_workspace_size", "paged_decode_workspace_size", "version", "KvbError",
+    "Pool", "write_kv", "paged_prefill", "paged_decode", "paged_decode_cascade", "gather_kv",
+    "paged_prefill_workspace_size", "paged_decode_workspace_size",
+    "paged_decode_cascade_workspace_size", "version", "KvbError",
 ]
 
 BLOCK_SIZE = 16
@@ -106,6 +107,13 @@ def paged_decode_workspace_size(batch: int, num_kv_heads: int, num_q_heads: int,
                                                            max_context_len, split_blocks))
 
 
+def paged_decode_cascade_workspace_size(batch: int, num_kv_heads: int, num_q_heads: int,
+                                        head_dim: int, max_context_len: int, shared_len: int,
+                                        split_blocks: int = 0) -> int:
+    return int(_lib.load().kvb_paged_decode_cascade_workspace_size(
+        batch, num_kv_heads, num_q_heads, head_dim, max_context_len, shared_len, split_blocks))
+
+
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return workspace
@@ -168,3 +176,26 @@ def gather_kv(pool: Pool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
         ctypes.byref(ps), _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
         _ptr(cu_seq_lens), _ptr(k_out), _ptr(v_out), int(seq_lens.numel()), int(max_len),
         _stream(stream)))
+
+
+def paged_decode_cascade(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
+                         block_tables: torch.Tensor, shared_blocks: Optional[torch.Tensor],
+                         shared_len: int, scale: float, max_context_len: int,
+                         split_blocks: int = 0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvb_paged_decode_cascade.  As ``paged_decode``; the first ``shared_len`` tokens of
+    every sequence are the blocks ``shared_blocks`` (int32), read once for all queries."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    B, hq, d = q.shape
+    need = paged_decode_cascade_workspace_size(B, pool.num_kv_heads, hq, d, max_context_len,
+                                               shared_len, split_blocks)
+    workspace = _workspace(need, q.device, workspace)
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_decode_cascade", lib.kvb_paged_decode_cascade(
+        ctypes.byref(ps), _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(shared_blocks), int(shared_len), B, hq,
+        int(max_context_len), int(split_blocks), float(scale), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

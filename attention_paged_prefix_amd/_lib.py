@@ -24,8 +24,10 @@ EXPORTS = (
     "kvb_write_kv",
     "kvb_paged_prefill",
     "kvb_paged_decode",
+    "kvb_paged_decode_cascade",
     "kvb_paged_prefill_workspace_size",
     "kvb_paged_decode_workspace_size",
+    "kvb_paged_decode_cascade_workspace_size",
     "kvb_gather_kv",
     "kvb_status_str",
     "kvb_version",
@@ -78,10 +80,15 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_decode.argtypes = [_PP, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _vp, _sz, _vp]
     lib.kvb_paged_decode.restype = ctypes.c_int
+    lib.kvb_paged_decode_cascade.argtypes = [_PP, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                             _i32, _i32, _f32, _vp, _sz, _vp]
+    lib.kvb_paged_decode_cascade.restype = ctypes.c_int
     lib.kvb_paged_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
     lib.kvb_paged_prefill_workspace_size.restype = _sz
     lib.kvb_paged_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
     lib.kvb_paged_decode_workspace_size.restype = _sz
+    lib.kvb_paged_decode_cascade_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.kvb_paged_decode_cascade_workspace_size.restype = _sz
     lib.kvb_gather_kv.argtypes = [_PP, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     lib.kvb_gather_kv.restype = ctypes.c_int
     lib.kvb_status_str.argtypes = [ctypes.c_int]

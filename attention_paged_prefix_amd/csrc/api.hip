@@ -134,6 +134,59 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
                                           sb, ns, scale, workspace, (hipStream_t)stream));
 }
 
+// private-pass split plan and shared-pass key split plan of a cascade decode
+static void cascade_plans(int batch, int hkv, int hq, int max_ctx, int shared_len, int split_blocks,
+                          int* sb, int* ns, int* nks, int* ks_tiles) {
+  kvb::decode_plan(batch, hkv, hq, max_ctx > shared_len ? max_ctx - shared_len : 0, split_blocks, sb, ns);
+  kvb::cascade_plan(batch, hkv, hq, shared_len < max_ctx ? shared_len : max_ctx, nks, ks_tiles);
+}
+
+size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_heads,
+                                               int32_t num_q_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t shared_len,
+                                               int32_t split_blocks) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
+      max_context_len <= 0 || split_blocks < 0 || shared_len < 0 || shared_len % 16)
+    return 0;
+  int sb = 0, ns = 0, nks = 0, kt = 0;
+  cascade_plans(batch, num_kv_heads, num_q_heads, max_context_len, shared_len, split_blocks, &sb,
+                &ns, &nks, &kt);
+  return (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, head_dim, nks + ns);
+}
+
+kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t block_table_stride, const int32_t* shared_blocks,
+                                    int32_t shared_len, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, int32_t split_blocks, float scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || split_blocks < 0)
+    return KVB_ERR_INVALID;
+  if (shared_len < 0 || shared_len % 16 != 0) return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0) return KVB_OK;
+  if (!q || !out || !context_lens || !block_tables) return KVB_ERR_NULL;
+  if (shared_len > 0 && !shared_blocks) return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)shared_blocks & 3u))
+    return KVB_ERR_INVALID;
+  if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
+    return KVB_ERR_INVALID;
+  int sb = 0, ns = 0, nks = 0, kt = 0;
+  cascade_plans(batch, pool->num_kv_heads, num_q_heads, max_context_len, shared_len, split_blocks,
+                &sb, &ns, &nks, &kt);
+  const size_t need = (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, pool->head_dim, nks + ns);
+  if (!workspace || workspace_bytes < need) return KVB_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_decode_cascade(*pool, q, out, context_lens, block_tables,
+                                                  block_table_stride, shared_blocks, shared_len,
+                                                  batch, num_q_heads, max_context_len, sb, ns,
+                                                  nks, kt, scale, workspace, (hipStream_t)stream));
+}
+
 kvb_status kvb_gather_kv(const kvb_pool* pool, const int32_t* block_tables,
                          int32_t block_table_stride, const int32_t* seq_lens,
                          const int32_t* cu_seq_lens, void* k_out, void* v_out, int32_t batch,

@@ -50,7 +50,8 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
                     uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens,
                     const int32_t* __restrict__ bt, int bt_stride, int hq, int hkv, int nchunks,
                     int split_blocks, int nsplit, int max_ctx, float c_log2,
-                    float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real) {
+                    float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real,
+                    int blk_first, int slot0, int ws_slots, int force_partial) {
   constexpr int NKK = D / 32;
   constexpr int NDB = D / 16;               // 16-row d blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -84,16 +85,17 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   n = min(n, min(max_ctx, bt_stride * kBlock));
   const int tid = threadIdx.x;
   if (n <= 0) {
-    if (split == 0)
+    if (split == 0 && !force_partial)
       for (int e = tid; e < nh * D; e += kDecThreads)
         out[((int64_t)b * hq + h0 + e / D) * D + (e % D)] = 0;
     return;
   }
+  // keys of this pass: blocks [blk_first, nblk) (blk_first > 0 after a shared prefix)
   const int nblk = (n + kBlock - 1) / kBlock;
-  const int blk_begin = split * split_blocks;
+  const int blk_begin = blk_first + split * split_blocks;
   if (blk_begin >= nblk) return;
   const int blk_end = min(nblk, blk_begin + split_blocks);
-  const bool single = nblk <= split_blocks;
+  const bool single = !force_partial && nblk <= split_blocks;
 
   for (int i = tid; i < blk_end - blk_begin; i += kDecThreads) {
     const int pb = bt[(int64_t)b * bt_stride + blk_begin + i];
@@ -268,39 +270,47 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     if (single) {
       out[row * D + d] = T::from_f32(ov / L);
     } else {
-      ws_o[(row * nsplit + split) * D + d] = ov;
+      const int64_t slot = row * ws_slots + slot0 + split;
+      ws_o[slot * D + d] = ov;
       if (d == 0) {
-        ws_ml[(row * nsplit + split) * 2 + 0] = M;
-        ws_ml[(row * nsplit + split) * 2 + 1] = L;
+        ws_ml[slot * 2 + 0] = M;
+        ws_ml[slot * 2 + 1] = L;
       }
     }
   }
 }
 
-// One work-group of 128 threads per (sequence, query head); only sequences whose
-// context spans more than one split have partials to combine.
+// One work-group of 128 threads per (sequence, query head).  Slots: `n_shared` partials
+// of a shared prefix (cascade form; 0 otherwise), then one per split of blocks
+// [blk_first, nblk).  Without a shared prefix only sequences spanning more than one
+// split have partials to combine (a single split wrote its row directly).
 template <typename T, int D>
 __global__ void __launch_bounds__(128)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                     uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens, int hq,
-                    int split_blocks, int nsplit, int max_ctx, int bt_stride) {
+                    int split_blocks, int ws_slots, int max_ctx, int bt_stride, int blk_first,
+                    int n_shared, int cascade) {
   const int row = blockIdx.x;          // b * hq + h
   const int b = row / hq;
   int n = ctx_lens[b];
   n = min(n, min(max_ctx, bt_stride * kBlock));
-  if (n <= 0) return;
-  const int nblk = (n + kBlock - 1) / kBlock;
-  const int ns = (nblk + split_blocks - 1) / split_blocks;
-  if (ns <= 1) return;
   const int d = threadIdx.x;
   if (d >= D) return;
-  const float* ml = ws_ml + (int64_t)row * nsplit * 2;
+  if (n <= 0) {
+    if (cascade) out[(int64_t)row * D + d] = 0;
+    return;
+  }
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const int ns_priv = nblk > blk_first ? (nblk - blk_first + split_blocks - 1) / split_blocks : 0;
+  if (!cascade && ns_priv <= 1) return;
+  const int ns = n_shared + ns_priv;
+  const float* ml = ws_ml + (int64_t)row * ws_slots * 2;
   float M = kNegBig;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
   float o = 0.f, L = 0.f;
   for (int s = 0; s < ns; ++s) {
     const float sc = fast_exp2(ml[2 * s] - M);
-    o = fmaf(sc, ws_o[((int64_t)row * nsplit + s) * D + d], o);
+    o = fmaf(sc, ws_o[((int64_t)row * ws_slots + s) * D + d], o);
     L = fmaf(sc, ml[2 * s + 1], L);
   }
   out[(int64_t)row * D + d] = T::from_f32(o / L);
@@ -344,12 +354,64 @@ static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, c
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
-                     nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real);
+                     nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, 0, 0, ns, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns <= 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(batch * hq)), dim3(128), 0, s,
-                     ws_o, ws_ml, (uint16_t*)out, ctx, hq, sb, ns, max_ctx, bt_stride);
+                     ws_o, ws_ml, (uint16_t*)out, ctx, hq, sb, ns, max_ctx, bt_stride, 0, 0, 0);
   return hipGetLastError();
+}
+
+// Cascade: private pass over blocks [shared_len/16, nblk) into slots nks.., then the
+// merge of the nks shared partials (written before by launch_cascade_shared) with them.
+template <typename T, int D>
+static hipError_t launch_decode_private_t(const kvb_pool& p, const void* q, void* out,
+                                          const int32_t* ctx, const int32_t* bt, int bt_stride,
+                                          int batch, int hq, int max_ctx, int sb, int ns,
+                                          int blk_first, int nks, float scale, float* ws_o,
+                                          float* ws_ml, hipStream_t s) {
+  const int G = hq / p.num_kv_heads;
+  const int nchunks = (G + kDecHeads - 1) / kDecHeads;
+  const int slots = nks + ns;
+  const long long real = (long long)batch * p.num_kv_heads * ns * nchunks;
+  if (real > 0) {
+    const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const float c = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+                       (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
+                       (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
+                       nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
+                       nks, slots, 1);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (batch * hq == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(batch * hq)), dim3(128), 0, s,
+                     ws_o, ws_ml, (uint16_t*)out, ctx, hq, sb, slots, max_ctx, bt_stride, blk_first,
+                     nks, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_cascade(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
+                                 const int32_t* bt, int bt_stride, const int32_t* shared_blocks,
+                                 int shared_len, int batch, int hq, int max_ctx, int sb, int ns,
+                                 int nks, int ks_tiles, float scale, void* ws, hipStream_t s) {
+  const int slots = nks + ns;
+  float* ws_o = (float*)ws;
+  float* ws_ml = ws_o + (int64_t)batch * hq * slots * p.head_dim;
+  hipError_t e = launch_cascade_shared(p, q, ctx, max_ctx, shared_blocks, shared_len, batch, hq,
+                                       scale, nks, ks_tiles, ws_o, ws_ml, slots, s);
+  if (e != hipSuccess) return e;
+  const int blk_first = shared_len / kBlock;
+  const bool bf = p.dtype == KVB_BF16;
+  switch (p.head_dim) {
+    case 64:  return bf ? launch_decode_private_t<BF16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s)
+                        : launch_decode_private_t<F16, 64>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s);
+    case 96:  return bf ? launch_decode_private_t<BF16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s)
+                        : launch_decode_private_t<F16, 96>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s);
+    default:  return bf ? launch_decode_private_t<BF16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s)
+                        : launch_decode_private_t<F16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s);
+  }
 }
 
 hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,

@@ -41,6 +41,23 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
                          const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
                          int ns, float scale, void* ws, hipStream_t s);
 
+// Cascade decode: the shared prefix pass (prefill kernel over all sequences' queries,
+// key tiles split over `nks` work-groups of `ks_tiles` tiles, partials to slots 0..nks-1)
+// and the private pass (decode split kernel from block `shared_len/16`, partials to
+// slots nks..), then the merge over every slot.
+void cascade_plan(int batch, int hkv, int hq, int shared_len, int* nks, int* ks_tiles);
+hipError_t launch_cascade_shared(const kvb_pool& p, const void* q, const int32_t* ctx, int max_ctx,
+                                 const int32_t* shared_blocks, int shared_len, int batch, int hq,
+                                 float scale, int nks, int ks_tiles, float* ws_o, float* ws_ml,
+                                 int ws_slots, hipStream_t s);
+hipError_t launch_decode_cascade(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
+                                 const int32_t* bt, int bt_stride, const int32_t* shared_blocks,
+                                 int shared_len, int batch, int hq, int max_ctx, int sb, int ns,
+                                 int nks, int ks_tiles, float scale, void* ws, hipStream_t s);
+inline int64_t cascade_ws_bytes(int batch, int hq, int d, int slots) {
+  return ((int64_t)batch * hq * slots * d + (int64_t)batch * hq * slots * 2) * 4;
+}
+
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,

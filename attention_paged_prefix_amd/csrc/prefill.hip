@@ -73,6 +73,22 @@ template <int D> struct PfLayout {
   }
 };
 
+// Shared-prefix (cascade) form.  The rows are the single queries of `total_q` sequences
+// (q as [sequence][query head][D], like decode) that all share one prefix, given as the
+// block list `bt` of length `shared_len`; row i sees the shared keys below ctx[i].  The
+// key tiles are split over `nks` work-groups of `ks_tiles` tiles, and each work-group
+// writes (unnormalised output, max, sum) partials, in the exp2 domain, to workspace slot
+// `ks` of its rows, for the decode merge.  With ctx null the kernel is ordinary prefill.
+struct PfCascade {
+  const int32_t* ctx;
+  int max_ctx;                               // contexts are clamped to this, as in decode
+  int shared_len;
+  int ks_tiles, nks;
+  float* ws_o;                               // [row][ws_slots][D], row = sequence*hq + head
+  float* ws_ml;                              // [row][ws_slots][2]
+  int ws_slots;
+};
+
 // Work-group = 4 * KS waves.  Wave w handles the 32 virtual rows 32*(w & 3) .. +31 of
 // the work-group's 128 and the key tiles t with t % KS == (w >> 2) ("key part").  With
 // KS = 2 (small grids: 8 waves, one work-group per CU) the two waves of a row group split
@@ -93,7 +109,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                uint16_t* __restrict__ out, const int32_t* __restrict__ cu,
                const int32_t* __restrict__ plen, const int32_t* __restrict__ bt, int bt_stride,
                int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
-               int real) {
+               int real, PfCascade cas) {
   using L = PfLayout<D>;
   constexpr int CPR = L::CPR;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
@@ -109,18 +125,20 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
-  // logical id -> (kvh, b, tile), tile fastest and KV head slowest
+  // logical id -> (kvh, b, key split, tile), tile fastest and KV head slowest
+  const bool cascade = cas.ctx != nullptr;
   int r = lid;
   const int tile = r % max_tiles; r /= max_tiles;
+  const int ks = r % cas.nks; r /= cas.nks;
   const int b = r % batch;
   const int kvh = r / batch;
   const int G = hq / hkv;
-  const int cu_b = min(max(cu[b], 0), total_q);
-  const int C = max(0, min(cu[b + 1], total_q) - cu_b);
+  const int cu_b = cascade ? 0 : min(max(cu[b], 0), total_q);
+  const int C = cascade ? total_q : max(0, min(cu[b + 1], total_q) - cu_b);
   const int nrows = C * G;
   const int v0 = tile * kBM;
   if (v0 >= nrows) return;
-  const int P = max(0, min(plen[b], bt_stride * kBlock));
+  const int P0 = max(0, min(cascade ? cas.shared_len : plen[b], bt_stride * kBlock));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
@@ -145,12 +163,37 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const bool wave_active = v0 + 32 * rw < nrows;
 
   const int last_row = min(nrows, v0 + kBM) - 1;
-  const int self_n = last_row / G + 1;       // chunk keys needed by this work-group
   const int i_first = v0 / G;
-  const int n_pre = (P + kKT - 1) / kKT;
+  // cascade: each row (sequence) sees only the shared keys below its context length.
+  // wg_lim is the smallest such limit over the work-group's rows; keys at or past the
+  // largest one are not even loaded (they read as zero), so every key row that reaches
+  // the PV product holds a real token of some sequence of this work-group.
+  int row_lim = 0x7fffffff, wg_lim = 0x7fffffff, P = P0;
+  if (cascade) {
+    const int cap = min(P0, cas.max_ctx);
+    row_lim = rvalid ? min(cap, max(0, cas.ctx[i_row])) : 0;
+    int mn = 0x7fffffff, mx = 0;
+    for (int i = i_first + lane; i <= last_row / G; i += 64) {
+      const int l = min(cap, max(0, cas.ctx[i]));
+      mn = min(mn, l);
+      mx = max(mx, l);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      mn = min(mn, __shfl_xor(mn, sh, 64));
+      mx = max(mx, __shfl_xor(mx, sh, 64));
+    }
+    wg_lim = uniform(mn);
+    P = uniform(mx);
+  }
+  // key tiles [t_begin, total): prefix tiles below n_pre, then the chunk's own tiles
+  // (none in the cascade form, where this work-group covers one split of the prefix)
+  const int t_begin = cascade ? ks * cas.ks_tiles : 0;
+  const int n_pre = cascade ? min((P + kKT - 1) / kKT, t_begin + cas.ks_tiles) : (P + kKT - 1) / kKT;
+  const int self_n = cascade ? 0 : last_row / G + 1;   // chunk keys needed by this work-group
   const int n_self = (self_n + kKT - 1) / kKT;
   const int total = n_pre + n_self;
-  const int nstage = (total + KS - 1) / KS;
+  const int nstage = max(1, (total - t_begin + KS - 1) / KS);
 
   f32x16 o[NDB];
 #pragma unroll
@@ -194,7 +237,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
-    return (count < kKT) || (!pre && base + kKT - 1 > i_first);
+    return (count < kKT) || (!pre && base + kKT - 1 > i_first) || (pre && base + kKT > wg_lim);
   };
 
   // Descriptor table of this wave's tile sequence: lane i describes the wave's block of
@@ -206,7 +249,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   uint64_t pre_bits, mask_bits;
   int u0 = 0;
   auto refill = [&](int u_first) {
-    const int t = KS * (u_first + lane) + kh;
+    const int t = t_begin + KS * (u_first + lane) + kh;
     const bool pre = t < n_pre;
     const int jb = t * 4 + ld_blk;
     const bool inpre = pre && jb * kBlock < P;
@@ -285,7 +328,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
-    const int lim = pre ? count : min(count, i_row - base + 1);
+    const int lim = pre ? min(count, row_lim - base) : min(count, i_row - base + 1);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
@@ -336,7 +379,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       s_cur[0] = T::mfma32(k_operand(kOffK0, kk, 0), qreg[kk], s_cur[0]);
       s_cur[1] = T::mfma32(k_operand(kOffK0, kk, 1), qreg[kk], s_cur[1]);
     }
-    if (mask_bits & 1) mask(kh, s_cur);
+    if (mask_bits & 1) mask(t_begin + kh, s_cur);
     float m = fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
     for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s_cur[0][rr], s_cur[1][rr]));
@@ -413,7 +456,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]));
     if (need_mask) {
       keep_branch();
-      mask(KS * (j + 1) + kh, s_nxt);
+      mask(t_begin + KS * (j + 1) + kh, s_nxt);
     }
     // Phase 2: PV MFMAs of tile j; row sums of tile j, row max and exp2 arguments of
     // tile j+1.  VALU work units: 0-3 partial maxima, 4 the wave-wide max and the new
@@ -502,7 +545,39 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int vrow_e = v0 + 32 * rw + (tid_e & 31);
   const bool rvalid_e = vrow_e < nrows;
   const int i_e = vrow_e / G;
-  uint16_t* const orow = out + ((int64_t)(cu_b + i_e) * hq + kvh * G + (vrow_e - i_e * G)) * D;
+  const int64_t row_e = (int64_t)(cu_b + i_e) * hq + kvh * G + (vrow_e - i_e * G);
+
+  // Final values of this lane's row: get(db, r) is the unnormalised output, M the
+  // reference max and L the row sum.  Ordinary prefill stores the normalised row in the
+  // input type; the cascade form stores the partial (unnormalised output, M, L).
+  auto emit = [&](auto get, float M, float L) {
+    if (!rvalid_e) return;
+    if (cascade) {
+      float* wo = cas.ws_o + (row_e * cas.ws_slots + ks) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<float4*>(wo + 32 * db + r4 * 8 + hf * 4) =
+              make_float4(get(db, 4 * r4), get(db, 4 * r4 + 1), get(db, 4 * r4 + 2), get(db, 4 * r4 + 3));
+      if (hf == 0) {
+        cas.ws_ml[(row_e * cas.ws_slots + ks) * 2 + 0] = M;
+        cas.ws_ml[(row_e * cas.ws_slots + ks) * 2 + 1] = L;
+      }
+      return;
+    }
+    const float inv = 1.0f / L;
+    uint16_t* const orow = out + row_e * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 uu;
+        uu.x = pack2<T>(get(db, 4 * r4 + 0) * inv, get(db, 4 * r4 + 1) * inv);
+        uu.y = pack2<T>(get(db, 4 * r4 + 2) * inv, get(db, 4 * r4 + 3) * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * db + r4 * 8 + hf * 4) = uu;
+      }
+  };
 
   // Merge the two key parts of each row group through LDS (the tile buffers are free):
   // key-part 1 waves publish (output, max, sum); key-part 0 waves combine and store.
@@ -511,19 +586,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   static_assert(KS == 1 || (kRowWaves * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
   float* my = mbuf + rw * (OPW + 2) * 64;
   if (KS == 1) {
-    float lt = halves_sum(l_run);
-    if (!rvalid_e) return;
-    const float inv = 1.0f / lt;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * db + r4 * 8 + hf * 4;
-        uint2 uu;
-        uu.x = pack2<T>(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
-        uu.y = pack2<T>(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = uu;
-      }
+    const float lt = halves_sum(l_run);
+    emit([&](int db, int rr) { return o[db][rr]; }, m_run, lt);
     return;
   }
   __syncthreads();                                  // every wave is done with the tiles
@@ -542,33 +606,19 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const float M = fmaxf(m_run, m1);
   const float a0 = fast_exp2(m_run - M), a1 = fast_exp2(m1 - M);
   const float lt = halves_sum(l_run * a0 + l1 * a1);
-  if (!rvalid_e) return;
-  const float inv0 = a0 / lt, inv1 = a1 / lt;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * db + r4 * 8 + hf * 4;
-      float vals[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vals[e] = o[db][4 * r4 + e] * inv0 + my[(db * 16 + 4 * r4 + e) * 64 + lane] * inv1;
-      uint2 uu;
-      uu.x = pack2<T>(vals[0], vals[1]);
-      uu.y = pack2<T>(vals[2], vals[3]);
-      *reinterpret_cast<uint2*>(orow + d) = uu;
-    }
+  emit([&](int db, int rr) { return o[db][rr] * a0 + my[(db * 16 + rr) * 64 + lane] * a1; }, M, lt);
 }
 
 template <typename T, int D>
 static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void* kn, const void* vn,
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
-                                   int total_q, int max_q_len, float scale, hipStream_t s) {
+                                   int total_q, int max_q_len, float scale, const PfCascade& cas,
+                                   hipStream_t s) {
   const int G = hq / p.num_kv_heads;
   const long long rows = (long long)max_q_len * G;
   const int max_tiles = (int)((rows + kBM - 1) / kBM);
-  const long long real = (long long)batch * p.num_kv_heads * max_tiles;
+  const long long real = (long long)batch * p.num_kv_heads * cas.nks * max_tiles;
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   // scale 0 (all scores equal) is kept positive so masked -inf scores stay -inf
@@ -581,14 +631,24 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real);
+                       (int)padded, (int)real, cas);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, 1>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real);
+                       (int)padded, (int)real, cas);
   return hipGetLastError();
+}
+
+template <typename F>
+static hipError_t dispatch_prefill(const kvb_pool& p, F&& f) {
+  const bool bf = p.dtype == KVB_BF16;
+  switch (p.head_dim) {
+    case 64:  return bf ? f(BF16{}, std::integral_constant<int, 64>{}) : f(F16{}, std::integral_constant<int, 64>{});
+    case 96:  return bf ? f(BF16{}, std::integral_constant<int, 96>{}) : f(F16{}, std::integral_constant<int, 96>{});
+    default:  return bf ? f(BF16{}, std::integral_constant<int, 128>{}) : f(F16{}, std::integral_constant<int, 128>{});
+  }
 }
 
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
@@ -596,15 +656,39 @@ hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, cons
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
                           float scale, hipStream_t s) {
   (void)max_prefix_len;
-  const bool bf = p.dtype == KVB_BF16;
-  switch (p.head_dim) {
-    case 64:  return bf ? launch_prefill_t<BF16, 64>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s)
-                        : launch_prefill_t<F16, 64>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s);
-    case 96:  return bf ? launch_prefill_t<BF16, 96>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s)
-                        : launch_prefill_t<F16, 96>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s);
-    default:  return bf ? launch_prefill_t<BF16, 128>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s)
-                        : launch_prefill_t<F16, 128>(p, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, s);
-  }
+  const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
+  return dispatch_prefill(p, [&](auto t, auto d) {
+    return launch_prefill_t<decltype(t), decltype(d)::value>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
+                                                             batch, hq, total_q, max_q_len, scale, none, s);
+  });
+}
+
+void cascade_plan(int batch, int hkv, int hq, int shared_len, int* nks, int* ks_tiles) {
+  const int n_tiles = (shared_len + kKT - 1) / kKT;
+  if (n_tiles <= 0) { *nks = 0; *ks_tiles = 0; return; }
+  const long long units = (long long)hkv * (((long long)batch * (hq / hkv) + kBM - 1) / kBM);
+  // about one work-group per CU, at least two tiles each (both key parts busy)
+  long long ns = (device_cu_count() + units - 1) / units;
+  if (ns > n_tiles) ns = n_tiles;
+  if (ns < 1) ns = 1;
+  int kt = (int)((n_tiles + ns - 1) / ns);
+  if (kt < 2) kt = 2;
+  *ks_tiles = kt;
+  *nks = (n_tiles + kt - 1) / kt;
+}
+
+hipError_t launch_cascade_shared(const kvb_pool& p, const void* q, const int32_t* ctx, int max_ctx,
+                                 const int32_t* shared_blocks, int shared_len, int batch, int hq,
+                                 float scale, int nks, int ks_tiles, float* ws_o, float* ws_ml,
+                                 int ws_slots, hipStream_t s) {
+  if (nks <= 0 || batch <= 0) return hipSuccess;
+  const PfCascade cas{ctx, max_ctx, shared_len, ks_tiles, nks, ws_o, ws_ml, ws_slots};
+  const int nsb = (shared_len + kBlock - 1) / kBlock;
+  return dispatch_prefill(p, [&](auto t, auto d) {
+    return launch_prefill_t<decltype(t), decltype(d)::value>(p, q, nullptr, nullptr, nullptr, nullptr,
+                                                             nullptr, shared_blocks, nsb, 1, hq, batch,
+                                                             batch, scale, cas, s);
+  });
 }
 
 }  // namespace kvb

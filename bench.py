@@ -363,33 +363,9 @@ def main(argv=None):
     return 0
 
 
-def bench_decode(torch, kvb, args):
-    """The paged-decode workload: 64 sequences, contexts U{512..4096} (seed 3), first 1024
-    tokens shared, 32/8 heads, d=128, bf16, pool of 16384 blocks."""
-    from workloads import make_config
-    w = make_config("decode")
-    k = _dev_bits(torch, w.k_pool, w.dtype)
-    v = _dev_bits(torch, w.v_pool, w.dtype)
-    pool = kvb.Pool.from_tensors(k, v)
-    q = _dev_bits(torch, w.q, w.dtype)
-    ctx = _idev(torch, w.context_lens)
-    bt = _idev(torch, w.block_tables)
-    out = torch.empty_like(q)
-    max_ctx = int(w.context_lens.max())
-    sb = args.split_blocks
-    n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx, sb)
-    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
-    # Cache flush by READING 1 GiB (more than L2 + Infinity Cache): a write-based flush
-    # would leave dirty lines whose write-back then competes with the timed kernel.
-    flush = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
-
-    def run():
-        kvb.paged_decode(pool, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
-
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    steps = max(args.steps, 10)
+def _time_warm_cold(torch, run, steps, flush):
+    """Mean ms of `run` launched back to back (warm caches) and after a 1 GiB read that
+    evicts L2 and the Infinity Cache (cold); events bracket the launch only."""
     warm, cold = [], []
     for _ in range(steps):
         a = torch.cuda.Event(enable_timing=True)
@@ -403,8 +379,52 @@ def bench_decode(torch, kvb, args):
         a.record(); run(); b.record()
         cold.append((a, b))
     torch.cuda.synchronize()
-    tw = float(np.mean([a.elapsed_time(b) for a, b in warm]))
-    tc = float(np.mean([a.elapsed_time(b) for a, b in cold]))
+    return (float(np.mean([a.elapsed_time(b) for a, b in warm])),
+            float(np.mean([a.elapsed_time(b) for a, b in cold])))
+
+
+def bench_decode(torch, kvb, args):
+    """The paged-decode workload: 64 sequences, contexts U{512..4096} (seed 3), first 1024
+    tokens shared, 32/8 heads, d=128, bf16, pool of 16384 blocks.  Timed as the plain split
+    decode and as the shared-prefix (cascade) decode, which reads the 1024 shared tokens
+    once for all sequences; both produce the same output up to rounding."""
+    from workloads import make_config
+    w = make_config("decode")
+    k = _dev_bits(torch, w.k_pool, w.dtype)
+    v = _dev_bits(torch, w.v_pool, w.dtype)
+    pool = kvb.Pool.from_tensors(k, v)
+    q = _dev_bits(torch, w.q, w.dtype)
+    ctx = _idev(torch, w.context_lens)
+    bt = _idev(torch, w.block_tables)
+    out = torch.empty_like(q)
+    max_ctx = int(w.context_lens.max())
+    sb = args.split_blocks
+    n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx, sb)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
+    members, shared_ids = w.notes["first_group"]
+    shared = _idev(torch, np.asarray(shared_ids, dtype=np.int32))
+    shared_len = 16 * len(shared_ids)
+    nc = kvb.paged_decode_cascade_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                                 max_ctx, shared_len, sb)
+    wsc = torch.empty(max(nc, 16), dtype=torch.uint8, device="cuda:0")
+    # Cache flush by READING 1 GiB (more than L2 + Infinity Cache): a write-based flush
+    # would leave dirty lines whose write-back then competes with the timed kernel.
+    flush = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")
+
+    def run():
+        kvb.paged_decode(pool, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
+
+    def run_cascade():
+        kvb.paged_decode_cascade(pool, q, ctx, bt, shared, shared_len, w.scale, max_ctx,
+                                 split_blocks=sb, out=out, workspace=wsc)
+
+    for _ in range(args.warmup):
+        run()
+        run_cascade()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 10)
+    tw, tc = _time_warm_cold(torch, run, steps, flush)
+    cw, cc = _time_warm_cold(torch, run_cascade, steps, flush)
     by = decode_bytes(w, w.context_lens, w.block_tables)
     logical = float(np.sum(w.context_lens)) * w.num_kv_heads * w.head_dim * 2 * ESZ
     return {"workload": "paged decode, 64 sequences, contexts 512..4096, first 1024 tokens shared",
@@ -412,7 +432,11 @@ def bench_decode(torch, kvb, args):
             "gbps_back_to_back": by / (tw * 1e-3) / 1e9, "gbps_cold_cache": by / (tc * 1e-3) / 1e9,
             "frac_hbm_peak_cold": by / (tc * 1e-3) / 1e9 / PEAK_GBPS,
             "logical_kv_gbps_cold": logical / (tc * 1e-3) / 1e9,
-            "tflops_cold": decode_flops(w.context_lens, w) / (tc * 1e-3) / 1e12}
+            "tflops_cold": decode_flops(w.context_lens, w) / (tc * 1e-3) / 1e12,
+            "cascade": {"shared_tokens": shared_len, "ms_back_to_back": cw, "ms_cold_cache": cc,
+                        "gbps_back_to_back": by / (cw * 1e-3) / 1e9,
+                        "gbps_cold_cache": by / (cc * 1e-3) / 1e9,
+                        "frac_hbm_peak_cold": by / (cc * 1e-3) / 1e9 / PEAK_GBPS}}
 
 
 if __name__ == "__main__":

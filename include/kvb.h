@@ -120,12 +120,36 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
                             int32_t max_context_len, int32_t split_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Shared-prefix (cascade) decode: the same result as kvb_paged_decode, but the first
+ * shared_len tokens of every sequence are one shared prefix, read once for all sequences'
+ * queries instead of once per sequence (kvboost 0.6.0, "How batching works" step 4: a
+ * shared prefix's KV is loaded once and broadcast across the batch).  Logical block
+ * j < shared_len/16 of every sequence is shared_blocks[j]; those entries of block_tables
+ * are not read.  A sequence with context_lens[b] < shared_len sees only its first
+ * context_lens[b] tokens.  The shared part runs as one tiled pass over all queries of
+ * each KV head (split over key tiles), the rest as the split decode, and every partial
+ * (unnormalised output, max, sum) is merged by log-sum-exp.
+ * shared_blocks: (device) int32 [ceil(shared_len/16)], may be NULL when shared_len == 0;
+ * shared_len: a multiple of 16, >= 0.  Other arguments as kvb_paged_decode.
+ * workspace: (device, required) at least kvb_paged_decode_cascade_workspace_size(...) bytes
+ * for the same batch, heads, head_dim, max_context_len, shared_len and split_blocks. */
+kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t block_table_stride, const int32_t* shared_blocks,
+                                    int32_t shared_len, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, int32_t split_blocks, float scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace sizes in bytes (0 = none needed).  Pure host arithmetic. */
 size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                         int32_t total_q, int32_t max_prefix_len);
 size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                        int32_t head_dim, int32_t max_context_len,
                                        int32_t split_blocks);
+size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_heads,
+                                               int32_t num_q_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t shared_len,
+                                               int32_t split_blocks);
 
 /* Test helper: gather through the block tables into a contiguous layout, bit-exact.
  * For b < batch, j < seq_lens[b]:

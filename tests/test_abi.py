@@ -127,6 +127,37 @@ def test_decode_validation_and_workspace(lib):
     assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 16 * 4 * 8 * (128 + 2) * 4
 
 
+def cascade(lib, p, **kw):
+    a = dict(q=FAKE, out=FAKE, ctx=FAKE, bt=FAKE, stride=256, shared=FAKE, slen=1024, batch=4,
+             hq=8, maxc=4000, sb=0, scale=0.1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kvb_paged_decode_cascade(ctypes.byref(p), a["q"], a["out"], a["ctx"], a["bt"],
+                                        a["stride"], a["shared"], a["slen"], a["batch"], a["hq"],
+                                        a["maxc"], a["sb"], a["scale"], a["ws"], a["wsb"], None)
+
+
+def test_cascade_decode_validation_and_workspace(lib):
+    p = pool()
+    need = lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 4000, 1024, 0)
+    assert need > 0
+    # the shared part adds workspace slots to the split decode's
+    assert need > lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000 - 1024, 0)
+    assert cascade(lib, p) == WS                      # always needs a workspace
+    assert cascade(lib, p, ws=FAKE, wsb=need - 1) == WS
+    assert cascade(lib, p, ws=FAKE + 8, wsb=need) == INVALID
+    assert cascade(lib, p, slen=1000) == INVALID      # whole blocks only
+    assert cascade(lib, p, slen=-16) == INVALID
+    assert cascade(lib, p, shared=None) == NULL
+    assert cascade(lib, p, shared=FAKE + 2) == INVALID
+    assert cascade(lib, p, stride=249) == INVALID
+    assert cascade(lib, p, hq=5) == INVALID
+    assert cascade(lib, p, batch=0) == OK
+    # no shared prefix: the shared block list may be NULL
+    need0 = lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 4000, 0, 0)
+    assert cascade(lib, p, shared=None, slen=0, ws=FAKE + 16, wsb=need0 - 1) == WS
+    assert lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 4000, 1000, 0) == 0
+
+
 def test_prefill_workspace_is_zero(lib):
     assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 0
 

@@ -80,3 +80,26 @@ def test_decode_full_size_sampled():
                               w.dtype, seqs=seqs)
     err = float(np.max(np.abs(vals[seqs] - ref[seqs])))
     assert err <= u.TOL[w.dtype], f"max abs err {err}"
+
+
+def test_cascade_decode_full_size_sampled():
+    """The decode workload's first 1024 tokens (64 blocks) are one shared prefix; the
+    cascade form reads them once for all 64 sequences."""
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    w = make_config("decode", poison=True)
+    dev = u.Dev(w)
+    members, ids = w.notes["first_group"]
+    assert len(members) == w.batch and len(ids) == 64
+    got = u.to_bits(kvb.paged_decode_cascade(dev.pool, dev.q, dev.ctx, dev.bt, u.idev(ids), 1024,
+                                             w.scale, int(w.context_lens.max())))
+    torch.cuda.synchronize()
+    import oracle
+    vals = oracle.decode_bits(got, w.dtype)
+    assert np.isfinite(vals).all()
+    rng = np.random.default_rng(97)
+    seqs = sorted(set([0, w.batch - 1] + [int(x) for x in rng.integers(0, w.batch, size=10)]))
+    ref = oracle.paged_decode(w.k_pool, w.v_pool, w.q, w.context_lens, w.block_tables, w.scale,
+                              w.dtype, seqs=seqs)
+    err = float(np.max(np.abs(vals[seqs] - ref[seqs])))
+    assert err <= u.TOL[w.dtype], f"max abs err {err}"

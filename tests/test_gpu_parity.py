@@ -216,3 +216,62 @@ def test_decode_equals_one_row_prefill_within_tolerance():
     assert u.max_err(got, ref, "fp16") <= 1e-2
     a = u.to_bits(dev.decode(split_blocks=2))
     assert np.array_equal(a, got)          # run-to-run deterministic
+
+
+# ------------------------------------------------------------------ cascade decode
+
+CASCADE_CASES = [
+    # seed, dtype, Hq, Hkv, d, context lengths, shared blocks
+    (401, "bf16", 32, 8, 128, [1024, 1500, 2100, 1030, 900, 17, 1024, 3000], 64),
+    (402, "fp16", 40, 8, 96, [300, 600, 513, 512, 1], 32),          # G=5, contexts below the share
+    (403, "bf16", 8, 1, 64, [64, 65, 10, 200, 0], 4),               # MQA, a zero context
+    (404, "fp16", 16, 16, 128, [800, 1200], 0),                     # no shared prefix
+    (405, "bf16", 16, 2, 128, [4096, 4096, 4000, 4090], 256),       # (almost) all shared
+]
+
+
+@pytest.mark.parametrize("case", CASCADE_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_sh{c[6]}")
+@pytest.mark.parametrize("split", [0, 3])
+def test_cascade_decode_matches_oracle(case, split):
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    seed, dt, hq, hkv, d, ctx, nsh = case
+    w = make_custom(seed, dt, hq, hkv, d, ctx, kind="decode",
+                    share=f"first:{nsh}" if nsh else "none", poison=True)
+    dev = u.Dev(w)
+    shared = u.idev(w.notes["first_group"][1]) if nsh else None
+    # the shared entries of the block tables must not be read: point them at a NaN block
+    bt = w.block_tables.copy()
+    assert w.poison_block >= 0
+    bt[:, :nsh] = w.poison_block
+    got = u.to_bits(kvb.paged_decode_cascade(dev.pool, dev.q, dev.ctx, u.idev(bt), shared, 16 * nsh,
+                                             w.scale, int(max(ctx)), split_blocks=split))
+    torch.cuda.synchronize()
+    ref = u.oracle_decode(w)                          # the true tables
+    vals = oracle.decode_bits(got, dt)
+    assert np.isfinite(vals).all()
+    for b, n in enumerate(ctx):
+        if n <= 0:
+            assert (got[b] == 0).all()
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+def test_cascade_decode_equals_plain_decode_within_tolerance():
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    w = make_custom(406, "bf16", 32, 8, 128, [700, 2000, 1300, 1100, 4001, 690], kind="decode",
+                    share="first:40", poison=True)
+    dev = u.Dev(w)
+    shared = u.idev(w.notes["first_group"][1])
+    a = u.to_bits(dev.decode())
+    c1 = u.to_bits(kvb.paged_decode_cascade(dev.pool, dev.q, dev.ctx, dev.bt, shared, 640, w.scale, 4001))
+    c2 = u.to_bits(kvb.paged_decode_cascade(dev.pool, dev.q, dev.ctx, dev.bt, shared, 640, w.scale, 4001))
+    assert np.array_equal(c1, c2)                     # run-to-run deterministic
+    assert u.max_err(c1, oracle_decode_bits(a, "bf16"), "bf16") <= 2e-2
+
+
+def oracle_decode_bits(bits, dt):
+    import oracle
+    return oracle.decode_bits(bits, dt)

@@ -222,6 +222,10 @@ def _build(name, seed, dtype, Hq, Hkv, d, num_blocks, prefix_lens, q_lens,
             shared_refs += counts[table[b][j]] > 1
     w.shared_fraction = shared_refs / refs if refs else 0.0
     w.notes["unique_blocks"] = len(counts)
+    # physical blocks of the first sharing group (placed first: perm[0:n]), for callers
+    # that pass a shared prefix as a block list
+    if groups:
+        w.notes["first_group"] = (list(groups[0][0]), [int(x) for x in perm[:groups[0][1]]])
     return w
 
 
@@ -293,7 +297,8 @@ def make_custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head
     """Small workloads for parity tests.
 
     ``share``: "none", "all" (every sequence shares the full blocks of the
-    shortest prefix) or "pairs" (random pairs share leading full blocks).
+    shortest prefix), "pairs" (random pairs share leading full blocks) or "first:N"
+    (every sequence's first N blocks, as far as it has them, are shared).
     For ``kind="decode"`` ``prefix_lens`` are the context lengths.
     """
     rng = np.random.default_rng(seed)
@@ -304,6 +309,8 @@ def make_custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head
         ctx = [int(p) for p in prefix_lens]
         q_lens = [0] * B
     need = sum(blocks_for(t) for t in ctx) + 1
+    if share.startswith("first:"):
+        need += int(share.split(":")[1])
     if num_blocks is None:
         num_blocks = need + 3
     if share == "all":
@@ -312,6 +319,11 @@ def make_custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head
         groups_fn = (lambda p: [(list(range(B)), nmin)]) if nmin > 0 else (lambda p: [])
     elif share == "pairs":
         groups_fn = _pair_groups([int(p) for p in prefix_lens])
+    elif share.startswith("first:"):
+        # every sequence's logical blocks 0..n-1 (as far as it has them) are the same
+        # n physical blocks, whatever its length
+        n_first = int(share.split(":")[1])
+        groups_fn = lambda p: [(list(range(B)), n_first)]
     else:
         groups_fn = lambda p: []
     return _build(f"custom{seed}", seed, dtype, num_q_heads, num_kv_heads, head_dim, num_blocks,
