@@ -101,7 +101,7 @@ struct PfCascade {
 // row max and scales its scores.  K is therefore staged one tile ahead of V: LDS holds
 // two K buffers and two V buffers per key part; step j loads K of tile j+2 and V of tile
 // j+1, and one barrier per step publishes them.
-template <typename T, int D, int KS>
+template <typename T, int D, int KS, bool CAS>
 __global__ void __launch_bounds__(256 * KS, 2 / KS)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -126,10 +126,11 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
   // logical id -> (kvh, b, key split, tile), tile fastest and KV head slowest
-  const bool cascade = cas.ctx != nullptr;
+  constexpr bool cascade = CAS;
   int r = lid;
   const int tile = r % max_tiles; r /= max_tiles;
-  const int ks = r % cas.nks; r /= cas.nks;
+  const int ks = CAS ? r % cas.nks : 0;
+  if (CAS) r /= cas.nks;
   const int b = r % batch;
   const int kvh = r / batch;
   const int G = hq / hkv;
@@ -169,7 +170,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // largest one are not even loaded (they read as zero), so every key row that reaches
   // the PV product holds a real token of some sequence of this work-group.
   int row_lim = 0x7fffffff, wg_lim = 0x7fffffff, P = P0;
-  if (cascade) {
+  if constexpr (CAS) {
     const int cap = min(P0, cas.max_ctx);
     row_lim = rvalid ? min(cap, max(0, cas.ctx[i_row])) : 0;
     int mn = 0x7fffffff, mx = 0;
@@ -302,13 +303,17 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   for (int kk = 0; kk < NKK; ++kk) kaddr[kk] = part_base + (uint32_t)(lr * CPR + L::posK(lr, 2 * kk + hf)) * 16;
   // V transpose-read source: rows 16*kp4 + 4*hf + (l%16)/4 (+8 for the high half),
   // columns 32*db + 16*((l/16)%2) + 4*(l%4), i.e. chunk 4*db + 2*((l/16)%2) + (l%4)/2
-  uint32_t vaddr[NDB][2];
+  // At head dims 128 and 64 the V chunk permutation repeats every 8 rows, so the high
+  // half's address is the low half's plus a constant (one register per d block).
+  constexpr bool kVRep8 = D != 96;
+  constexpr int NVH = kVRep8 ? 1 : 2;
+  uint32_t vaddr[NDB][NVH];
   {
     const int s4 = (lane & 15) >> 2;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
+      for (int hi = 0; hi < NVH; ++hi) {
         const int row = 4 * hf + s4 + 8 * hi;
         const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
         vaddr[db][hi] = part_base + (uint32_t)((row * CPR + L::posV(row, c)) * 16 + 8 * (lane & 1));
@@ -318,8 +323,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     return *reinterpret_cast<const s16x8*>(lds + (kaddr[kk] + off + (uint32_t)(half * 32 * D * 2)));
   };
   auto v_operand = [&](uint32_t off, int db, int kp4) {
+    const uint32_t a_hi = kVRep8 ? vaddr[db][0] + (uint32_t)(8 * CPR * 16) : vaddr[db][NVH - 1];
     const s16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(lds + (vaddr[db][0] + off + (uint32_t)(kp4 * 16 * D * 2))));
-    const s16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(lds + (vaddr[db][1] + off + (uint32_t)(kp4 * 16 * D * 2))));
+    const s16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(lds + (a_hi + off + (uint32_t)(kp4 * 16 * D * 2))));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
@@ -609,7 +615,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   emit([&](int db, int rr) { return o[db][rr] * a0 + my[(db * 16 + rr) * 64 + lane] * a1; }, M, lt);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool CAS>
 static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void* kn, const void* vn,
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
@@ -627,13 +633,13 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   // split inside each work-group instead, so every SIMD still runs two waves.
   const bool split = real < 2LL * device_cu_count();
   if (split)
-    hipLaunchKernelGGL((prefill_kernel<T, D, 2>), dim3((unsigned)padded), dim3(512), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 2, CAS>), dim3((unsigned)padded), dim3(512), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
                        (int)padded, (int)real, cas);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, 1>), dim3((unsigned)padded), dim3(256), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 1, CAS>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
@@ -658,7 +664,7 @@ hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, cons
   (void)max_prefix_len;
   const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
   return dispatch_prefill(p, [&](auto t, auto d) {
-    return launch_prefill_t<decltype(t), decltype(d)::value>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
+    return launch_prefill_t<decltype(t), decltype(d)::value, false>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
                                                              batch, hq, total_q, max_q_len, scale, none, s);
   });
 }
@@ -685,7 +691,7 @@ hipError_t launch_cascade_shared(const kvb_pool& p, const void* q, const int32_t
   const PfCascade cas{ctx, max_ctx, shared_len, ks_tiles, nks, ws_o, ws_ml, ws_slots};
   const int nsb = (shared_len + kBlock - 1) / kBlock;
   return dispatch_prefill(p, [&](auto t, auto d) {
-    return launch_prefill_t<decltype(t), decltype(d)::value>(p, q, nullptr, nullptr, nullptr, nullptr,
+    return launch_prefill_t<decltype(t), decltype(d)::value, true>(p, q, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, shared_blocks, nsb, 1, hq, batch,
                                                              batch, scale, cas, s);
   });
