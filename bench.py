@@ -198,6 +198,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step from eager launches instead of a captured HIP graph")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back runs before the warmup steps so clocks reach steady state")
     ap.add_argument("--config", default="shared_prompt",
                     choices=["shared_prompt", "long_prefix", "ragged_d96", "ragged_d64", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -277,9 +281,13 @@ def main(argv=None):
                 part(p_)
             parts = ["decode"]
 
-    for _ in range(args.warmup):
+    def one_step():
         for p_ in parts:
             part(p_)
+
+    settle(torch, one_step, args.settle_ms)
+    for _ in range(args.warmup):
+        one_step()
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
@@ -297,7 +305,33 @@ def main(argv=None):
     total_ms = t_start.elapsed_time(t_end)
     per_part = {p_: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
                 for i, p_ in enumerate(parts)}
-    ms_step = total_ms / args.steps
+    ms_step_eager = total_ms / args.steps
+
+    # The whole step as one HIP graph, the way a serving loop runs it: one launch per step
+    # instead of four, so the step time is the kernels' time rather than host launch gaps.
+    # The per-kernel times above come from the eager pass (events between the kernels).
+    ms_step, launch = ms_step_eager, "eager"
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_step, launch = g0.elapsed_time(g1) / args.steps, "hip graph"
 
     pf = prefill_flops(w)
     df = decode_flops(w.dec_context_lens, w)
@@ -324,7 +358,10 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms_step,
+        "ms_per_step_eager_launches": ms_step_eager,
+        "launch": launch,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -361,6 +398,17 @@ def main(argv=None):
 
     print(json.dumps(res))
     return 0
+
+
+def settle(torch, fn, ms: float) -> None:
+    """Run `fn` back to back for about `ms` milliseconds (untimed).  The GPU raises its
+    clocks only after some time under load; without this the first timed steps of a short
+    run are measured at lower clocks than the steady state the kernels run at when busy."""
+    t0 = time.time()
+    while (time.time() - t0) * 1e3 < ms:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
 
 
 def _time_warm_cold(torch, run, steps, flush):
@@ -418,6 +466,7 @@ def bench_decode(torch, kvb, args):
         kvb.paged_decode_cascade(pool, q, ctx, bt, shared, shared_len, w.scale, max_ctx,
                                  split_blocks=sb, out=out, workspace=wsc)
 
+    settle(torch, lambda: (run(), run_cascade()), args.settle_ms)
     for _ in range(args.warmup):
         run()
         run_cascade()
