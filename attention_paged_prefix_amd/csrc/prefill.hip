@@ -7,22 +7,21 @@
 // future K/V tiles).  That page's CUDA kernel is prior art; this kernel is laid out for
 // CDNA4 (gfx950):
 //
-//  * Work-group = 4 waves = 128 "virtual rows" of one (sequence, KV head).  Virtual
-//    row v = i*G + g packs chunk row i and query head kvh*G + g, so the G query heads
-//    that share a KV head share every K/V tile staged in LDS (GQA packing; works for
-//    any G, including 5).
-//  * K/V tiles of 64 keys = four 16-token blocks.  Each block (or each 16-row group of
-//    the chunk's own K/V) is read through a buffer resource sized to its valid rows:
-//    one 16-byte load per thread, rows past the end read as zero with no memory
-//    traffic, and every load is unconditional so it overlaps the previous tile's math.
-//  * LDS is double buffered: tile t+1 is loaded into registers while tile t is used,
-//    then stored to the other buffer; one barrier per tile.
+//  * Each wave owns 32 "virtual rows" v = i*G + g (chunk row i, query head kvh*G + g),
+//    so the G query heads that share a KV head share every K/V tile staged in LDS
+//    (GQA packing; works for any G, including 5).
+//  * K/V tiles of 64 keys = four 16-token blocks, copied straight from the pool (or the
+//    chunk's own K/V) into LDS by buffer loads with an LDS destination, 1 KiB per
+//    instruction, through buffer resources sized to the valid rows (rows past the end
+//    read as zero, with no memory traffic).  The 16-byte chunks of each LDS row are
+//    permuted so that both operand read patterns are bank-conflict free.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 (A = K rows
-//    from LDS, B = Q held in registers for the whole kernel).  Each lane then owns one
-//    query row, so the row max needs one cross-lane step and the row sum none.
-//  * The output is accumulated transposed, O^T += V^T P^T: the score accumulators are
-//    already the B operand, and V stays in its natural row-major layout in LDS and is
-//    read transposed with ds_read_b64_tr_b16.
+//    from LDS, B = Q held in registers), so each lane owns one query row; the output is
+//    accumulated transposed, O^T += V^T P^T: the score accumulators are already the B
+//    operand and V is read transposed with ds_read_b64_tr_b16.
+//  * Software pipelined inside each wave: while the S MFMAs of tile j+1 run, the VALU
+//    turns tile j's scores into probabilities; while the PV MFMAs of tile j run, it takes
+//    tile j+1's row max.  K is staged one tile ahead of V.
 //  * Online softmax in the exp2 domain with scale*log2(e) folded into one FMA; the
 //    running max only moves (and the output is only rescaled) when a score exceeds it
 //    by more than 2^8.  Only tiles crossing the causal diagonal or the end of the keys
