@@ -32,13 +32,15 @@ summing to one; a single key returning its V; equal scores returning the mean
 of V; block-permutation invariance; the reuse invariant (prefill over a cached
 prefix equals full causal attention on those rows); decode equals a one-row
 prefill; GQA equals MHA with repeated K/V; causality; the log-sum-exp merge of
-key partitions.  The softmax scale 1/sqrt(head_dim) is the conventional reading
+key partitions; block copies leave every sequence's gathered tokens unchanged under
+a remapped table.  The softmax scale 1/sqrt(head_dim) is the conventional reading
 (the tiny workload states it; the pages state no other): parity unpinned by the
 pages for that convention beyond the tiny workload.
 """
 from .attention import (  # noqa: F401
     decode_bits,
     write_kv,
+    copy_blocks,
     gather_kv,
     attend,
     paged_prefill,

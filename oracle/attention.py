@@ -44,6 +44,27 @@ def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: n
     return kp, vp
 
 
+def copy_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                src_ids: Sequence[int], dst_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """Whole-block copies between two pools of the same shape.
+
+    A sequence about to write into a physical block it shares copy-on-write first
+    gets a private copy of it (kvboost 0.6.0, "CPU paged attention"; kvstream 0.1.0,
+    "Request lifecycle" step 3), and low-priority sequences are spilled to a CPU page
+    pool and brought back (kvstream 0.1.0, "Why KVStream?", swap & preemption).  Block
+    ``dst_ids[i]`` becomes block ``src_ids[i]`` (every head, every row); a pair with an
+    id outside its pool is skipped.  Returns new destination arrays.
+    """
+    dk = np.array(dst_k, copy=True)
+    dv = np.array(dst_v, copy=True)
+    for s_id, d_id in zip(np.asarray(src_ids, dtype=np.int64), np.asarray(dst_ids, dtype=np.int64)):
+        if not (0 <= s_id < src_k.shape[0] and 0 <= d_id < dk.shape[0]):
+            continue
+        dk[d_id] = src_k[s_id]
+        dv[d_id] = src_v[s_id]
+    return dk, dv
+
+
 def gather_kv(pool: np.ndarray, table_row: np.ndarray, n_tokens: int) -> np.ndarray:
     """Logical tokens 0..n_tokens-1 of one sequence, gathered through its block table.
 

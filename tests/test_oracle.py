@@ -358,3 +358,30 @@ def test_selected_rows_equal_full_result():
     b_ = oracle.paged_decode(dec.k_pool, dec.v_pool, dec.q, dec.context_lens, dec.block_tables, dec.scale, "fp16",
                              seqs=[2])
     np.testing.assert_allclose(a[2], b_[2], rtol=0, atol=1e-14)
+
+
+def test_copy_blocks_preserves_sequences_through_remapped_tables():
+    """A sequence whose blocks are copied elsewhere and whose table is remapped to the
+    copies gathers to exactly the same tokens; other destination blocks are untouched,
+    and pairs with an id outside its pool are skipped."""
+    w = make_custom(31, "bf16", 4, 2, 64, [70, 33], poison=True, kind="decode")
+    nb = w.num_blocks
+    rng = np.random.default_rng(3)
+    host_k = rng.integers(0, 1 << 16, size=(nb + 5,) + w.k_pool.shape[1:]).astype(np.uint16)
+    host_v = rng.integers(0, 1 << 16, size=(nb + 5,) + w.v_pool.shape[1:]).astype(np.uint16)
+    src = list(w.block_tables[0][:5])
+    dst = [nb + 4, 0 + 7, 3, 11, 2]
+    ids_s = src + [nb + 100, 1]
+    ids_d = dst + [5, -1]                             # invalid pairs: skipped
+    hk, hv = oracle.copy_blocks(w.k_pool, w.v_pool, host_k, host_v, ids_s, ids_d)
+    for a, b in ((hk, host_k), (hv, host_v)):
+        keep = np.ones(nb + 5, bool)
+        keep[dst] = False
+        assert np.array_equal(a[keep], b[keep])
+    table = np.asarray(dst, np.int32)
+    n = int(w.context_lens[0])
+    assert np.array_equal(oracle.gather_kv(hk, table, n), oracle.gather_kv(w.k_pool, w.block_tables[0], n))
+    assert np.array_equal(oracle.gather_kv(hv, table, n), oracle.gather_kv(w.v_pool, w.block_tables[0], n))
+    # round trip back into a fresh pool: identity on the copied blocks
+    bk, bv = oracle.copy_blocks(hk, hv, np.zeros_like(w.k_pool), np.zeros_like(w.v_pool), dst, src)
+    assert np.array_equal(bk[src], w.k_pool[src]) and np.array_equal(bv[src], w.v_pool[src])
