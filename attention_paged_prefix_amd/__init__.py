@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool  # noqa: F401
 
 __all__ = [
-    "Pool", "write_kv", "paged_prefill", "paged_decode", "paged_decode_cascade", "gather_kv",
+    "Pool", "write_kv", "paged_prefill", "paged_decode", "paged_decode_cascade", "copy_blocks",
+    "gather_kv",
     "paged_prefill_workspace_size", "paged_decode_workspace_size",
     "paged_decode_cascade_workspace_size", "version", "KvbError",
 ]
@@ -199,3 +200,14 @@ def paged_decode_cascade(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
         int(max_context_len), int(split_blocks), float(scale), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def copy_blocks(src: Pool, dst: Pool, src_ids: torch.Tensor, dst_ids: torch.Tensor,
+                stream=None) -> None:
+    """kvb_copy_blocks: block dst_ids[i] of ``dst`` becomes a copy of block src_ids[i] of
+    ``src`` (K and V, every head).  ``src_ids``/``dst_ids``: int32 device tensors."""
+    lib = _lib.load()
+    a, b = src.c_struct(), dst.c_struct()
+    _lib.check("kvb_copy_blocks", lib.kvb_copy_blocks(
+        ctypes.byref(a), ctypes.byref(b), _ptr(src_ids), _ptr(dst_ids), int(src_ids.numel()),
+        _stream(stream)))

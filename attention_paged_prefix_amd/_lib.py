@@ -28,6 +28,7 @@ EXPORTS = (
     "kvb_paged_prefill_workspace_size",
     "kvb_paged_decode_workspace_size",
     "kvb_paged_decode_cascade_workspace_size",
+    "kvb_copy_blocks",
     "kvb_gather_kv",
     "kvb_status_str",
     "kvb_version",
@@ -89,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_decode_workspace_size.restype = _sz
     lib.kvb_paged_decode_cascade_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.kvb_paged_decode_cascade_workspace_size.restype = _sz
+    lib.kvb_copy_blocks.argtypes = [_PP, _PP, _vp, _vp, _i32, _vp]
+    lib.kvb_copy_blocks.restype = ctypes.c_int
     lib.kvb_gather_kv.argtypes = [_PP, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     lib.kvb_gather_kv.restype = ctypes.c_int
     lib.kvb_status_str.argtypes = [ctypes.c_int]

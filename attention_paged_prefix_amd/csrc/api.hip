@@ -187,6 +187,41 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
                                                   nks, kt, scale, workspace, (hipStream_t)stream));
 }
 
+// Address the device uses for p: itself for device memory, the mapped address for pinned
+// host memory; NULL for memory the device cannot address (e.g. pageable host memory).
+static void* device_address(void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();                 // clear the sticky error of an unknown pointer
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return p;
+  if (a.type == hipMemoryTypeHost) return a.devicePointer;
+  return nullptr;
+}
+
+kvb_status kvb_copy_blocks(const kvb_pool* src, const kvb_pool* dst, const int32_t* src_ids,
+                           const int32_t* dst_ids, int32_t n, void* stream) {
+  kvb_status st = check_pool(src);
+  if (st != KVB_OK) return st;
+  if ((st = check_pool(dst)) != KVB_OK) return st;
+  if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim ||
+      src->dtype != dst->dtype)
+    return KVB_ERR_INVALID;
+  if (n < 0) return KVB_ERR_INVALID;
+  if (n == 0) return KVB_OK;
+  if (!src_ids || !dst_ids) return KVB_ERR_NULL;
+  if (((uintptr_t)src_ids & 3u) || ((uintptr_t)dst_ids & 3u)) return KVB_ERR_INVALID;
+  // either pool may live in pinned host memory (swap): use the addresses the device sees
+  kvb_pool s = *src, d = *dst;
+  s.k = device_address(s.k);
+  s.v = device_address(s.v);
+  d.k = device_address(d.k);
+  d.v = device_address(d.v);
+  if (!s.k || !s.v || !d.k || !d.v) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_copy_blocks(s, d, src_ids, dst_ids, n, (hipStream_t)stream));
+}
+
 kvb_status kvb_gather_kv(const kvb_pool* pool, const int32_t* block_tables,
                          int32_t block_table_stride, const int32_t* seq_lens,
                          const int32_t* cu_seq_lens, void* k_out, void* v_out, int32_t batch,

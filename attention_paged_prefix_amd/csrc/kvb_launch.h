@@ -22,6 +22,8 @@ inline int device_cu_count() {
 
 hipError_t launch_write_kv(const kvb_pool& p, const void* kn, const void* vn, const int64_t* slots,
                            int num_tokens, hipStream_t s);
+hipError_t launch_copy_blocks(const kvb_pool& src, const kvb_pool& dst, const int32_t* src_ids,
+                              const int32_t* dst_ids, int n, hipStream_t s);
 hipError_t launch_gather_kv(const kvb_pool& p, const int32_t* bt, int bt_stride,
                             const int32_t* seq_lens, const int32_t* cu, void* ko, void* vo,
                             int batch, int max_len, hipStream_t s);

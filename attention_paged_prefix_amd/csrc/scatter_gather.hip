@@ -59,6 +59,35 @@ gather_kv_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ v
   *reinterpret_cast<uint4*>(vo + dst) = *reinterpret_cast<const uint4*>(vp + src);
 }
 
+// Whole-block copies between two pools of the same shape (kvboost 0.6.0, "CPU paged
+// attention": shared prefixes share physical blocks copy-on-write; kvstream 0.1.0, "Why
+// KVStream?": sequences spilled to a CPU page pool).  One work-group per (pair, K or V
+// part); the part of a block, num_kv_heads x 16 x head_dim, is contiguous.  Pairs whose
+// source or destination id is outside its pool are skipped.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(const uint16_t* __restrict__ sk, const uint16_t* __restrict__ sv, int64_t s_stride,
+                   int s_nb, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t d_stride,
+                   int d_nb, const int32_t* __restrict__ src_ids, const int32_t* __restrict__ dst_ids,
+                   int64_t chunks) {
+  const int i = blockIdx.x;
+  const int sb = src_ids[i], db = dst_ids[i];
+  if (sb < 0 || sb >= s_nb || db < 0 || db >= d_nb) return;
+  const uint4* src = reinterpret_cast<const uint4*>((blockIdx.y ? sv : sk) + (int64_t)sb * s_stride);
+  uint4* dst = reinterpret_cast<uint4*>((blockIdx.y ? dv : dk) + (int64_t)db * d_stride);
+  for (int64_t c = threadIdx.x; c < chunks; c += 256) dst[c] = src[c];
+}
+
+hipError_t launch_copy_blocks(const kvb_pool& src, const kvb_pool& dst, const int32_t* src_ids,
+                              const int32_t* dst_ids, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t chunks = (int64_t)src.num_kv_heads * kBlock * src.head_dim / 8;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n, 2), dim3(256), 0, s,
+                     (const uint16_t*)src.k, (const uint16_t*)src.v, src.block_stride, src.num_blocks,
+                     (uint16_t*)dst.k, (uint16_t*)dst.v, dst.block_stride, dst.num_blocks, src_ids,
+                     dst_ids, chunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_write_kv(const kvb_pool& p, const void* kn, const void* vn, const int64_t* slots,
                            int num_tokens, hipStream_t s) {
   const int64_t total = (int64_t)num_tokens * p.num_kv_heads * (p.head_dim / 8);

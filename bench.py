@@ -207,7 +207,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0, help="decode split size (0 = auto)")
     ap.add_argument("--no-decode", action="store_true", help="skip the separate decode workload")
-    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy", "decode_workload"],
+    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy", "decode_workload",
+                                       "copy_blocks"],
                     default="step", help="profiling aid: time only one part")
     args = ap.parse_args(argv)
 
@@ -236,6 +237,9 @@ def main(argv=None):
 
     if args.only == "decode_workload":
         print(json.dumps(bench_decode(torch, kvb, args)))
+        return 0
+    if args.only == "copy_blocks":
+        print(json.dumps(bench_copy_blocks(torch, kvb, args)))
         return 0
 
     w = make_config(args.config, with_decode=True)
@@ -429,6 +433,44 @@ def _time_warm_cold(torch, run, steps, flush):
     torch.cuda.synchronize()
     return (float(np.mean([a.elapsed_time(b) for a, b in warm])),
             float(np.mean([a.elapsed_time(b) for a, b in cold])))
+
+
+def bench_copy_blocks(torch, kvb, args):
+    """Block copies (kvb_copy_blocks) of 1024 random blocks of a 16384-block pool, 8 KV
+    heads, d=128, bf16 (64 KiB per block, K and V): inside the device pool (copy-on-write)
+    and between the device pool and a pool in pinned host memory (swap out / in)."""
+    nb, n, hkv, d = 16384, 1024, 8, 128
+    k = torch.empty((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda:0").normal_()
+    v = torch.empty_like(k).normal_()
+    dev = kvb.Pool.from_tensors(k, v)
+    hk = torch.empty((n, hkv, 16, d), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    host = kvb.Pool.from_tensors(hk, hv)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(nb)
+    src = torch.as_tensor(perm[:n].astype(np.int32)).to("cuda:0")
+    dst = torch.as_tensor(perm[n:2 * n].astype(np.int32)).to("cuda:0")
+    seq = torch.arange(n, dtype=torch.int32, device="cuda:0")
+    nbytes = n * 2 * hkv * 16 * d * 2
+    res = {"workload": "1024 random blocks of a 16384-block pool, 8 KV heads, d=128, bf16",
+           "bytes_per_call": nbytes}
+    for name, fn, moved in (("device_to_device", lambda: kvb.copy_blocks(dev, dev, src, dst), 2 * nbytes),
+                            ("device_to_host", lambda: kvb.copy_blocks(dev, host, src, seq), nbytes),
+                            ("host_to_device", lambda: kvb.copy_blocks(host, dev, seq, dst), nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(args.steps, 10)):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / max(args.steps, 10)
+        res[name] = {"ms": ms, "gbps": moved / (ms * 1e-3) / 1e9}
+    res["device_to_device"]["frac_hbm_peak"] = res["device_to_device"]["gbps"] / PEAK_GBPS
+    return res
 
 
 def bench_decode(torch, kvb, args):

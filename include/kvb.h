@@ -151,6 +151,20 @@ size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_hea
                                                int32_t max_context_len, int32_t shared_len,
                                                int32_t split_blocks);
 
+/* Block copies between pools (kvboost 0.6.0, "CPU paged attention": shared prefixes share
+ * physical blocks copy-on-write, so a sequence about to write into a shared block first
+ * copies it; kvstream 0.1.0, "Why KVStream?": low-priority sequences are swapped to a CPU
+ * page pool).  For i < n: block dst_ids[i] of dst (K and V, every head) becomes a copy of
+ * block src_ids[i] of src, bit-exact.  src and dst may be the same pool, or one of them a
+ * pool in pinned host memory that the device can address (swap out / in).  Both pools need
+ * the same num_kv_heads, head_dim and dtype; block_stride may differ.  Pool memory the
+ * device cannot address (pageable host memory) gives KVB_ERR_INVALID; pinned host memory
+ * is used through its device-mapped address.  Pairs with an id outside its pool are skipped.  Destination blocks must be distinct and, within one pool,
+ * not also sources of the same call (copies run concurrently).
+ * src_ids, dst_ids: (device) int32 [n]. */
+kvb_status kvb_copy_blocks(const kvb_pool* src, const kvb_pool* dst, const int32_t* src_ids,
+                           const int32_t* dst_ids, int32_t n, void* stream);
+
 /* Test helper: gather through the block tables into a contiguous layout, bit-exact.
  * For b < batch, j < seq_lens[b]:
  *   k_out[cu_seq_lens[b] + j][h][:] = pool.k[block_tables[b*stride + j/16]][h][j%16][:]

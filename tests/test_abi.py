@@ -158,6 +158,20 @@ def test_cascade_decode_validation_and_workspace(lib):
     assert lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 4000, 1000, 0) == 0
 
 
+def test_copy_blocks_validation(lib):
+    p = pool()
+    c = lambda a, b, **kw: lib.kvb_copy_blocks(ctypes.byref(a), ctypes.byref(b), kw.get("s", FAKE),
+                                               kw.get("d", FAKE), kw.get("n", 4), None)
+    assert lib.kvb_copy_blocks(None, ctypes.byref(p), FAKE, FAKE, 4, None) == NULL
+    assert c(p, pool(head_dim=64)) == INVALID          # shapes must match
+    assert c(p, pool(num_kv_heads=4)) == INVALID
+    assert c(p, pool(dtype=_lib.KVB_FP16)) == INVALID
+    assert c(p, p, n=-1) == INVALID
+    assert c(p, p, n=0) == OK
+    assert c(p, p, s=None) == NULL
+    assert c(p, p, d=FAKE + 2) == INVALID
+
+
 def test_prefill_workspace_is_zero(lib):
     assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 0
 
