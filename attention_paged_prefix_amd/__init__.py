@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool  # noqa: F401
 
 __all__ = [
-    "Pool", "write_kv", "paged_prefill", "paged_decode", "paged_decode_cascade", "copy_blocks",
+    "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_cascade", "copy_blocks",
     "gather_kv",
     "paged_prefill_workspace_size", "paged_decode_workspace_size",
     "paged_decode_cascade_workspace_size", "version", "KvbError",
@@ -143,6 +143,25 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
         _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch, hq, T,
         int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def paged_prefill_pooled(pool: Pool, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                         prefix_lens: torch.Tensor, block_tables: torch.Tensor, scale: float,
+                         max_q_len: int, max_prefix_len: int, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """kvb_paged_prefill_pooled: as ``paged_prefill``, with the chunk's own K/V read from
+    the pool (written there by ``write_kv`` first) through ``block_tables``."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    batch = int(prefix_lens.numel())
+    T, hq, d = q.shape
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_prefill_pooled", lib.kvb_paged_prefill_pooled(
+        ctypes.byref(ps), _ptr(q), _ptr(out), _ptr(cu_q_lens), _ptr(prefix_lens),
+        _ptr(block_tables), int(block_tables.shape[1]), batch, hq, T, int(max_q_len),
+        int(max_prefix_len), float(scale), _stream(stream)))
     return out
 
 

@@ -95,6 +95,34 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
                                            (hipStream_t)stream));
 }
 
+kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                    int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                    void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_prefix_len < 0 || num_q_heads <= 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0 || total_q == 0) return KVB_OK;
+  if (!q || !out || !cu_q_lens || !prefix_lens || !block_tables) return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)cu_q_lens & 3u) ||
+      ((uintptr_t)prefix_lens & 3u) || ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (max_q_len > total_q) return KVB_ERR_INVALID;
+  // each row must reach prefix_lens[b] + C_b tokens (not checkable on the host; keys past
+  // block_table_stride * 16 are never read)
+  if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
+  if (max_q_len == 0) return KVB_OK;
+  return launch_status(kvb::launch_prefill_pooled(*pool, q, out, cu_q_lens, prefix_lens,
+                                                  block_tables, block_table_stride, batch,
+                                                  num_q_heads, total_q, max_q_len, scale,
+                                                  (hipStream_t)stream));
+}
+
 size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                        int32_t head_dim, int32_t max_context_len,
                                        int32_t split_blocks) {

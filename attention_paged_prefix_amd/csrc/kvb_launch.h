@@ -60,6 +60,9 @@ inline int64_t cascade_ws_bytes(int batch, int hq, int d, int slots) {
   return ((int64_t)batch * hq * slots * d + (int64_t)batch * hq * slots * 2) * 4;
 }
 
+hipError_t launch_prefill_pooled(const kvb_pool& p, const void* q, void* out, const int32_t* cu,
+                                 const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
+                                 int hq, int total_q, int max_q_len, float scale, hipStream_t s);
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,

@@ -100,7 +100,12 @@ struct PfCascade {
 // row max and scales its scores.  K is therefore staged one tile ahead of V: LDS holds
 // two K buffers and two V buffers per key part; step j loads K of tile j+2 and V of tile
 // j+1, and one barrier per step publishes them.
-template <typename T, int D, int KS, bool CAS>
+// MODE: kModePrefill (prefix from the pool, the chunk's own K/V from k_new/v_new),
+// kModeCascade (the shared-prefix form above), kModePooled (every key, the chunk's own
+// included, read from the pool through the block table after kvb_write_kv).
+constexpr int kModePrefill = 0, kModeCascade = 1, kModePooled = 2;
+
+template <typename T, int D, int KS, int MODE>
 __global__ void __launch_bounds__(256 * KS, 2 / KS)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -125,11 +130,12 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
   // logical id -> (kvh, b, key split, tile), tile fastest and KV head slowest
-  constexpr bool cascade = CAS;
+  constexpr bool cascade = MODE == kModeCascade;
+  constexpr bool pooled = MODE == kModePooled;
   int r = lid;
   const int tile = r % max_tiles; r /= max_tiles;
-  const int ks = CAS ? r % cas.nks : 0;
-  if (CAS) r /= cas.nks;
+  const int ks = cascade ? r % cas.nks : 0;
+  if (cascade) r /= cas.nks;
   const int b = r % batch;
   const int kvh = r / batch;
   const int G = hq / hkv;
@@ -168,8 +174,15 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // wg_lim is the smallest such limit over the work-group's rows; keys at or past the
   // largest one are not even loaded (they read as zero), so every key row that reaches
   // the PV product holds a real token of some sequence of this work-group.
+  // pooled: the chunk's keys follow the prefix in the pool; chunk row i sees keys up to
+  // P0 + i, and keys past the work-group's last row are not loaded.
   int row_lim = 0x7fffffff, wg_lim = 0x7fffffff, P = P0;
-  if constexpr (CAS) {
+  if constexpr (pooled) {
+    row_lim = rvalid ? P0 + i_row + 1 : 0;
+    wg_lim = P0 + i_first + 1;
+    P = min(P0 + last_row / G + 1, bt_stride * kBlock);
+  }
+  if constexpr (cascade) {
     const int cap = min(P0, cas.max_ctx);
     row_lim = rvalid ? min(cap, max(0, cas.ctx[i_row])) : 0;
     int mn = 0x7fffffff, mx = 0;
@@ -190,7 +203,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // (none in the cascade form, where this work-group covers one split of the prefix)
   const int t_begin = cascade ? ks * cas.ks_tiles : 0;
   const int n_pre = cascade ? min((P + kKT - 1) / kKT, t_begin + cas.ks_tiles) : (P + kKT - 1) / kKT;
-  const int self_n = cascade ? 0 : last_row / G + 1;   // chunk keys needed by this work-group
+  const int self_n = (cascade || pooled) ? 0 : last_row / G + 1;   // chunk keys needed here
   const int n_self = (self_n + kKT - 1) / kKT;
   const int total = n_pre + n_self;
   const int nstage = max(1, (total - t_begin + KS - 1) / KS);
@@ -614,7 +627,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   emit([&](int db, int rr) { return o[db][rr] * a0 + my[(db * 16 + rr) * 64 + lane] * a1; }, M, lt);
 }
 
-template <typename T, int D, bool CAS>
+template <typename T, int D, int MODE>
 static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void* kn, const void* vn,
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
@@ -632,13 +645,13 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   // split inside each work-group instead, so every SIMD still runs two waves.
   const bool split = real < 2LL * device_cu_count();
   if (split)
-    hipLaunchKernelGGL((prefill_kernel<T, D, 2, CAS>), dim3((unsigned)padded), dim3(512), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 2, MODE>), dim3((unsigned)padded), dim3(512), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
                        (int)padded, (int)real, cas);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, 1, CAS>), dim3((unsigned)padded), dim3(256), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
@@ -663,8 +676,19 @@ hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, cons
   (void)max_prefix_len;
   const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
   return dispatch_prefill(p, [&](auto t, auto d) {
-    return launch_prefill_t<decltype(t), decltype(d)::value, false>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
+    return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
                                                              batch, hq, total_q, max_q_len, scale, none, s);
+  });
+}
+
+hipError_t launch_prefill_pooled(const kvb_pool& p, const void* q, void* out, const int32_t* cu,
+                                 const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
+                                 int hq, int total_q, int max_q_len, float scale, hipStream_t s) {
+  const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
+  return dispatch_prefill(p, [&](auto t, auto d) {
+    return launch_prefill_t<decltype(t), decltype(d)::value, kModePooled>(
+        p, q, nullptr, nullptr, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale,
+        none, s);
   });
 }
 
@@ -690,7 +714,7 @@ hipError_t launch_cascade_shared(const kvb_pool& p, const void* q, const int32_t
   const PfCascade cas{ctx, max_ctx, shared_len, ks_tiles, nks, ws_o, ws_ml, ws_slots};
   const int nsb = (shared_len + kBlock - 1) / kBlock;
   return dispatch_prefill(p, [&](auto t, auto d) {
-    return launch_prefill_t<decltype(t), decltype(d)::value, true>(p, q, nullptr, nullptr, nullptr, nullptr,
+    return launch_prefill_t<decltype(t), decltype(d)::value, kModeCascade>(p, q, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, shared_blocks, nsb, 1, hq, batch,
                                                              batch, scale, cas, s);
   });

@@ -102,6 +102,22 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
                              int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
                              float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged prefill with every key read from the pool: the same result as kvb_paged_prefill,
+ * but the chunk's own K/V is read back through the block table (positions
+ * prefix_lens[b] .. prefix_lens[b] + C_b - 1 of sequence b), after kvb_write_kv has put it
+ * there, so cached and new keys take one path (kvboost 0.6.0, "How it works" steps 3 and
+ * 5: the chunk attends to the cached prefix and to itself in one pass).
+ * block_tables: (device) int32 [batch][block_table_stride]; row b must cover
+ * prefix_lens[b] + C_b tokens (keys past block_table_stride*16 are never read), and
+ * block_table_stride >= ceil(max_prefix_len/16).  Other arguments as kvb_paged_prefill;
+ * no workspace. */
+kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                    int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                    void* stream);
+
 /* Paged decode: one query per sequence over its whole context, which is already in the
  * pool (kvstream 0.1.0, "Request lifecycle" step 2; kvboost 0.6.0, "CPU paged attention":
  * only the decode loop changes).  The query of sequence b sits at position

@@ -172,6 +172,23 @@ def test_copy_blocks_validation(lib):
     assert c(p, p, d=FAKE + 2) == INVALID
 
 
+def test_prefill_pooled_validation(lib):
+    p = pool()
+    def pp(**kw):
+        a = dict(q=FAKE, out=FAKE, cu=FAKE, pl=FAKE, bt=FAKE, stride=200, batch=4, hq=8, T=512,
+                 maxq=200, maxp=3000, scale=0.1)
+        a.update(kw)
+        return lib.kvb_paged_prefill_pooled(ctypes.byref(p), a["q"], a["out"], a["cu"], a["pl"],
+                                            a["bt"], a["stride"], a["batch"], a["hq"], a["T"],
+                                            a["maxq"], a["maxp"], a["scale"], None)
+    assert pp(stride=187) == INVALID                  # ceil(3000 / 16) = 188 entries at least
+    assert pp(q=None) == NULL
+    assert pp(out=FAKE + 8) == INVALID
+    assert pp(hq=5) == INVALID
+    assert pp(maxq=600) == INVALID                    # longer than total_q
+    assert pp(batch=0) == OK
+
+
 def test_prefill_workspace_is_zero(lib):
     assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 0
 

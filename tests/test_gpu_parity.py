@@ -127,6 +127,26 @@ def test_prefill_large_grid_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+@pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:1],
+                         ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
+def test_prefill_pooled_matches_oracle(case):
+    """Every key through the pool: the chunk's K/V is written with write_kv first (slots
+    past the chunk stay NaN-poisoned and must not be read)."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
+    dev = u.Dev(w)
+    kvb.write_kv(dev.pool, dev.k_new, dev.v_new, dev.slots)
+    got = u.to_bits(kvb.paged_prefill_pooled(dev.pool, dev.q, dev.cu, dev.pl, dev.bt, w.scale,
+                                             int(w.q_lens.max()), int(w.prefix_lens.max())))
+    torch.cuda.synchronize()
+    assert np.isfinite(oracle.decode_bits(got, dt)).all()
+    err = u.max_err(got, u.oracle_prefill(w), dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
 def test_prefill_tiny_config_and_row0_bit_exact():
     u = _util()
     w = make_config("tiny", poison=True)
