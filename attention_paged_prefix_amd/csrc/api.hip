@@ -162,11 +162,25 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
                                           sb, ns, scale, workspace, (hipStream_t)stream));
 }
 
-// private-pass split plan and shared-pass key split plan of a cascade decode
-static void cascade_plans(int batch, int hkv, int hq, int max_ctx, int shared_len, int split_blocks,
-                          int* sb, int* ns, int* nks, int* ks_tiles) {
-  kvb::decode_plan(batch, hkv, hq, max_ctx > shared_len ? max_ctx - shared_len : 0, split_blocks, sb, ns);
-  kvb::cascade_plan(batch, hkv, hq, shared_len < max_ctx ? shared_len : max_ctx, nks, ks_tiles);
+// Plan of a cascade decode: the private splits, and the shared prefix either in group
+// work-groups of the same launch (grouped) or in a separate pass of the prefill kernel
+// (nks key splits of ks_tiles tiles; for the grouped form, nks splits of ks_tiles blocks).
+struct CascadePlan {
+  bool grouped;
+  int sb, ns, nks, ks_tiles;
+};
+static CascadePlan cascade_plans(int batch, int hkv, int hq, int max_ctx, int shared_len,
+                                 int split_blocks) {
+  CascadePlan c{};
+  kvb::decode_plan(batch, hkv, hq, max_ctx > shared_len ? max_ctx - shared_len : 0, split_blocks,
+                   &c.sb, &c.ns);
+  const int shared_eff = shared_len < max_ctx ? shared_len : max_ctx;
+  c.grouped = kvb::cascade_use_grouped(batch, hkv, hq, shared_eff);
+  if (c.grouped)
+    kvb::decode_group_plan(shared_eff, c.sb, &c.ks_tiles, &c.nks);
+  else
+    kvb::cascade_plan(batch, hkv, hq, shared_eff, &c.nks, &c.ks_tiles);
+  return c;
 }
 
 size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_heads,
@@ -176,10 +190,9 @@ size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_hea
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
       max_context_len <= 0 || split_blocks < 0 || shared_len < 0 || shared_len % 16)
     return 0;
-  int sb = 0, ns = 0, nks = 0, kt = 0;
-  cascade_plans(batch, num_kv_heads, num_q_heads, max_context_len, shared_len, split_blocks, &sb,
-                &ns, &nks, &kt);
-  return (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, head_dim, nks + ns);
+  const CascadePlan c = cascade_plans(batch, num_kv_heads, num_q_heads, max_context_len,
+                                      shared_len, split_blocks);
+  return (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, head_dim, c.nks + c.ns);
 }
 
 kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* out,
@@ -203,16 +216,22 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
     return KVB_ERR_INVALID;
   if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
     return KVB_ERR_INVALID;
-  int sb = 0, ns = 0, nks = 0, kt = 0;
-  cascade_plans(batch, pool->num_kv_heads, num_q_heads, max_context_len, shared_len, split_blocks,
-                &sb, &ns, &nks, &kt);
-  const size_t need = (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, pool->head_dim, nks + ns);
+  const CascadePlan c = cascade_plans(batch, pool->num_kv_heads, num_q_heads, max_context_len,
+                                      shared_len, split_blocks);
+  const size_t need = (size_t)kvb::cascade_ws_bytes(batch, num_q_heads, pool->head_dim, c.nks + c.ns);
   if (!workspace || workspace_bytes < need) return KVB_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVB_ERR_INVALID;
+  if (c.grouped)
+    return launch_status(kvb::launch_decode_grouped(*pool, q, out, context_lens, block_tables,
+                                                    block_table_stride, shared_blocks, shared_len,
+                                                    batch, num_q_heads, max_context_len, c.sb, c.ns,
+                                                    c.ks_tiles, c.nks, scale, workspace,
+                                                    (hipStream_t)stream));
   return launch_status(kvb::launch_decode_cascade(*pool, q, out, context_lens, block_tables,
                                                   block_table_stride, shared_blocks, shared_len,
-                                                  batch, num_q_heads, max_context_len, sb, ns,
-                                                  nks, kt, scale, workspace, (hipStream_t)stream));
+                                                  batch, num_q_heads, max_context_len, c.sb, c.ns,
+                                                  c.nks, c.ks_tiles, scale, workspace,
+                                                  (hipStream_t)stream));
 }
 
 // Address the device uses for p: itself for device memory, the mapped address for pinned

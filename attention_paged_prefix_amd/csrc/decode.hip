@@ -41,9 +41,25 @@ template <int D> struct DecStep {
   uint4 k[2][VCH];
   uint4 v[2][VCH];
   int rows[2];                              // valid key rows of each block (0..16)
+  int pos[2];                               // position of each block's first key
 };
 
-template <typename T, int D>
+// Shared-prefix part of a grouped cascade decode (ignored by the plain form).  A group
+// work-group fills its 16 query columns with `cols` heads of each of `seqs` sequences,
+// so every shared block it reads serves all of them.
+struct DecGroup {
+  const int32_t* blocks;    // physical ids of the shared prefix blocks
+  int n_blocks;             // shared prefix length / 16
+  int split_blocks;         // shared blocks per group work-group
+  int nsplit;               // key splits of the shared prefix: partial slots 0..nsplit-1
+  int ngroups;              // sequence groups per (KV head, head chunk)
+  int seqs;                 // sequences per group
+  int cols;                 // heads per sequence in a group: min(G, 16)
+  int per_kvh;              // group work-groups per KV head
+  int batch;
+};
+
+template <typename T, int D, bool GROUP>
 __global__ void __launch_bounds__(kDecThreads, 2)
 decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                     int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -51,7 +67,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
                     const int32_t* __restrict__ bt, int bt_stride, int hq, int hkv, int nchunks,
                     int split_blocks, int nsplit, int max_ctx, float c_log2,
                     float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real,
-                    int blk_first, int slot0, int ws_slots, int force_partial) {
+                    int blk_first, int slot0, int ws_slots, int force_partial, DecGroup grp) {
   constexpr int NKK = D / 32;
   constexpr int NDB = D / 16;               // 16-row d blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -69,50 +85,104 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
 
   const int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
-  // logical id -> (kvh, b, split, chunk), chunk fastest and KV head slowest: each XCD
-  // works on few KV heads, so prefix blocks shared by many sequences stay in its L2
-  const int batch = real / (nchunks * nsplit * hkv);
-  int r = lid;
-  const int chunk = r % nchunks; r /= nchunks;
-  const int split = r % nsplit; r /= nsplit;
-  const int b = r % batch;
-  const int kvh = r / batch;
   const int G = hq / hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = uniform(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  // logical id -> (kvh, b, split, chunk), chunk fastest and KV head slowest: each XCD
+  // works on few KV heads, so prefix blocks shared by many sequences stay in its L2.
+  // The grouped form puts each KV head's group work-groups (chunk, sequence group,
+  // shared key split) ahead of its private ones.
+  int kvh, b = 0, split = 0, chunk, gi = 0, ks = 0;
+  bool group_wg = false;
+  if constexpr (GROUP) {
+    const int stride = grp.per_kvh + grp.batch * nsplit * nchunks;
+    kvh = lid / stride;
+    int r = lid - kvh * stride;
+    if (r < grp.per_kvh) {
+      group_wg = true;
+      ks = r % grp.nsplit; r /= grp.nsplit;
+      gi = r % grp.ngroups;
+      chunk = r / grp.ngroups;
+    } else {
+      r -= grp.per_kvh;
+      chunk = r % nchunks; r /= nchunks;
+      split = r % nsplit;
+      b = r / nsplit;
+    }
+  } else {
+    const int batch = real / (nchunks * nsplit * hkv);
+    int r = lid;
+    chunk = r % nchunks; r /= nchunks;
+    split = r % nsplit; r /= nsplit;
+    b = r % batch;
+    kvh = r / batch;
+  }
   const int h0 = kvh * G + chunk * kDecHeads;
   const int nh = min(kDecHeads, G - chunk * kDecHeads);
+  // Query row of column h, or -1: head h0 + h of sequence b, or in a group work-group
+  // head chunk * cols + h % cols of sequence gi * seqs + h / cols.
+  auto row_of = [&](int h) -> int {
+    if (GROUP && group_wg) {
+      const int seq = gi * grp.seqs + h / grp.cols;
+      const int hl = chunk * grp.cols + h % grp.cols;
+      return (h < grp.seqs * grp.cols && seq < grp.batch && hl < G) ? seq * hq + kvh * G + hl : -1;
+    }
+    return h < nh ? b * hq + h0 + h : -1;
+  };
+  const int ctx_cap = min(max_ctx, bt_stride * kBlock);
 
-  int n = ctx_lens[b];
-  n = min(n, min(max_ctx, bt_stride * kBlock));
-  const int tid = threadIdx.x;
-  if (n <= 0) {
-    if (split == 0 && !force_partial)
-      for (int e = tid; e < nh * D; e += kDecThreads)
-        out[((int64_t)b * hq + h0 + e / D) * D + (e % D)] = 0;
-    return;
+  int n, lim;                   // key bound of the loads; key bound of this lane's column
+  int blk_begin, blk_end;
+  bool single = false;
+  const int32_t* tbl;           // block ids from blk_begin on
+  if (GROUP && group_wg) {
+    // every column's keys in the shared range: min(context, shared length)
+    const int row = row_of(c16);
+    const int shared_len = grp.n_blocks * kBlock;
+    lim = row >= 0 ? min(min(ctx_lens[row / hq], ctx_cap), shared_len) : 0;
+    n = lim;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) n = max(n, __shfl_xor(n, m, 64));
+    n = uniform(n);
+    blk_begin = ks * grp.split_blocks;
+    blk_end = min((n + kBlock - 1) / kBlock, blk_begin + grp.split_blocks);
+    tbl = grp.blocks + blk_begin;
+  } else {
+    n = min(ctx_lens[b], ctx_cap);
+    if (n <= 0) {
+      if (split == 0 && !force_partial)
+        for (int e = tid; e < nh * D; e += kDecThreads)
+          out[((int64_t)b * hq + h0 + e / D) * D + (e % D)] = 0;
+      return;
+    }
+    lim = n;
+    // keys of this pass: blocks [blk_first, nblk) (blk_first > 0 after a shared prefix)
+    const int nblk = (n + kBlock - 1) / kBlock;
+    blk_begin = blk_first + split * split_blocks;
+    if (blk_begin >= nblk) return;
+    blk_end = min(nblk, blk_begin + split_blocks);
+    single = !force_partial && nblk <= split_blocks;
+    tbl = bt + (int64_t)b * bt_stride + blk_begin;
   }
-  // keys of this pass: blocks [blk_first, nblk) (blk_first > 0 after a shared prefix)
-  const int nblk = (n + kBlock - 1) / kBlock;
-  const int blk_begin = blk_first + split * split_blocks;
-  if (blk_begin >= nblk) return;
-  const int blk_end = min(nblk, blk_begin + split_blocks);
-  const bool single = !force_partial && nblk <= split_blocks;
-
+  // a group work-group whose columns all end before its key split still writes its
+  // (empty) partials: the merge reads every shared slot of a row
   for (int i = tid; i < blk_end - blk_begin; i += kDecThreads) {
-    const int pb = bt[(int64_t)b * bt_stride + blk_begin + i];
+    const int pb = tbl[i];
     s_bt[i] = (pb >= 0 && pb < num_blocks) ? pb : -1;
   }
 
-  const int lane = tid & 63, w = uniform(tid >> 6);
-  const int c16 = lane & 15, g4 = lane >> 4;
-
-  // queries as the B operand: column c16 (head h0 + c16), d chunk 4*kk + g4
+  // queries as the B operand: column c16 (row row_of(c16)), d chunk 4*kk + g4
   s16x8 qb[NKK];
+  {
+    const int qrow = row_of(c16);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (c16 < nh)
-      qb[kk] = *reinterpret_cast<const s16x8*>(q + ((int64_t)b * hq + h0 + c16) * D + 8 * (4 * kk + g4));
-    else
-      qb[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (qrow >= 0)
+        qb[kk] = *reinterpret_cast<const s16x8*>(q + (int64_t)qrow * D + 8 * (4 * kk + g4));
+      else
+        qb[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
 
   f32x4 o[NDB];
@@ -124,6 +194,12 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   const int64_t head_off = (int64_t)kvh * kBlock * D;
   uint16_t* slot = sV + w * SLOT;           // V rows 0..31
   uint16_t* kslot = slot + 32 * VROW;       // K rows 0..31
+  // Store positions in the slot: when a row is a whole number of 16-byte chunks that
+  // divides 64 (d = 64, 128), chunk j of every lane lands a constant number of rows
+  // below chunk 0, so one base per K and V serves every store.
+  constexpr bool kWholeRows = 64 % CPR == 0;
+  const int v_st = (lane / CPR) * VROW + (lane % CPR) * 8;
+  const int k_st = (lane / CPR) * KROW + (lane % CPR) * 8;
 
   // Both blocks of a step through buffer resources sized to their valid rows: rows past
   // the context, blocks past the split and blocks outside the pool read as zero and
@@ -135,6 +211,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       const int pb = uniform(blk < blk_end ? s_bt[blk - blk_begin] : -1);
       const int rows = pb >= 0 ? min(kBlock, n - blk * kBlock) : 0;
       R.rows[hb] = rows;
+      R.pos[hb] = blk * kBlock;
       const int64_t off = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + off, (uint32_t)(rows * D * 2));
@@ -146,17 +223,25 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     }
   };
 
-  auto step = [&](int blk0, const DecStep<D>& R) {
+  auto step = [&](const DecStep<D>& R) {
     // V of both blocks into this wave's LDS slot, natural [key][d] layout (rows past
     // the context arrive as zeros, so NaN left in unused pool slots never reaches PV)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int j = 0; j < VCH; ++j) {
-        const int c = j * 64 + lane;
-        const int row = c / CPR, col = c - (c / CPR) * CPR;
-        *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 8) = R.v[hb][j];
-        *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 8) = R.k[hb][j];
+        int vo, ko;
+        if constexpr (kWholeRows) {
+          vo = v_st + (hb * 16 + j * (64 / CPR)) * VROW;
+          ko = k_st + (hb * 16 + j * (64 / CPR)) * KROW;
+        } else {
+          const int c = j * 64 + lane;
+          const int row = c / CPR, col = c - (c / CPR) * CPR;
+          vo = (hb * 16 + row) * VROW + col * 8;
+          ko = (hb * 16 + row) * KROW + col * 8;
+        }
+        *reinterpret_cast<uint4*>(slot + vo) = R.v[hb][j];
+        *reinterpret_cast<uint4*>(kslot + ko) = R.k[hb][j];
       }
     __builtin_amdgcn_wave_barrier();
     // S^T = K Q^T per block: A operand = key row c16, d chunk 4*kk + g4
@@ -177,14 +262,14 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const bool ok = 4 * g4 + rr < R.rows[hb];
+        bool ok = 4 * g4 + rr < R.rows[hb];
+        if constexpr (GROUP) ok = ok && R.pos[hb] + 4 * g4 + rr < lim;
         const float tv = ok ? s[hb][rr] * c_log2 : -INFINITY;
         t[hb * 4 + rr] = tv;
         mx = fmaxf(mx, tv);
       }
     }
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
+    mx = halves_max(fmaxf(mx, xor16(mx)));
     if (__any(mx > m_run + kRescaleThreshold)) {
       keep_branch();
       const float mn = fmaxf(m_run, mx);
@@ -219,10 +304,10 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     __builtin_amdgcn_wave_barrier();
   };
 
-  // each wave takes every fourth pair of blocks; the next pair's loads are in flight
-  // while the current pair is used (past the end they are zero-size, i.e. free)
-  // Two named buffers in ping-pong so no register copy forces a wait on the loads
-  // that are still in flight.
+  // Each wave takes every fourth pair of blocks; the next pair's loads are in flight
+  // while the current pair is used (past the end they are zero-size, i.e. free), in two
+  // named buffers in ping-pong so that no register copy forces a wait on loads that are
+  // still in flight.
   const int nsteps = (blk_end - blk_begin - 2 * w + 2 * kDecWaves - 1) / (2 * kDecWaves);
   if (nsteps > 0) {
     constexpr int kStride = 2 * kDecWaves;
@@ -231,20 +316,20 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     load(blk0, A);
     for (int it = 0; it < nsteps; it += 2) {
       load(blk0 + kStride, B);
-      step(blk0, A);
+      step(A);
       if (it + 1 >= nsteps) break;
       load(blk0 + 2 * kStride, A);
-      step(blk0 + kStride, B);
+      step(B);
       blk0 += 2 * kStride;
     }
   }
 
   // row sums over the four key groups of the wave
   float lsum = l_run;
-  lsum += xor_lane(lsum, 16);
-  lsum += xor_lane(lsum, 32);
+  lsum = halves_sum(lsum + xor16(lsum));
   __syncthreads();                          // V slots are reused as the merge buffer
-  if (c16 < nh) {
+  const int ncol = (GROUP && group_wg) ? kDecHeads : nh;
+  if (c16 < ncol) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -254,8 +339,11 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   }
   __syncthreads();
 
-  for (int e = tid; e < nh * D; e += kDecThreads) {
+  const int slot_w = (GROUP && group_wg) ? ks : slot0 + split;
+  for (int e = tid; e < ncol * D; e += kDecThreads) {
     const int h = e / D, d = e - h * D;
+    const int qrow = row_of(h);
+    if (qrow < 0) continue;
     float M = s_m[0][h];
 #pragma unroll
     for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
@@ -266,11 +354,11 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       ov = fmaf(sc, s_o[(ww * kDecHeads + h) * D + d], ov);
       L = fmaf(sc, s_l[ww][h], L);
     }
-    const int64_t row = (int64_t)b * hq + h0 + h;
+    const int64_t row = qrow;
     if (single) {
       out[row * D + d] = T::from_f32(ov / L);
     } else {
-      const int64_t slot = row * ws_slots + slot0 + split;
+      const int64_t slot = row * ws_slots + slot_w;
       ws_o[slot * D + d] = ov;
       if (d == 0) {
         ws_ml[slot * 2 + 0] = M;
@@ -280,40 +368,99 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   }
 }
 
-// One work-group of 128 threads per (sequence, query head).  Slots: `n_shared` partials
-// of a shared prefix (cascade form; 0 otherwise), then one per split of blocks
+// One wave per (sequence, query head) row, four rows per work-group.  Slots: `n_shared`
+// partials of a shared prefix (cascade form; 0 otherwise), then one per split of blocks
 // [blk_first, nblk).  Without a shared prefix only sequences spanning more than one
 // split have partials to combine (a single split wrote its row directly).
+// Every slot of the row is loaded without waiting for the context length (eight at a
+// time, all in flight together); slots past the row's count only enter through selects,
+// so whatever they hold never reaches the result.  The merge is one memory round trip.
+constexpr int kMergeRows = 4;
+constexpr int kMergeBatch = 8;
+
 template <typename T, int D>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(64 * kMergeRows)
 decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-                    uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens, int hq,
-                    int split_blocks, int ws_slots, int max_ctx, int bt_stride, int blk_first,
-                    int n_shared, int cascade) {
-  const int row = blockIdx.x;          // b * hq + h
+                    uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens, int rows,
+                    int hq, int split_blocks, int ws_slots, int max_ctx, int bt_stride,
+                    int blk_first, int n_shared, int cascade) {
+  constexpr int NV = (D + 63) / 64;    // d values per lane: d = lane + 64 * i
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kMergeRows + uniform(threadIdx.x >> 6);
+  if (row >= rows) return;
   const int b = row / hq;
   int n = ctx_lens[b];
+  const float* ml = ws_ml + (int64_t)row * ws_slots * 2;
+  const float* po = ws_o + (int64_t)row * ws_slots * D;
+  float2 mine;                         // (max, sum) of slot s0 + lane % 8
+  float v[kMergeBatch][NV];
+  auto load = [&](int s0) {
+    mine = *reinterpret_cast<const float2*>(ml + 2 * min(s0 + (lane & (kMergeBatch - 1)), ws_slots - 1));
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int s = min(s0 + j, ws_slots - 1);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int d = lane + 64 * i;
+        v[j][i] = d < D ? po[(int64_t)s * D + d] : 0.f;
+      }
+    }
+  };
+  load(0);
+  // keeps the first batch of loads ahead of the branches on the context length
+  asm volatile("" :: "v"(mine.x), "v"(mine.y));
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; ++j) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" :: "v"(v[j][i]));
+  }
   n = min(n, min(max_ctx, bt_stride * kBlock));
-  const int d = threadIdx.x;
-  if (d >= D) return;
   if (n <= 0) {
-    if (cascade) out[(int64_t)row * D + d] = 0;
+    if (cascade)
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (lane + 64 * i < D) out[(int64_t)row * D + lane + 64 * i] = 0;
     return;
   }
   const int nblk = (n + kBlock - 1) / kBlock;
   const int ns_priv = nblk > blk_first ? (nblk - blk_first + split_blocks - 1) / split_blocks : 0;
   if (!cascade && ns_priv <= 1) return;
   const int ns = n_shared + ns_priv;
-  const float* ml = ws_ml + (int64_t)row * ws_slots * 2;
-  float M = kNegBig;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float o = 0.f, L = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float sc = fast_exp2(ml[2 * s] - M);
-    o = fmaf(sc, ws_o[((int64_t)row * ws_slots + s) * D + d], o);
-    L = fmaf(sc, ml[2 * s + 1], L);
+  float M = kNegBig, L = 0.f;
+  float o[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) o[i] = 0.f;
+  for (int s0 = 0;;) {
+    float mj[kMergeBatch], lj[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      mj[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.x), j));
+      lj[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.y), j));
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) Mb = s0 + j < ns ? fmaxf(Mb, mj[j]) : Mb;
+    const float a = fast_exp2(M - Mb);
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) o[i] *= a;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool ok = s0 + j < ns;
+      const float sc = ok ? fast_exp2(mj[j] - Mb) : 0.f;
+      L = fmaf(sc, ok ? lj[j] : 0.f, L);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) o[i] = fmaf(sc, ok ? v[j][i] : 0.f, o[i]);
+    }
+    M = Mb;
+    s0 += kMergeBatch;
+    if (s0 >= ns) break;
+    load(s0);
   }
-  out[(int64_t)row * D + d] = T::from_f32(o / L);
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+    if (lane + 64 * i < D) out[(int64_t)row * D + lane + 64 * i] = T::from_f32(o[i] * inv);
 }
 
 int decode_heads_per_wg(int G) { return G < kDecHeads ? G : kDecHeads; }
@@ -325,9 +472,11 @@ void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, 
   const int max_blocks = max_ctx > 0 ? (max_ctx + kBlock - 1) / kBlock : 1;
   int sb = split_blocks_req;
   if (sb <= 0) {
-    // aim for >= 2048 work-groups (8 per CU) without splits shorter than 16 blocks
+    // about six work-groups per CU (three rounds of the two that fit at once) without
+    // splits shorter than 16 blocks
     const long long units = (long long)batch * hkv * nchunks;
-    long long ns = (2048 + units - 1) / units;
+    const long long target = 6LL * device_cu_count();
+    long long ns = (target + units - 1) / units;
     const long long max_ns = (max_blocks + 15) / 16;
     if (ns > max_ns) ns = max_ns;
     if (ns < 1) ns = 1;
@@ -351,14 +500,17 @@ static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, c
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   const float c = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
-                     nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, 0, 0, ns, 0);
+                     nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, 0, 0, ns, 0,
+                     DecGroup{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns <= 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(batch * hq)), dim3(128), 0, s,
-                     ws_o, ws_ml, (uint16_t*)out, ctx, hq, sb, ns, max_ctx, bt_stride, 0, 0, 0);
+  const int rows = batch * hq;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)),
+                     dim3(64 * kMergeRows), 0, s, ws_o, ws_ml, (uint16_t*)out, ctx, rows, hq, sb, ns,
+                     max_ctx, bt_stride, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -377,18 +529,19 @@ static hipError_t launch_decode_private_t(const kvb_pool& p, const void* q, void
   if (real > 0) {
     const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                        nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
-                       nks, slots, 1);
+                       nks, slots, 1, DecGroup{});
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (batch * hq == 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)(batch * hq)), dim3(128), 0, s,
-                     ws_o, ws_ml, (uint16_t*)out, ctx, hq, sb, slots, max_ctx, bt_stride, blk_first,
-                     nks, 1);
+  const int rows = batch * hq;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)),
+                     dim3(64 * kMergeRows), 0, s, ws_o, ws_ml, (uint16_t*)out, ctx, rows, hq, sb,
+                     slots, max_ctx, bt_stride, blk_first, nks, 1);
   return hipGetLastError();
 }
 
@@ -412,6 +565,92 @@ hipError_t launch_decode_cascade(const kvb_pool& p, const void* q, void* out, co
     default:  return bf ? launch_decode_private_t<BF16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s)
                         : launch_decode_private_t<F16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, blk_first, nks, scale, ws_o, ws_ml, s);
   }
+}
+
+// Grouped cascade: one launch of the split kernel holds, per KV head, the group
+// work-groups over the shared prefix (partials to slots 0..sh_ns-1) and the private
+// splits from block shared_len/16 (slots sh_ns..), then the merge over every slot.
+void decode_group_plan(int shared_len, int sb, int* sh_split_blocks, int* sh_nsplit) {
+  const int nsh = (shared_len + kBlock - 1) / kBlock;
+  if (nsh <= 0) { *sh_split_blocks = 0; *sh_nsplit = 0; return; }
+  int ns = (nsh + sb - 1) / sb;
+  int ssb = (nsh + ns - 1) / ns;
+  ssb = (ssb + 7) & ~7;                 // whole steps for the four waves
+  if (ssb > kMaxSplitBlocks) ssb = kMaxSplitBlocks;
+  *sh_split_blocks = ssb;
+  *sh_nsplit = (nsh + ssb - 1) / ssb;
+}
+
+// The grouped form re-reads every shared block once per sequence group (from L2, beside
+// the private work in the same launch); the separate pass reads it once per 128 query
+// rows but costs a launch of its own on the critical path.  Measured on MI355X (d = 128,
+// 32 or 64 query heads, 8 KV heads, 8..256 sequences, shared prefixes of 1K..16K tokens):
+// grouped is ahead up to about 1024 group-block reads per KV head and head chunk, the
+// separate pass beyond 2048.
+bool cascade_use_grouped(int batch, int hkv, int hq, int shared_len) {
+  const int G = hq / hkv;
+  const int cols = G < kDecHeads ? G : kDecHeads;
+  const long long ngroups = (batch + kDecHeads / cols - 1) / (kDecHeads / cols);
+  const long long nsh = (shared_len + kBlock - 1) / kBlock;
+  return ngroups * nsh <= 1024;
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_grouped_t(const kvb_pool& p, const void* q, void* out,
+                                          const int32_t* ctx, const int32_t* bt, int bt_stride,
+                                          const int32_t* shared_blocks, int shared_len, int batch,
+                                          int hq, int max_ctx, int sb, int ns, int sh_sb, int sh_ns,
+                                          float scale, float* ws_o, float* ws_ml, hipStream_t s) {
+  const int G = hq / p.num_kv_heads;
+  const int nchunks = (G + kDecHeads - 1) / kDecHeads;
+  DecGroup g{};
+  g.blocks = shared_blocks;
+  g.n_blocks = (min(shared_len, max_ctx) + kBlock - 1) / kBlock;
+  g.split_blocks = sh_sb;
+  g.nsplit = sh_ns;
+  g.cols = G < kDecHeads ? G : kDecHeads;
+  g.seqs = kDecHeads / g.cols;
+  g.ngroups = (batch + g.seqs - 1) / g.seqs;
+  g.per_kvh = sh_ns > 0 ? nchunks * g.ngroups * sh_ns : 0;
+  g.batch = batch;
+  const int slots = sh_ns + ns;
+  const int blk_first = shared_len / kBlock;
+  const long long real = (long long)p.num_kv_heads * (g.per_kvh + (long long)batch * ns * nchunks);
+  if (real > 0) {
+    const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const float c = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+                       (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
+                       (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
+                       nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
+                       sh_ns, slots, 1, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int rows = batch * hq;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)),
+                     dim3(64 * kMergeRows), 0, s, ws_o, ws_ml, (uint16_t*)out, ctx, rows, hq, sb,
+                     slots, max_ctx, bt_stride, blk_first, sh_ns, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_grouped(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
+                                 const int32_t* bt, int bt_stride, const int32_t* shared_blocks,
+                                 int shared_len, int batch, int hq, int max_ctx, int sb, int ns,
+                                 int sh_sb, int sh_ns, float scale, void* ws, hipStream_t s) {
+  const int slots = sh_ns + ns;
+  float* ws_o = (float*)ws;
+  float* ws_ml = ws_o + (int64_t)batch * hq * slots * p.head_dim;
+  const bool bf = p.dtype == KVB_BF16;
+#define KVB_GROUPED(TT, DD) launch_decode_grouped_t<TT, DD>(p, q, out, ctx, bt, bt_stride, shared_blocks, \
+    shared_len, batch, hq, max_ctx, sb, ns, sh_sb, sh_ns, scale, ws_o, ws_ml, s)
+  switch (p.head_dim) {
+    case 64:  return bf ? KVB_GROUPED(BF16, 64) : KVB_GROUPED(F16, 64);
+    case 96:  return bf ? KVB_GROUPED(BF16, 96) : KVB_GROUPED(F16, 96);
+    default:  return bf ? KVB_GROUPED(BF16, 128) : KVB_GROUPED(F16, 128);
+  }
+#undef KVB_GROUPED
 }
 
 hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,

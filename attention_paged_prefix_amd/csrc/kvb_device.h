@@ -107,6 +107,11 @@ __device__ inline float quad_xor2(float x) {
 }
 
 __device__ inline float xor_lane(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// x of lane l ^ 16: ds_swizzle in bit-mask mode (and 0x1f, or 0, xor 0x10 within each
+// 32-lane group), which needs no lane-address register, unlike a permute.
+__device__ inline float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+}
 
 // Both halves of a wave exchanged (lane l <-> lane l^32) with gfx950's v_permlane32_swap,
 // which swaps lanes 32..63 of its first operand with lanes 0..31 of its second.  With x in

@@ -56,6 +56,16 @@ hipError_t launch_decode_cascade(const kvb_pool& p, const void* q, void* out, co
                                  const int32_t* bt, int bt_stride, const int32_t* shared_blocks,
                                  int shared_len, int batch, int hq, int max_ctx, int sb, int ns,
                                  int nks, int ks_tiles, float scale, void* ws, hipStream_t s);
+// Grouped cascade decode: the shared prefix in group work-groups of the split kernel's
+// launch (16 / min(G, 16) sequences per work-group, `sh_nsplit` key splits of
+// `sh_split_blocks` blocks, partials to slots 0..sh_nsplit-1), the private splits in the
+// same launch, then the merge.  cascade_use_grouped picks it over the separate pass.
+void decode_group_plan(int shared_len, int sb, int* sh_split_blocks, int* sh_nsplit);
+bool cascade_use_grouped(int batch, int hkv, int hq, int shared_len);
+hipError_t launch_decode_grouped(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
+                                 const int32_t* bt, int bt_stride, const int32_t* shared_blocks,
+                                 int shared_len, int batch, int hq, int max_ctx, int sb, int ns,
+                                 int sh_sb, int sh_ns, float scale, void* ws, hipStream_t s);
 inline int64_t cascade_ws_bytes(int batch, int hq, int d, int slots) {
   return ((int64_t)batch * hq * slots * d + (int64_t)batch * hq * slots * 2) * 4;
 }

@@ -247,6 +247,9 @@ CASCADE_CASES = [
     (403, "bf16", 8, 1, 64, [64, 65, 10, 200, 0], 4),               # MQA, a zero context
     (404, "fp16", 16, 16, 128, [800, 1200], 0),                     # no shared prefix
     (405, "bf16", 16, 2, 128, [4096, 4096, 4000, 4090], 256),       # (almost) all shared
+    (406, "bf16", 40, 2, 64, [700, 1600, 33], 48),                  # G=20: two head chunks
+    # 10 sequence groups x 128 shared blocks: the separate shared pass, not the grouped form
+    (407, "bf16", 32, 8, 128, [2048 + 37 * i for i in range(39)] + [1500], 128),
 ]
 
 
