@@ -127,16 +127,21 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
                   cu_q_lens: torch.Tensor, prefix_lens: torch.Tensor, block_tables: torch.Tensor,
                   scale: float, max_q_len: int, max_prefix_len: int,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
+                  stream=None, dispatch_plan: bool = True) -> torch.Tensor:
     """kvb_paged_prefill.  ``q [T][Hq][d]``, ``k_new/v_new [T][Hkv][d]``, ``cu_q_lens`` int32
-    [B+1], ``prefix_lens`` int32 [B], ``block_tables`` int32 [B][stride]."""
+    [B+1], ``prefix_lens`` int32 [B], ``block_tables`` int32 [B][stride].
+    ``dispatch_plan=False`` passes no workspace: work-groups start in table order instead
+    of longest first (same results)."""
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
     batch = int(prefix_lens.numel())
     T, hq, d = q.shape
-    need = paged_prefill_workspace_size(batch, hq, d, T, max_prefix_len)
-    workspace = _workspace(need, q.device, workspace)
+    if dispatch_plan:
+        need = paged_prefill_workspace_size(batch, hq, d, T, max_prefix_len)
+        workspace = _workspace(need, q.device, workspace)
+    else:
+        workspace = None
     ps = pool.c_struct()
     _lib.check("kvb_paged_prefill", lib.kvb_paged_prefill(
         ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(cu_q_lens),

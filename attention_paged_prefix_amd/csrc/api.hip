@@ -61,8 +61,8 @@ kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_n
 
 size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                         int32_t total_q, int32_t max_prefix_len) {
-  (void)batch; (void)num_q_heads; (void)head_dim; (void)total_q; (void)max_prefix_len;
-  return 0;
+  (void)head_dim; (void)max_prefix_len;
+  return (size_t)kvb::prefill_plan_bytes(batch, num_q_heads, total_q);
 }
 
 kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
@@ -85,14 +85,16 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
     return KVB_ERR_INVALID;
   if (max_q_len > total_q) return KVB_ERR_INVALID;
   if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
+  // the workspace is optional (it holds the dispatch plan); one that is passed must be big enough
   const size_t need = kvb_paged_prefill_workspace_size(batch, num_q_heads, pool->head_dim, total_q,
                                                        max_prefix_len);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
+  if (workspace && workspace_bytes < need) return KVB_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return KVB_ERR_INVALID;
   if (max_q_len == 0) return KVB_OK;
   return launch_status(kvb::launch_prefill(*pool, q, k_new, v_new, out, cu_q_lens, prefix_lens,
                                            block_tables, block_table_stride, batch, num_q_heads,
                                            total_q, max_q_len, max_prefix_len, scale,
-                                           (hipStream_t)stream));
+                                           need > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
 kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* out,

@@ -73,9 +73,12 @@ inline int64_t cascade_ws_bytes(int batch, int hq, int d, int slots) {
 hipError_t launch_prefill_pooled(const kvb_pool& p, const void* q, void* out, const int32_t* cu,
                                  const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
                                  int hq, int total_q, int max_q_len, float scale, hipStream_t s);
+// Prefill: `plan_ws` (may be NULL) holds prefill_plan_bytes(...) bytes for the
+// longest-first dispatch plan of a grid of several rounds.
+int64_t prefill_plan_bytes(int batch, int hq, int total_q);
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
-                          float scale, hipStream_t s);
+                          float scale, void* plan_ws, hipStream_t s);
 
 }  // namespace kvb

@@ -113,7 +113,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                uint16_t* __restrict__ out, const int32_t* __restrict__ cu,
                const int32_t* __restrict__ plen, const int32_t* __restrict__ bt, int bt_stride,
                int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
-               int real, PfCascade cas) {
+               int real, const int32_t* __restrict__ order, PfCascade cas) {
   using L = PfLayout<D>;
   constexpr int CPR = L::CPR;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
@@ -127,8 +127,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // [key part][parity][K | V][64 x D]
   __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT];
 
-  const int lid = xcd_logical_id(blockIdx.x, padded);
+  int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
+  // with a dispatch plan, the position in the XCD's range names the work item
+  if (order) lid = order[lid];
   // logical id -> (kvh, b, key split, tile), tile fastest and KV head slowest
   constexpr bool cascade = MODE == kModeCascade;
   constexpr bool pooled = MODE == kModePooled;
@@ -627,12 +629,71 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   emit([&](int db, int rr) { return o[db][rr] * a0 + my[(db * 16 + rr) * 64 + lane] * a1; }, M, lt);
 }
 
+// Longest-first dispatch plan.  The dispatcher starts work-groups in grid order, so on a
+// grid of several rounds the last work-groups to start set the tail.  One work-group per
+// XCD range (the logical ids one XCD runs) computes every item's key count (prefix plus
+// the causal part of its last row; 0 for tiles past the chunk), sorts the range by it,
+// largest first (ties by id, so the plan is deterministic), and writes the item for each
+// position.  Items never leave their XCD range, so each XCD keeps its KV heads in L2.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMax = 4096;          // items per XCD range sorted in LDS
+
+__global__ void __launch_bounds__(kPlanThreads)
+prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ plen, int batch,
+                    int G, int total_q, int bt_stride, int max_tiles, int padded, int real,
+                    int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kPlanMax];
+  const int per = padded / kNumXcd;
+  const int lo = blockIdx.x * per;
+  const int n = min(per, real - lo);
+  if (n <= 0) return;
+  int N = 1;
+  while (N < n) N <<= 1;
+  for (int i = threadIdx.x; i < N; i += kPlanThreads) {
+    uint64_t k = ~0ull;                 // padding sorts last
+    if (i < n) {
+      const int lid = lo + i;
+      const int tile = lid % max_tiles;
+      const int b = (lid / max_tiles) % batch;
+      const int cu_b = min(max(cu[b], 0), total_q);
+      const int C = max(0, min(cu[b + 1], total_q) - cu_b);
+      const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
+      const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * kBM;
+      int64_t cost = v0 < nrows ? P0 + (min(nrows, v0 + kBM) - 1) / G + 1 : 0;
+      cost = min(cost, (int64_t)0x7ffffffe);
+      // ascending order of (largest - cost, id): descending cost, ascending id
+      k = ((uint64_t)(0x7fffffff - cost) << 32) | (uint32_t)lid;
+    }
+    key[i] = k;
+  }
+  __syncthreads();
+  for (int size = 2; size <= N; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < N / 2; i += kPlanThreads) {
+        const int a = 2 * i - (i & (stride - 1));      // pair (a, a + stride), bit `stride` of a clear
+        const uint64_t x = key[a], y = key[a + stride];
+        if ((x > y) == ((a & size) == 0)) { key[a] = y; key[a + stride] = x; }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < n; i += kPlanThreads) order[lo + i] = (int32_t)(uint32_t)key[i];
+}
+
+int64_t prefill_plan_bytes(int batch, int hq, int total_q) {
+  if (batch <= 0 || hq <= 0 || total_q <= 0) return 0;
+  // items: batch * hkv * ceil(max_q * G / kBM) <= batch * (ceil(total_q * hq / kBM) + hq),
+  // and no plan is made beyond kPlanMax items per XCD range
+  int64_t items = (int64_t)batch * (((int64_t)total_q * hq + kBM - 1) / kBM + hq);
+  if (items > (int64_t)kNumXcd * kPlanMax) items = (int64_t)kNumXcd * kPlanMax;
+  return (items * 4 + 255) / 256 * 256;
+}
+
 template <typename T, int D, int MODE>
 static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void* kn, const void* vn,
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
                                    int total_q, int max_q_len, float scale, const PfCascade& cas,
-                                   hipStream_t s) {
+                                   int32_t* plan_ws, hipStream_t s) {
   const int G = hq / p.num_kv_heads;
   const long long rows = (long long)max_q_len * G;
   const int max_tiles = (int)((rows + kBM - 1) / kBM);
@@ -644,18 +705,27 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   // Up to two work-groups per CU fit: with fewer work-groups than 2 x CUs the keys are
   // split inside each work-group instead, so every SIMD still runs two waves.
   const bool split = real < 2LL * device_cu_count();
+  // a plan pays off only on a grid of several rounds
+  const int32_t* order = nullptr;
+  if (MODE == kModePrefill && plan_ws && !split && padded / kNumXcd <= kPlanMax) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(kNumXcd), dim3(kPlanThreads), 0, s, cu, plen,
+                       batch, G, total_q, bt_stride, max_tiles, (int)padded, (int)real, plan_ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    order = plan_ws;
+  }
   if (split)
     hipLaunchKernelGGL((prefill_kernel<T, D, 2, MODE>), dim3((unsigned)padded), dim3(512), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, cas);
+                       (int)padded, (int)real, order, cas);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, cas);
+                       (int)padded, (int)real, order, cas);
   return hipGetLastError();
 }
 
@@ -672,12 +742,13 @@ static hipError_t dispatch_prefill(const kvb_pool& p, F&& f) {
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
-                          float scale, hipStream_t s) {
+                          float scale, void* plan_ws, hipStream_t s) {
   (void)max_prefix_len;
   const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
   return dispatch_prefill(p, [&](auto t, auto d) {
     return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
-                                                             batch, hq, total_q, max_q_len, scale, none, s);
+                                                             batch, hq, total_q, max_q_len, scale, none,
+                                                             (int32_t*)plan_ws, s);
   });
 }
 
@@ -688,7 +759,7 @@ hipError_t launch_prefill_pooled(const kvb_pool& p, const void* q, void* out, co
   return dispatch_prefill(p, [&](auto t, auto d) {
     return launch_prefill_t<decltype(t), decltype(d)::value, kModePooled>(
         p, q, nullptr, nullptr, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale,
-        none, s);
+        none, nullptr, s);
   });
 }
 
@@ -716,7 +787,7 @@ hipError_t launch_cascade_shared(const kvb_pool& p, const void* q, const int32_t
   return dispatch_prefill(p, [&](auto t, auto d) {
     return launch_prefill_t<decltype(t), decltype(d)::value, kModeCascade>(p, q, nullptr, nullptr, nullptr, nullptr,
                                                              nullptr, shared_blocks, nsb, 1, hq, batch,
-                                                             batch, scale, cas, s);
+                                                             batch, scale, cas, nullptr, s);
   });
 }
 

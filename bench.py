@@ -266,12 +266,15 @@ def main(argv=None):
     dws_n = kvb.paged_decode_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim, max_ctx)
     dws = torch.empty(max(dws_n, 16), dtype=torch.uint8, device="cuda:0")
     T = w.total_q
+    pws_n = kvb.paged_prefill_workspace_size(w.batch, w.num_q_heads, w.head_dim, T, max_p)
+    pws = torch.empty(max(pws_n, 16), dtype=torch.uint8, device="cuda:0")
 
     def part(name):
         if name == "write_kv":
             kvb.write_kv(pool, kn, vn, slots)
         elif name == "prefill":
-            kvb.paged_prefill(pool, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out)
+            kvb.paged_prefill(pool, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out,
+                              workspace=pws)
         elif name == "write_kv_dec":
             kvb.write_kv(pool, dk, dv, dslots)
         elif name == "decode":
@@ -325,6 +328,8 @@ def main(argv=None):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             one_step()
+        # the capture leaves the GPU idle: bring the clocks back up before timing
+        settle(torch, graph.replay, args.settle_ms)
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()

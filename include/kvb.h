@@ -93,8 +93,12 @@ kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_n
  * max_prefix_len >= every prefix length (host bounds used for the launch grid; a
  * larger value only costs idle work-groups).  Only pool entries of the prefix are read,
  * so kvb_write_kv of the same chunk may run before or after this call.
- * workspace: (device) at least kvb_paged_prefill_workspace_size(...) bytes (may be NULL
- * when that size is 0). */
+ * workspace: (device, optional) NULL, or at least kvb_paged_prefill_workspace_size(...)
+ * bytes, 16-byte aligned (else KVB_ERR_WORKSPACE / KVB_ERR_INVALID).  With it, a grid
+ * of several rounds of work-groups is started longest first (a small plan kernel sorts
+ * each XCD's work items by key count into the workspace first), which shortens the tail
+ * on ragged batches; the results are the same bits either way.  Its contents on entry
+ * do not matter. */
 kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
                              const void* v_new, void* out, const int32_t* cu_q_lens,
                              const int32_t* prefix_lens, const int32_t* block_tables,

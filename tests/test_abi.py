@@ -189,8 +189,17 @@ def test_prefill_pooled_validation(lib):
     assert pp(batch=0) == OK
 
 
-def test_prefill_workspace_is_zero(lib):
-    assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 0
+def test_prefill_workspace_size_and_validation(lib):
+    # dispatch plan: one int per work item, items <= batch * (ceil(total_q * hq / 128) + hq),
+    # at most 8 x 4096, rounded up to 256 bytes
+    assert lib.kvb_paged_prefill_workspace_size(8, 16, 128, 2048, 2048) == 8 * (256 + 16) * 4
+    assert lib.kvb_paged_prefill_workspace_size(0, 16, 128, 2048, 2048) == 0
+    assert lib.kvb_paged_prefill_workspace_size(64, 64, 128, 1 << 20, 0) == 8 * 4096 * 4
+    assert lib.kvb_paged_prefill_workspace_size(1, 1, 64, 1, 0) == 256
+    p = pool()
+    need = lib.kvb_paged_prefill_workspace_size(2, 4, 128, 10, 64)
+    assert prefill(lib, p, ws=FAKE, wsb=need - 1) == WS     # too small (optional, but checked)
+    assert prefill(lib, p, ws=FAKE + 8, wsb=need) == INVALID
 
 
 def test_gather_validation(lib):

@@ -127,6 +127,34 @@ def test_prefill_large_grid_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+def test_prefill_dispatch_plan_gives_same_bits():
+    """Longest-first dispatch (the plan kernel writes the order into the workspace) and
+    table order (no workspace) give the same bits, and match the oracle, on a ragged grid
+    of several rounds whose work items differ widely in key count.  The workspace starts
+    out filled with garbage: its contents on entry must not matter."""
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    P = [0, 3000, 17, 9000, 450, 6100, 1, 2500]
+    C = [300, 37, 511, 129, 64, 400, 250, 1]
+    hq, hkv = 32, 8
+    groups = len(P) * hkv * ((max(C) * (hq // hkv) + 127) // 128)
+    assert groups >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    w = make_custom(216, "bf16", hq, hkv, 128, P, C, share="pairs", poison=True)
+    dev = u.Dev(w)
+    mq, mp = int(w.q_lens.max()), int(w.prefix_lens.max())
+    need = kvb.paged_prefill_workspace_size(w.batch, hq, 128, w.total_q, mp)
+    assert need > 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda:0")
+    planned = u.to_bits(kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl,
+                                          dev.bt, w.scale, mq, mp, workspace=ws))
+    table = u.to_bits(kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl,
+                                        dev.bt, w.scale, mq, mp, dispatch_plan=False))
+    torch.cuda.synchronize()
+    assert np.array_equal(planned, table)
+    err = u.max_err(planned, u.oracle_prefill(w), "bf16")
+    assert err <= u.TOL["bf16"], f"max abs err {err}"
+
+
 @pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:1],
                          ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
 def test_prefill_pooled_matches_oracle(case):
