@@ -33,7 +33,11 @@ of V; block-permutation invariance; the reuse invariant (prefill over a cached
 prefix equals full causal attention on those rows); decode equals a one-row
 prefill; GQA equals MHA with repeated K/V; causality; the log-sum-exp merge of
 key partitions; block copies leave every sequence's gathered tokens unchanged under
-a remapped table.  The softmax scale 1/sqrt(head_dim) is the conventional reading
+a remapped table.  The 8-bit pool (``oracle.quant``: per-channel K scales, per-token V
+scales) is pinned by hand-derived codes under ``tests/golden`` (round half to even,
+clamping, zero scales), the half-step error bound, and the reduction that decode over a
+pool whose values are exactly what their codes stand for equals the 16-bit decode bit
+for bit.  The softmax scale 1/sqrt(head_dim) is the conventional reading
 (the tiny workload states it; the pages state no other): parity unpinned by the
 pages for that convention beyond the tiny workload.
 """

@@ -1,0 +1,112 @@
+"""8-bit K/V pool: quantisation, dequantisation and decode over the quantised pool.
+
+Test infrastructure only (see the package docstring).  The pages store cached K/V at
+8 bits with per-channel scales for K and per-token scales for V (kvboost 0.6.0,
+"Optional: KV quantization": the KIVI asymmetry, about 2x smaller).  They fix the two
+axes and nothing else; the readings taken here:
+
+* codes are signed integers in [-127, 127] (symmetric, no zero point): a value x with
+  scale s becomes ``rint(x / s)`` clamped to that range, the division and the rounding
+  (half to even) done in IEEE float32, so a GPU that does the same steps in float32
+  produces the same codes; a zero scale gives code 0;
+* K: one scale per (KV head, channel) for the whole pool, given by the caller (for
+  example the per-channel absolute maximum of the prompt's K over its tokens, / 127);
+  stored codes never change when tokens are appended;
+* V: one scale per (token, KV head) = max_c |v_c| / 127 (float32), computed when the
+  token is written;
+* the value a code stands for is ``code * scale``, exact in float64.
+
+Pool arrays: codes int8 ``[num_blocks][num_kv_heads][16][d]``, V scales float32
+``[num_blocks][num_kv_heads][16]``, K scales float32 ``[num_kv_heads][d]``.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+from .attention import BLOCK_SIZE, attend, decode_bits, gather_kv
+
+CODE_MAX = 127
+
+
+def quantize(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """int8 codes of float32 values ``x`` at float32 scales ``s`` (broadcast):
+    ``rint(x / s)`` in float32, clamped to [-127, 127]; 0 where s == 0."""
+    x = np.asarray(x, dtype=np.float32)
+    s = np.broadcast_to(np.asarray(s, dtype=np.float32), x.shape)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(np.divide(x, s, dtype=np.float32))
+    r = np.where(s == 0, np.float32(0), r)
+    return np.clip(r, -CODE_MAX, CODE_MAX).astype(np.int8)
+
+
+def token_scale(v: np.ndarray) -> np.ndarray:
+    """Per-token V scale over the last axis: max |v| / 127 in float32."""
+    a = np.abs(np.asarray(v, dtype=np.float32)).max(axis=-1)
+    return np.divide(a, np.float32(CODE_MAX), dtype=np.float32)
+
+
+def channel_scales(k_tokens: np.ndarray) -> np.ndarray:
+    """A K scale per (KV head, channel) from example tokens ``[n][Hkv][d]`` (float32):
+    max over the tokens of |k| / 127.  One way a caller can pick the pool's K scales."""
+    a = np.abs(np.asarray(k_tokens, dtype=np.float32)).max(axis=0)
+    return np.divide(a, np.float32(CODE_MAX), dtype=np.float32)
+
+
+def write_kv_q8(k_codes: np.ndarray, v_codes: np.ndarray, v_scales: np.ndarray,
+                k_scale: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, slot_mapping: np.ndarray,
+                dtype: str) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Quantise each new token and scatter it into its pool slot; negative slots are
+    skipped (the slot rule of ``write_kv``: block ``slot // 16``, row ``slot % 16``).
+    ``k_new``/``v_new`` are 16-bit payloads ``[T][Hkv][d]``.  Returns new arrays."""
+    kc = np.array(k_codes, copy=True)
+    vc = np.array(v_codes, copy=True)
+    vs = np.array(v_scales, copy=True)
+    kf = decode_bits(k_new, dtype).astype(np.float32)      # exact: 16-bit -> float32
+    vf = decode_bits(v_new, dtype).astype(np.float32)
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:
+            continue
+        blk, row = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
+        kc[blk, :, row, :] = quantize(kf[t], k_scale)
+        s = token_scale(vf[t])                              # [Hkv]
+        vs[blk, :, row] = s
+        vc[blk, :, row, :] = quantize(vf[t], s[:, None])
+    return kc, vc, vs
+
+
+def dequant_k(codes: np.ndarray, k_scale: np.ndarray) -> np.ndarray:
+    """Values of K codes ``[..][Hkv][d]`` at scales ``[Hkv][d]``, float64 (exact)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(k_scale, dtype=np.float64)
+
+
+def dequant_v(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of V codes ``[..][d]`` at per-token scales ``[..]``, float64 (exact)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def paged_decode_q8(k_codes, v_codes, v_scales, k_scale, q, context_lens, block_tables,
+                    scale: float, dtype: str, want_lse: bool = False):
+    """Decode (one query per sequence over its whole context, as ``paged_decode``) over
+    the values the 8-bit pool stands for.  ``q`` holds 16-bit payloads ``[B][Hq][d]``."""
+    B, Hq, d = q.shape
+    Hkv = k_codes.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    lse_all = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(context_lens[b])
+        if n <= 0:
+            continue
+        K = dequant_k(gather_kv(k_codes, block_tables[b], n), k_scale)
+        j = np.arange(n)
+        blocks = np.asarray(block_tables[b], dtype=np.int64)[j // BLOCK_SIZE]
+        Vs = v_scales[blocks, :, j % BLOCK_SIZE]                      # [n][Hkv]
+        V = dequant_v(gather_kv(v_codes, block_tables[b], n), Vs)
+        qb = decode_bits(q[b], dtype)
+        for h in range(Hq):
+            o, lse = attend(qb[h:h + 1], K[:, h // G], V[:, h // G], [n - 1], scale)
+            out[b, h] = o[0]
+            lse_all[b, h] = lse[0]
+    return (out, lse_all) if want_lse else out
