@@ -632,37 +632,51 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 // Longest-first dispatch plan.  The dispatcher starts work-groups in grid order, so on a
 // grid of several rounds the last work-groups to start set the tail.  One work-group per
 // XCD range (the logical ids one XCD runs) computes every item's key count (prefix plus
-// the causal part of its last row; 0 for tiles past the chunk), sorts the range by it,
-// largest first (ties by id, so the plan is deterministic), and writes the item for each
-// position.  Items never leave their XCD range, so each XCD keeps its KV heads in L2.
-constexpr int kPlanThreads = 1024;
+// the causal part of its last row; 0 for tiles past the chunk), sorts the range by it in
+// 32 buckets relative to the range's largest count, largest first, and writes the item
+// for each position.  Within a bucket items keep table order (tiles of one sequence and
+// KV head together, so they share its K/V through L2), and the plan is deterministic.
+// Items never leave their XCD range, so each XCD keeps its KV heads in L2.
+constexpr int kPlanThreads = 256;
 constexpr int kPlanMax = 4096;          // items per XCD range sorted in LDS
+constexpr int kPlanBuckets = 32;
 
 __global__ void __launch_bounds__(kPlanThreads)
 prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ plen, int batch,
                     int G, int total_q, int bt_stride, int max_tiles, int padded, int real,
                     int32_t* __restrict__ order) {
   __shared__ uint64_t key[kPlanMax];
+  __shared__ int s_max;
   const int per = padded / kNumXcd;
   const int lo = blockIdx.x * per;
   const int n = min(per, real - lo);
   if (n <= 0) return;
   int N = 1;
   while (N < n) N <<= 1;
+  if (threadIdx.x == 0) s_max = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += kPlanThreads) {
+    const int lid = lo + i;
+    const int tile = lid % max_tiles;
+    const int b = (lid / max_tiles) % batch;
+    const int cu_b = min(max(cu[b], 0), total_q);
+    const int C = max(0, min(cu[b + 1], total_q) - cu_b);
+    const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
+    const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * kBM;
+    const int64_t cost = v0 < nrows ? min(P0 + (min(nrows, v0 + kBM) - 1) / G + 1, (int64_t)0x3fffffff) : 0;
+    key[i] = (uint64_t)cost;
+    atomicMax(&s_max, (int)cost);
+  }
+  __syncthreads();
+  const int64_t cmax = s_max;
   for (int i = threadIdx.x; i < N; i += kPlanThreads) {
     uint64_t k = ~0ull;                 // padding sorts last
     if (i < n) {
-      const int lid = lo + i;
-      const int tile = lid % max_tiles;
-      const int b = (lid / max_tiles) % batch;
-      const int cu_b = min(max(cu[b], 0), total_q);
-      const int C = max(0, min(cu[b + 1], total_q) - cu_b);
-      const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
-      const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * kBM;
-      int64_t cost = v0 < nrows ? P0 + (min(nrows, v0 + kBM) - 1) / G + 1 : 0;
-      cost = min(cost, (int64_t)0x7ffffffe);
-      // ascending order of (largest - cost, id): descending cost, ascending id
-      k = ((uint64_t)(0x7fffffff - cost) << 32) | (uint32_t)lid;
+      const int64_t cost = (int64_t)key[i];
+      // empty tiles after every bucket; bucket kPlanBuckets - 1 holds the largest counts
+      const int64_t rank = cost > 0 ? kPlanBuckets - 1 - min((int64_t)kPlanBuckets - 1, cost * kPlanBuckets / (cmax + 1))
+                                    : kPlanBuckets;
+      k = ((uint64_t)rank << 32) | (uint32_t)(lo + i);
     }
     key[i] = k;
   }
