@@ -24,6 +24,8 @@
 //    the output rescale is rarely executed.
 //  * A split covering the whole context writes the normalised output directly; other
 //    splits write (output, max, sum) partials that decode_merge combines.
+#include <type_traits>
+
 #include "kvb_device.h"
 #include "kvb_launch.h"
 
@@ -44,6 +46,40 @@ template <int D> struct DecStep {
   int pos[2];                               // position of each block's first key
 };
 
+// The 8-bit pool's step: 16 codes per 16-byte chunk, so a block's K (or V) is D chunks,
+// (D + 63) / 64 per lane; plus the V scales of the lane's four keys of each block.
+template <int D> struct DecStepQ8 {
+  static constexpr int NCH = (D + 63) / 64;
+  uint4 k[2][NCH];
+  uint4 v[2][NCH];
+  f32x4 vs[2];
+  int rows[2];
+  int pos[2];
+};
+
+// Scales of the 8-bit pool (ignored by the 16-bit forms): the per-channel K scales
+// [Hkv][D] and the per-token V scales [block][Hkv][16].
+struct DecQ8 {
+  const float* k_scale;
+  const float* v_scale;
+};
+
+// 16 int8 codes -> 16 values of T in two 16-byte halves (exact: |code| <= 127 fits the
+// 8-bit significand of bf16 and the 11-bit one of fp16).
+template <typename T>
+__device__ inline void codes_to(uint4 c, uint4& lo, uint4& hi) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t x = (int32_t)w[i];
+    o[2 * i] = pack2<T>((float)((x << 24) >> 24), (float)((x << 16) >> 24));
+    o[2 * i + 1] = pack2<T>((float)((x << 8) >> 24), (float)(x >> 24));
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 // Shared-prefix part of a grouped cascade decode (ignored by the plain form).  A group
 // work-group fills its 16 query columns with `cols` heads of each of `seqs` sequences,
 // so every shared block it reads serves all of them.
@@ -59,7 +95,13 @@ struct DecGroup {
   int batch;
 };
 
-template <typename T, int D, bool GROUP>
+// Sequences after which the first work-group of a sequence lands on the same shader
+// engine again (engines taken in a cycle of four, nsplit work-groups per sequence).
+__device__ inline int se_period(int nsplit) {
+  return (nsplit & 3) == 0 ? 1 : (nsplit & 1) ? 4 : 2;
+}
+
+template <typename T, int D, bool GROUP, bool Q8>
 __global__ void __launch_bounds__(kDecThreads, 2)
 decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                     int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -67,7 +109,10 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
                     const int32_t* __restrict__ bt, int bt_stride, int hq, int hkv, int nchunks,
                     int split_blocks, int nsplit, int max_ctx, float c_log2,
                     float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real,
-                    int blk_first, int slot0, int ws_slots, int force_partial, DecGroup grp) {
+                    int blk_first, int slot0, int ws_slots, int force_partial, DecGroup grp,
+                    DecQ8 q8) {
+  static_assert(!(GROUP && Q8), "the 8-bit pool has the plain form only");
+  using Step = std::conditional_t<Q8, DecStepQ8<D>, DecStep<D>>;
   constexpr int NKK = D / 32;
   constexpr int NDB = D / 16;               // 16-row d blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -91,8 +136,12 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   const int c16 = lane & 15, g4 = lane >> 4;
   // logical id -> (kvh, b, split, chunk), chunk fastest and KV head slowest: each XCD
   // works on few KV heads, so prefix blocks shared by many sequences stay in its L2.
-  // The grouped form puts each KV head's group work-groups (chunk, sequence group,
-  // shared key split) ahead of its private ones.
+  // Sequence b takes its splits rotated by b / se_period(nsplit): the dispatcher hands an
+  // XCD's work-groups to its four shader engines in a fixed cycle, and without the
+  // rotation a split count sharing a factor with that cycle would send every sequence's
+  // first split (often all shared-prefix blocks, cheap L2 hits) to the same engines
+  // while the others carry the long private splits.  The grouped form puts each KV head's group
+  // work-groups (chunk, sequence group, shared key split) ahead of its private ones.
   int kvh, b = 0, split = 0, chunk, gi = 0, ks = 0;
   bool group_wg = false;
   if constexpr (GROUP) {
@@ -107,16 +156,18 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     } else {
       r -= grp.per_kvh;
       chunk = r % nchunks; r /= nchunks;
-      split = r % nsplit;
+      const int sr = r % nsplit;
       b = r / nsplit;
+      split = (sr + b / se_period(nsplit)) % nsplit;
     }
   } else {
     const int batch = real / (nchunks * nsplit * hkv);
     int r = lid;
     chunk = r % nchunks; r /= nchunks;
-    split = r % nsplit; r /= nsplit;
+    const int sr = r % nsplit; r /= nsplit;
     b = r % batch;
     kvh = r / batch;
+    split = (sr + b / se_period(nsplit)) % nsplit;
   }
   const int h0 = kvh * G + chunk * kDecHeads;
   const int nh = min(kDecHeads, G - chunk * kDecHeads);
@@ -184,6 +235,22 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
         qb[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  if constexpr (Q8) {
+    // K's per-channel scales folded into the queries: q . k = sum_e (q_e s_e) code_e
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const float* ks = q8.k_scale + kvh * D + 8 * (4 * kk + g4);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(ks);
+      const f32x4 c = *reinterpret_cast<const f32x4*>(ks + 4);
+      const float sc[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack2<T>(T::to_f32((uint16_t)qb[kk][2 * i]) * sc[2 * i],
+                        T::to_f32((uint16_t)qb[kk][2 * i + 1]) * sc[2 * i + 1]);
+      qb[kk] = __builtin_bit_cast(s16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  }
 
   f32x4 o[NDB];
 #pragma unroll
@@ -204,7 +271,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   // Both blocks of a step through buffer resources sized to their valid rows: rows past
   // the context, blocks past the split and blocks outside the pool read as zero and
   // cost no memory traffic, and every load is issued unconditionally.
-  auto load = [&](int blk0, DecStep<D>& R) {
+  auto load = [&](int blk0, Step& R) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int blk = blk0 + hb;
@@ -213,6 +280,21 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       R.rows[hb] = rows;
       R.pos[hb] = blk * kBlock;
       const int64_t off = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
+      if constexpr (Q8) {
+        // codes: one byte per element, so the same offsets count bytes
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(kp) + off;
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(vp) + off;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)(rows * D));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)(rows * D));
+#pragma unroll
+        for (int j = 0; j < DecStepQ8<D>::NCH; ++j) {
+          R.k[hb][j] = buf_load16(rk, (uint32_t)(j * 64 + lane) * 16);
+          R.v[hb][j] = buf_load16(rv, (uint32_t)(j * 64 + lane) * 16);
+        }
+        const float* sb = q8.v_scale + ((int64_t)(pb >= 0 ? pb : 0) * hkv + kvh) * kBlock;
+        R.vs[hb] = __builtin_bit_cast(f32x4, buf_load16(make_rsrc(sb, (uint32_t)(rows * 4)), 16 * g4));
+        continue;
+      }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + off, (uint32_t)(rows * D * 2));
 #pragma unroll
@@ -223,9 +305,27 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
     }
   };
 
-  auto step = [&](const DecStep<D>& R) {
+  auto step = [&](const Step& R) {
     // V of both blocks into this wave's LDS slot, natural [key][d] layout (rows past
-    // the context arrive as zeros, so NaN left in unused pool slots never reaches PV)
+    // the context arrive as zeros, so NaN left in unused pool slots never reaches PV).
+    // 8-bit codes are widened to T on the way (chunk c: row c / (D/16), 16 columns).
+    if constexpr (Q8) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < DecStepQ8<D>::NCH; ++j) {
+          const int c = j * 64 + lane;
+          if (c >= D) continue;                   // d = 96: the second chunk of half the lanes
+          const int row = c / (D / 16), col = c - row * (D / 16);
+          uint4 lo, hi;
+          codes_to<T>(R.v[hb][j], lo, hi);
+          *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16) = lo;
+          *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16 + 8) = hi;
+          codes_to<T>(R.k[hb][j], lo, hi);
+          *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16) = lo;
+          *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16 + 8) = hi;
+        }
+    } else
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -287,7 +387,10 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       const float p0 = fast_exp2(t[2 * e] - m_run);
       const float p1 = fast_exp2(t[2 * e + 1] - m_run);
       l_run += p0 + p1;
-      pw[e] = pack2<T>(p0, p1);
+      if constexpr (Q8)      // O sums p * (V scale of the key) * code
+        pw[e] = pack2<T>(p0 * R.vs[e >> 1][2 * (e & 1)], p1 * R.vs[e >> 1][2 * (e & 1) + 1]);
+      else
+        pw[e] = pack2<T>(p0, p1);
     }
     const s16x8 pb8 = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     __builtin_amdgcn_wave_barrier();
@@ -312,7 +415,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   if (nsteps > 0) {
     constexpr int kStride = 2 * kDecWaves;
     int blk0 = blk_begin + 2 * w;
-    DecStep<D> A, B;
+    Step A, B;
     load(blk0, A);
     for (int it = 0; it < nsteps; it += 2) {
       load(blk0 + kStride, B);
@@ -489,22 +592,22 @@ void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, 
   *nsplit = (max_blocks + sb - 1) / sb;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool Q8 = false>
 static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
                                   const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx,
                                   int sb, int ns, float scale, float* ws_o, float* ws_ml,
-                                  hipStream_t s) {
+                                  hipStream_t s, DecQ8 q8 = DecQ8{}) {
   const int G = hq / p.num_kv_heads;
   const int nchunks = (G + kDecHeads - 1) / kDecHeads;
   const long long real = (long long)batch * p.num_kv_heads * ns * nchunks;
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   const float c = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, false, Q8>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                      nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, 0, 0, ns, 0,
-                     DecGroup{});
+                     DecGroup{}, q8);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns <= 1) return e;
   const int rows = batch * hq;
@@ -529,11 +632,11 @@ static hipError_t launch_decode_private_t(const kvb_pool& p, const void* q, void
   if (real > 0) {
     const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                        nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
-                       nks, slots, 1, DecGroup{});
+                       nks, slots, 1, DecGroup{}, DecQ8{});
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -619,11 +722,11 @@ static hipError_t launch_decode_grouped_t(const kvb_pool& p, const void* q, void
   if (real > 0) {
     const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                        nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
-                       sh_ns, slots, 1, g);
+                       sh_ns, slots, 1, g, DecQ8{});
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -667,6 +770,28 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
     default:  return bf ? launch_decode_t<BF16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s)
                         : launch_decode_t<F16, 128>(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, sb, ns, scale, ws_o, ws_ml, s);
   }
+}
+
+// Decode over the 8-bit pool: the split kernel's Q8 form (codes widened in the LDS
+// stage, K scales folded into the queries, V scales into the probabilities), then the
+// same merge.  The workspace layout is the 16-bit decode's.
+hipError_t launch_decode_q8(const kvb_pool_q8& p8, int dtype, const void* q, void* out,
+                            const int32_t* ctx, const int32_t* bt, int bt_stride, int batch, int hq,
+                            int max_ctx, int sb, int ns, float scale, void* ws, hipStream_t s) {
+  const kvb_pool p{p8.k, p8.v, p8.block_stride, p8.num_blocks, kBlock, p8.num_kv_heads,
+                   p8.head_dim, dtype};
+  const DecQ8 q8{p8.k_scale, p8.v_scale};
+  float* ws_o = (float*)ws;
+  float* ws_ml = ws_o + decode_ws_o_floats(batch, hq, p.head_dim, ns);
+  const bool bf = dtype == KVB_BF16;
+#define KVB_DQ8(TT, DD) launch_decode_t<TT, DD, true>(p, q, out, ctx, bt, bt_stride, batch, hq, \
+    max_ctx, sb, ns, scale, ws_o, ws_ml, s, q8)
+  switch (p.head_dim) {
+    case 64:  return bf ? KVB_DQ8(BF16, 64) : KVB_DQ8(F16, 64);
+    case 96:  return bf ? KVB_DQ8(BF16, 96) : KVB_DQ8(F16, 96);
+    default:  return bf ? KVB_DQ8(BF16, 128) : KVB_DQ8(F16, 128);
+  }
+#undef KVB_DQ8
 }
 
 }  // namespace kvb
