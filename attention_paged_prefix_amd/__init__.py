@@ -20,10 +20,11 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool  # noqa: F401
+from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool, KvbPoolQ8  # noqa: F401
 
 __all__ = [
     "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_cascade", "copy_blocks",
+    "PoolQ8", "write_kv_q8", "paged_decode_q8",
     "gather_kv",
     "paged_prefill_workspace_size", "paged_decode_workspace_size",
     "paged_decode_cascade_workspace_size", "version", "KvbError",
@@ -235,3 +236,83 @@ def copy_blocks(src: Pool, dst: Pool, src_ids: torch.Tensor, dst_ids: torch.Tens
     _lib.check("kvb_copy_blocks", lib.kvb_copy_blocks(
         ctypes.byref(a), ctypes.byref(b), _ptr(src_ids), _ptr(dst_ids), int(src_ids.numel()),
         _stream(stream)))
+
+
+@dataclass
+class PoolQ8:
+    """8-bit K/V pool (kvb_pool_q8): int8 codes ``k``/``v`` ``[num_blocks][num_kv_heads][16]
+    [head_dim]``, per-token V scales ``v_scale`` float32 ``[num_blocks][num_kv_heads][16]``
+    and the pool's per-channel K scales ``k_scale`` float32 ``[num_kv_heads][head_dim]``.
+    A code c stands for c * scale (kvboost 0.6.0, "Optional: KV quantization")."""
+    k: torch.Tensor
+    v: torch.Tensor
+    v_scale: torch.Tensor
+    k_scale: torch.Tensor
+
+    @classmethod
+    def empty(cls, num_blocks: int, num_kv_heads: int, head_dim: int, k_scale: torch.Tensor,
+              device="cuda") -> "PoolQ8":
+        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+        return cls(torch.zeros(shape, dtype=torch.int8, device=device),
+                   torch.zeros(shape, dtype=torch.int8, device=device),
+                   torch.zeros(shape[:3], dtype=torch.float32, device=device),
+                   k_scale.to(device=device, dtype=torch.float32).contiguous())
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[3])
+
+    def c_struct(self) -> KvbPoolQ8:
+        nb, hkv, bs, d = self.k.shape
+        for t, dt in ((self.k, torch.int8), (self.v, torch.int8), (self.v_scale, torch.float32),
+                      (self.k_scale, torch.float32)):
+            if t.dtype != dt or not t.is_contiguous():
+                raise ValueError("PoolQ8 tensors: contiguous int8 codes and float32 scales")
+        if self.v.shape != self.k.shape or self.v_scale.shape != (nb, hkv, bs) or \
+                self.k_scale.shape != (hkv, d):
+            raise ValueError("PoolQ8 tensor shapes do not match")
+        return KvbPoolQ8(self.k.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(),
+                         self.k_scale.data_ptr(), hkv * bs * d, nb, bs, hkv, d)
+
+
+def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                stream=None) -> None:
+    """kvb_write_kv_q8: code ``k_new/v_new [T][Hkv][d]`` (fp16/bf16) into the 8-bit pool's
+    slots ``slot_mapping`` (int64), writing each token's V scale."""
+    lib = _lib.load()
+    if k_new.dtype not in _DT or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new/v_new must both be float16 or bfloat16")
+    ps = pool.c_struct()
+    _lib.check("kvb_write_kv_q8", lib.kvb_write_kv_q8(
+        ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], _ptr(slot_mapping),
+        int(slot_mapping.numel()), _stream(stream)))
+
+
+def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
+                    block_tables: torch.Tensor, scale: float, max_context_len: int,
+                    split_blocks: int = 0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvb_paged_decode_q8: ``paged_decode`` over the 8-bit pool; ``q``/``out`` fp16 or bf16."""
+    lib = _lib.load()
+    if q.dtype not in _DT:
+        raise ValueError("q must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    B, hq, d = q.shape
+    need = paged_decode_workspace_size(B, pool.num_kv_heads, hq, d, max_context_len, split_blocks)
+    workspace = _workspace(need, q.device, workspace)
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_decode_q8", lib.kvb_paged_decode_q8(
+        ctypes.byref(ps), _DT[q.dtype], _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
+        int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out

@@ -30,6 +30,8 @@ EXPORTS = (
     "kvb_paged_decode_workspace_size",
     "kvb_paged_decode_cascade_workspace_size",
     "kvb_copy_blocks",
+    "kvb_write_kv_q8",
+    "kvb_paged_decode_q8",
     "kvb_gather_kv",
     "kvb_status_str",
     "kvb_version",
@@ -49,6 +51,20 @@ class KvbPool(ctypes.Structure):
     ]
 
 
+class KvbPoolQ8(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("block_stride", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
 class KvbError(RuntimeError):
     def __init__(self, fn: str, code: int):
         super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
@@ -62,6 +78,7 @@ _i32 = ctypes.c_int32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 _PP = ctypes.POINTER(KvbPool)
+_PQ = ctypes.POINTER(KvbPoolQ8)
 
 
 def load() -> ctypes.CDLL:
@@ -96,6 +113,11 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_decode_cascade_workspace_size.restype = _sz
     lib.kvb_copy_blocks.argtypes = [_PP, _PP, _vp, _vp, _i32, _vp]
     lib.kvb_copy_blocks.restype = ctypes.c_int
+    lib.kvb_write_kv_q8.argtypes = [_PQ, _vp, _vp, _i32, _vp, _i32, _vp]
+    lib.kvb_write_kv_q8.restype = ctypes.c_int
+    lib.kvb_paged_decode_q8.argtypes = [_PQ, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _f32, _vp, _sz, _vp]
+    lib.kvb_paged_decode_q8.restype = ctypes.c_int
     lib.kvb_gather_kv.argtypes = [_PP, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     lib.kvb_gather_kv.restype = ctypes.c_int
     lib.kvb_status_str.argtypes = [ctypes.c_int]

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvb.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "scatter_gather.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "scatter_gather.hip", "quant.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

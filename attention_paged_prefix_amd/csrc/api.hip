@@ -22,6 +22,20 @@ kvb_status check_pool(const kvb_pool* p) {
   return KVB_OK;
 }
 
+kvb_status check_pool_q8(const kvb_pool_q8* p) {
+  if (!p) return KVB_ERR_NULL;
+  if (!p->k || !p->v || !p->v_scale || !p->k_scale) return KVB_ERR_NULL;
+  if (p->block_size != 16) return KVB_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 96 && p->head_dim != 128) return KVB_ERR_UNSUPPORTED;
+  if (p->num_kv_heads <= 0 || p->num_blocks <= 0) return KVB_ERR_INVALID;
+  if (p->block_stride < (int64_t)p->num_kv_heads * 16 * p->head_dim) return KVB_ERR_INVALID;
+  if (p->block_stride % 16 != 0) return KVB_ERR_INVALID;
+  if (p->block_stride > 0x7fffffffLL) return KVB_ERR_INVALID;
+  if (!aligned16(p->k) || !aligned16(p->v) || !aligned16(p->v_scale) || !aligned16(p->k_scale))
+    return KVB_ERR_INVALID;
+  return KVB_OK;
+}
+
 kvb_status check_scale(float scale) {
   if (!isfinite(scale) || scale < 0.f) return KVB_ERR_INVALID;
   return KVB_OK;
@@ -234,6 +248,50 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
                                                   batch, num_q_heads, max_context_len, c.sb, c.ns,
                                                   c.nks, c.ks_tiles, scale, workspace,
                                                   (hipStream_t)stream));
+}
+
+kvb_status kvb_write_kv_q8(const kvb_pool_q8* pool, const void* k_new, const void* v_new,
+                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* stream) {
+  kvb_status st = check_pool_q8(pool);
+  if (st != KVB_OK) return st;
+  if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return KVB_ERR_INVALID;
+  if (num_tokens == 0) return KVB_OK;
+  if (!k_new || !v_new || !slot_mapping) return KVB_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_mapping & 7u)) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_write_kv_q8(*pool, dtype, k_new, v_new, slot_mapping, num_tokens,
+                                               (hipStream_t)stream));
+}
+
+kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q, void* out,
+                               const int32_t* context_lens, const int32_t* block_tables,
+                               int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t split_blocks, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  kvb_status st = check_pool_q8(pool);
+  if (st != KVB_OK) return st;
+  if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
+  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || split_blocks < 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0) return KVB_OK;
+  if (!q || !out || !context_lens || !block_tables) return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
+    return KVB_ERR_INVALID;
+  int sb = 0, ns = 0;
+  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
+  const size_t need = (size_t)kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return KVB_ERR_INVALID;
+  return launch_status(kvb::launch_decode_q8(*pool, dtype, q, out, context_lens, block_tables,
+                                             block_table_stride, batch, num_q_heads,
+                                             max_context_len, sb, ns, scale, workspace,
+                                             (hipStream_t)stream));
 }
 
 // Address the device uses for p: itself for device memory, the mapped address for pinned

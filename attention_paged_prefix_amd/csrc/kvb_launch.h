@@ -43,6 +43,13 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
                          const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
                          int ns, float scale, void* ws, hipStream_t s);
 
+// 8-bit pool: quantising slot scatter and decode (workspace as launch_decode's).
+hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int dtype, const void* kn, const void* vn,
+                              const int64_t* slots, int num_tokens, hipStream_t s);
+hipError_t launch_decode_q8(const kvb_pool_q8& p, int dtype, const void* q, void* out,
+                            const int32_t* ctx, const int32_t* bt, int bt_stride, int batch, int hq,
+                            int max_ctx, int sb, int ns, float scale, void* ws, hipStream_t s);
+
 // Cascade decode: the shared prefix pass (prefill kernel over all sequences' queries,
 // key tiles split over `nks` work-groups of `ks_tiles` tiles, partials to slots 0..nks-1)
 // and the private pass (decode split kernel from block `shared_len/16`, partials to

@@ -67,6 +67,16 @@ def decode_bytes(w, ctx, tables) -> float:
     return float(kv + qo + tab)
 
 
+def decode_bytes_q8(w, ctx, tables) -> float:
+    """Algorithmic bytes of decode over the 8-bit pool: one byte per K and V element plus
+    a float32 V scale per (token, KV head)."""
+    B = len(ctx)
+    kv = unique_kv_tokens(tables, ctx) * w.num_kv_heads * (2 * w.head_dim + 4)
+    qo = 2 * B * w.num_q_heads * w.head_dim * ESZ
+    tab = sum((int(n) + 15) // 16 for n in ctx) * 4 + B * 4
+    return float(kv + qo + tab)
+
+
 def prefill_bytes(w) -> float:
     T = w.total_q
     qo = 2 * T * w.num_q_heads * w.head_dim * ESZ
@@ -481,8 +491,9 @@ def bench_copy_blocks(torch, kvb, args):
 def bench_decode(torch, kvb, args):
     """The paged-decode workload: 64 sequences, contexts U{512..4096} (seed 3), first 1024
     tokens shared, 32/8 heads, d=128, bf16, pool of 16384 blocks.  Timed as the plain split
-    decode and as the shared-prefix (cascade) decode, which reads the 1024 shared tokens
-    once for all sequences; both produce the same output up to rounding."""
+    decode, as the shared-prefix (cascade) decode, which reads the 1024 shared tokens
+    once for all sequences (both produce the same output up to rounding), and as decode
+    over the same tokens in the 8-bit pool."""
     from workloads import make_config
     w = make_config("decode")
     k = _dev_bits(torch, w.k_pool, w.dtype)
@@ -513,14 +524,34 @@ def bench_decode(torch, kvb, args):
         kvb.paged_decode_cascade(pool, q, ctx, bt, shared, shared_len, w.scale, max_ctx,
                                  split_blocks=sb, out=out, workspace=wsc)
 
-    settle(torch, lambda: (run(), run_cascade()), args.settle_ms)
+    # The same context tokens in the 8-bit pool (kvb_write_kv_q8); the pool's per-channel
+    # K scales are the context tokens' absolute maxima / 127.
+    slot_list = []
+    for b in range(w.batch):
+        j = np.arange(int(w.context_lens[b]))
+        slot_list.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    slots = torch.from_numpy(np.unique(np.concatenate(slot_list))).to("cuda:0")
+    kt = k[slots // 16, :, slots % 16, :].contiguous()
+    vt = v[slots // 16, :, slots % 16, :].contiguous()
+    k_scale = (kt.float().abs().amax(dim=0) / 127.0).contiguous()
+    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, k_scale)
+    kvb.write_kv_q8(p8, kt, vt, slots)
+    del kt, vt
+
+    def run_q8():
+        kvb.paged_decode_q8(p8, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
+
+    settle(torch, lambda: (run(), run_cascade(), run_q8()), args.settle_ms)
     for _ in range(args.warmup):
         run()
         run_cascade()
+        run_q8()
     torch.cuda.synchronize()
     steps = max(args.steps, 10)
     tw, tc = _time_warm_cold(torch, run, steps, flush)
     cw, cc = _time_warm_cold(torch, run_cascade, steps, flush)
+    qw, qc = _time_warm_cold(torch, run_q8, steps, flush)
+    by8 = decode_bytes_q8(w, w.context_lens, w.block_tables)
     by = decode_bytes(w, w.context_lens, w.block_tables)
     logical = float(np.sum(w.context_lens)) * w.num_kv_heads * w.head_dim * 2 * ESZ
     return {"workload": "paged decode, 64 sequences, contexts 512..4096, first 1024 tokens shared",
@@ -532,7 +563,12 @@ def bench_decode(torch, kvb, args):
             "cascade": {"shared_tokens": shared_len, "ms_back_to_back": cw, "ms_cold_cache": cc,
                         "gbps_back_to_back": by / (cw * 1e-3) / 1e9,
                         "gbps_cold_cache": by / (cc * 1e-3) / 1e9,
-                        "frac_hbm_peak_cold": by / (cc * 1e-3) / 1e9 / PEAK_GBPS}}
+                        "frac_hbm_peak_cold": by / (cc * 1e-3) / 1e9 / PEAK_GBPS},
+            "q8": {"pool": "8-bit codes, per-channel K scales, per-token V scales",
+                   "algorithmic_bytes": by8, "ms_back_to_back": qw, "ms_cold_cache": qc,
+                   "gbps_cold_cache": by8 / (qc * 1e-3) / 1e9,
+                   "frac_hbm_peak_cold": by8 / (qc * 1e-3) / 1e9 / PEAK_GBPS,
+                   "speedup_vs_16bit_cold": tc / qc}}
 
 
 if __name__ == "__main__":

@@ -185,6 +185,51 @@ size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_hea
 kvb_status kvb_copy_blocks(const kvb_pool* src, const kvb_pool* dst, const int32_t* src_ids,
                            const int32_t* dst_ids, int32_t n, void* stream);
 
+/* 8-bit K/V pool (kvboost 0.6.0, "Optional: KV quantization": cached K is stored at
+ * per-channel scales and V at per-token scales, about half the bytes of a 16-bit pool).
+ * A code c (int8, -127..127) stands for the value c * scale.
+ *   k, v (device, int8): code (block, kv_head, row, e) at
+ *       block*block_stride + (kv_head*16 + row)*head_dim + e            (bytes)
+ *   v_scale (device, float32): scale of token (block, kv_head, row) at
+ *       (block*num_kv_heads + kv_head)*16 + row; written by kvb_write_kv_q8
+ *   k_scale (device, float32): the pool's K scale of channel (kv_head, e) at
+ *       kv_head*head_dim + e; chosen by the caller (for instance max |k| over the prompt's
+ *       tokens / 127), finite and >= 0; read by every call, changed by none.
+ * block_stride (bytes) >= num_kv_heads*16*head_dim, a multiple of 16, below 2^31. */
+typedef struct {
+  void*        k;             /* (device) K codes                                */
+  void*        v;             /* (device) V codes                                */
+  float*       v_scale;       /* (device) per-token V scales                     */
+  const float* k_scale;       /* (device) per-channel K scales                   */
+  int64_t      block_stride;  /* bytes between consecutive physical blocks       */
+  int32_t      num_blocks;    /* physical blocks in the pool (> 0)               */
+  int32_t      block_size;    /* must be 16                                      */
+  int32_t      num_kv_heads;  /* > 0                                             */
+  int32_t      head_dim;      /* 64, 96 or 128                                   */
+} kvb_pool_q8;
+
+/* Quantising slot scatter: kvb_write_kv's slot rule, each token coded on the way in.
+ * For token t with an in-pool slot, kv head h, channel e (x taken exactly as float32):
+ *   K code = rint(k_new[t][h][e] / k_scale[h][e]) clamped to [-127, 127] (0 where the
+ *   scale is 0); V scale s = max_e |v_new[t][h][e]| / 127, stored in v_scale; V code =
+ *   rint(v_new[t][h][e] / s) (0 where s is 0).  Divisions are IEEE float32, rint rounds
+ *   half to even.  k_new, v_new: (device) [num_tokens][num_kv_heads][head_dim] in `dtype`
+ *   (a kvb_dtype).  slot_mapping: (device) int64 [num_tokens]. */
+kvb_status kvb_write_kv_q8(const kvb_pool_q8* pool, const void* k_new, const void* v_new,
+                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* stream);
+
+/* Paged decode over the 8-bit pool: kvb_paged_decode with every key and value read as
+ * the value its code stands for.  q, out: (device) [batch][num_q_heads][head_dim] in
+ * `dtype`.  workspace: kvb_paged_decode_workspace_size(...) bytes for the same batch,
+ * heads, head_dim, max_context_len and split_blocks (the same split plan).  Other
+ * arguments as kvb_paged_decode. */
+kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q, void* out,
+                               const int32_t* context_lens, const int32_t* block_tables,
+                               int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t split_blocks, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Test helper: gather through the block tables into a contiguous layout, bit-exact.
  * For b < batch, j < seq_lens[b]:
  *   k_out[cu_seq_lens[b] + j][h][:] = pool.k[block_tables[b*stride + j/16]][h][j%16][:]

@@ -172,6 +172,45 @@ def test_copy_blocks_validation(lib):
     assert c(p, p, d=FAKE + 2) == INVALID
 
 
+def pool_q8(**kw):
+    p = dict(k=FAKE, v=FAKE + 4096, v_scale=FAKE + 8192, k_scale=FAKE + 12288,
+             block_stride=2 * 16 * 128, num_blocks=8, block_size=16, num_kv_heads=2, head_dim=128)
+    p.update(kw)
+    return _lib.KvbPoolQ8(**p)
+
+
+def test_q8_validation(lib):
+    def w(p, **kw):
+        return lib.kvb_write_kv_q8(ctypes.byref(p), kw.get("kn", FAKE), kw.get("vn", FAKE),
+                                   kw.get("dt", _lib.KVB_BF16), kw.get("slots", FAKE), kw.get("n", 4), None)
+    assert lib.kvb_write_kv_q8(None, FAKE, FAKE, 1, FAKE, 4, None) == NULL
+    assert w(pool_q8(k_scale=None)) == NULL
+    assert w(pool_q8(v_scale=FAKE + 4)) == INVALID
+    assert w(pool_q8(block_stride=2 * 16 * 128 + 8)) == INVALID     # whole 16-byte units
+    assert w(pool_q8(block_stride=16 * 128)) == INVALID             # < heads * 16 * head_dim
+    assert w(pool_q8(head_dim=80)) == UNSUP
+    assert w(pool_q8(block_size=8)) == UNSUP
+    assert w(pool_q8(), dt=5) == UNSUP
+    assert w(pool_q8(), kn=None) == NULL
+    assert w(pool_q8(), slots=FAKE + 4) == INVALID
+    assert w(pool_q8(), n=-1) == INVALID
+    assert w(pool_q8(), n=0) == OK
+
+    def d(p, **kw):
+        return lib.kvb_paged_decode_q8(ctypes.byref(p), kw.get("dt", 1), kw.get("q", FAKE), FAKE, FAKE,
+                                       FAKE, kw.get("stride", 256), kw.get("batch", 4), kw.get("hq", 8),
+                                       4000, 0, 0.1, kw.get("ws", None), kw.get("wsb", 0), None)
+    need = lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 0)
+    assert d(pool_q8()) == WS                         # the split decode's workspace
+    assert d(pool_q8(), ws=FAKE, wsb=need - 1) == WS
+    assert d(pool_q8(), ws=FAKE + 8, wsb=need) == INVALID
+    assert d(pool_q8(), stride=249) == INVALID
+    assert d(pool_q8(), hq=5) == INVALID
+    assert d(pool_q8(), dt=9) == UNSUP
+    assert d(pool_q8(), q=None) == NULL
+    assert d(pool_q8(), batch=0) == OK
+
+
 def test_prefill_pooled_validation(lib):
     p = pool()
     def pp(**kw):

@@ -1,0 +1,181 @@
+"""GPU parity of the 8-bit K/V pool (kvb_write_kv_q8, kvb_paged_decode_q8) against the
+oracle (oracle/quant.py): the quantising scatter bit-exact (codes and V scales), decode
+over the 8-bit pool within the decode tolerance (max abs error <= 1e-2 fp16, 2e-2 bf16).
+Every expected value comes from the oracle's own quantisation of the 16-bit inputs."""
+import numpy as np
+import pytest
+
+from workloads import make_config, make_custom
+from workloads.gen import round_to_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _util():
+    import gpu_util
+    return gpu_util
+
+
+def _pool_q8(kc, vc, vs, ks):
+    import attention_paged_prefix_amd as kvb
+    dev = "cuda:0"
+    return kvb.PoolQ8(torch.from_numpy(np.ascontiguousarray(kc)).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(vc)).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(vs)).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(ks)).to(dev))
+
+
+def _poisoned(nb, hkv, d):
+    """Unwritten slots: codes at the extremes and NaN V scales, so a read of one shows."""
+    return (np.full((nb, hkv, 16, d), 127, np.int8), np.full((nb, hkv, 16, d), -127, np.int8),
+            np.full((nb, hkv, 16), np.nan, np.float32))
+
+
+def _context_slots(w, seqs=None):
+    """Distinct pool slots of the contexts of a decode workload (shared blocks once)."""
+    slots = []
+    for b in (range(w.batch) if seqs is None else seqs):
+        n = int(w.context_lens[b])
+        j = np.arange(n)
+        slots.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    return np.unique(np.concatenate(slots)) if slots else np.zeros(0, np.int64)
+
+
+def _tokens_at(pool_bits, slots):
+    return np.ascontiguousarray(pool_bits[slots // 16, :, slots % 16, :])
+
+
+@pytest.mark.parametrize("dt,d,hkv", [("bf16", 128, 8), ("fp16", 96, 2), ("bf16", 64, 1),
+                                      ("fp16", 128, 4)])
+def test_write_kv_q8_bit_exact(dt, d, hkv):
+    from oracle import quant
+    u = _util()
+    rng = np.random.default_rng(801 + d + hkv)
+    nb, T = 12, 150
+    mag = rng.uniform(0.05, 20.0, size=(T, hkv, 1))
+    K = rng.standard_normal((T, hkv, d)) * mag
+    V = rng.standard_normal((T, hkv, d)) * mag
+    V[7] = 0.0                                            # a zero token: scale 0, codes 0
+    kb, vb = round_to_bits(K, dt), round_to_bits(V, dt)
+    k_scale = quant.channel_scales(oracle_f32(kb, dt)) * np.float32(0.8)   # some codes clamp
+    k_scale[0, 3] = 0.0                                   # a zero channel scale
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[[2, 50]] = -1
+    slots[60] = nb * 16 + 5                               # outside the pool: skipped
+    kc0 = rng.integers(-127, 128, size=(nb, hkv, 16, d)).astype(np.int8)
+    vc0 = rng.integers(-127, 128, size=(nb, hkv, 16, d)).astype(np.int8)
+    vs0 = rng.uniform(0, 1, size=(nb, hkv, 16)).astype(np.float32)
+    ref = quant.write_kv_q8(kc0, vc0, vs0, k_scale, kb, vb, np.where(slots < nb * 16, slots, -1), dt)
+    pool = _pool_q8(kc0, vc0, vs0, k_scale)
+    import attention_paged_prefix_amd as kvb
+    kvb.write_kv_q8(pool, u.to_dev(kb, dt), u.to_dev(vb, dt), u.idev(slots, torch.int64))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.k.cpu().numpy(), ref[0])
+    assert np.array_equal(pool.v.cpu().numpy(), ref[1])
+    assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), ref[2].view(np.uint32))
+
+
+def oracle_f32(bits, dt):
+    import oracle
+    return oracle.decode_bits(bits, dt).astype(np.float32)
+
+
+Q8_DECODE_CASES = [
+    (811, "bf16", 32, 8, 128, [517, 1, 16, 17, 4001, 2048]),
+    (812, "fp16", 8, 8, 64, [3, 64, 100, 0]),
+    (813, "fp16", 40, 8, 96, [1000, 33]),
+    (814, "bf16", 16, 2, 128, [300, 2000, 15]),
+]
+
+
+def _oracle_q8_pool(w, slots):
+    """The oracle's 8-bit pool of a decode workload: K scales from the context tokens,
+    every context slot written by the oracle, the other slots poisoned."""
+    from oracle import quant
+    kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+    k_scale = quant.channel_scales(oracle_f32(kt, w.dtype))
+    kc, vc, vs = _poisoned(w.k_pool.shape[0], w.num_kv_heads, w.head_dim)
+    kc, vc, vs = quant.write_kv_q8(kc, vc, vs, k_scale, kt, vt, slots, w.dtype)
+    return kc, vc, vs, k_scale, kt, vt
+
+
+@pytest.mark.parametrize("case", Q8_DECODE_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+@pytest.mark.parametrize("split", [0, 3])
+def test_decode_q8_matches_oracle(case, split):
+    """Decode over an 8-bit pool the oracle wrote, against the oracle's decode over it."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    seed, dt, hq, hkv, d, ctx = case
+    w = make_custom(seed, dt, hq, hkv, d, ctx, kind="decode", share="all", poison=False)
+    kc, vc, vs, ks, _, _ = _oracle_q8_pool(w, _context_slots(w))
+    pool = _pool_q8(kc, vc, vs, ks)
+    got = u.to_bits(kvb.paged_decode_q8(pool, u.to_dev(w.q, dt), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(max(ctx)),
+                                        split_blocks=split))
+    torch.cuda.synchronize()
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, dt)
+    import oracle
+    assert np.isfinite(oracle.decode_bits(got, dt)).all()
+    for b, n in enumerate(ctx):
+        if n <= 0:
+            assert (got[b] == 0).all()
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+def test_write_then_decode_q8_end_to_end():
+    """Every context token written by the GPU's quantising scatter, then decoded on the
+    GPU; the oracle writes and decodes the same tokens itself."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    w = make_custom(815, "bf16", 32, 8, 128, [700, 2049, 16, 1333], kind="decode", share="pairs",
+                    poison=False)
+    slots = _context_slots(w)
+    kc, vc, vs, ks, kt, vt = _oracle_q8_pool(w, slots)
+    pk, pv, ps = _poisoned(w.k_pool.shape[0], 8, 128)
+    pool = _pool_q8(pk, pv, ps, ks)
+    kvb.write_kv_q8(pool, u.to_dev(kt, "bf16"), u.to_dev(vt, "bf16"), u.idev(slots, torch.int64))
+    got = u.to_bits(kvb.paged_decode_q8(pool, u.to_dev(w.q, "bf16"), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(w.context_lens.max())))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.k.cpu().numpy(), kc) and np.array_equal(pool.v.cpu().numpy(), vc)
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, "bf16")
+    assert u.max_err(got, ref, "bf16") <= u.TOL["bf16"]
+
+
+def test_decode_q8_full_size_sampled():
+    """The paged-decode workload (64 sequences, contexts 512..4096, 1024 shared tokens,
+    32/8 heads, d=128, bf16) through the 8-bit pool, in the benchmark's launch
+    configuration; eight sequences checked against the oracle, which quantises and
+    decodes their tokens itself."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    w = make_config("decode")
+    slots = _context_slots(w)
+    kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+    ks = quant.channel_scales(oracle_f32(kt, "bf16"))
+    pk, pv, ps = _poisoned(w.k_pool.shape[0], 8, 128)
+    pool = _pool_q8(pk, pv, ps, ks)
+    kvb.write_kv_q8(pool, u.to_dev(kt, "bf16"), u.to_dev(vt, "bf16"), u.idev(slots, torch.int64))
+    got = u.to_bits(kvb.paged_decode_q8(pool, u.to_dev(w.q, "bf16"), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(w.context_lens.max())))
+    torch.cuda.synchronize()
+    seqs = [0, 5, 17, 31, 40, 47, 58, 63]
+    sl = _context_slots(w, seqs)
+    kc, vc, vs = _poisoned(w.k_pool.shape[0], 8, 128)
+    kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, _tokens_at(w.k_pool, sl), _tokens_at(w.v_pool, sl),
+                                   sl, "bf16")
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q[seqs], w.context_lens[seqs],
+                                w.block_tables[seqs], w.scale, "bf16")
+    assert u.max_err(got[seqs], ref, "bf16") <= u.TOL["bf16"]
