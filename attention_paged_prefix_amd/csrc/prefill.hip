@@ -634,7 +634,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 // XCD range (the logical ids one XCD runs) computes every item's key count (prefix plus
 // the causal part of its last row; 0 for tiles past the chunk), sorts the range by it in
 // 32 buckets relative to the range's largest count, largest first, and writes the item
-// for each position.  Within a bucket items keep table order (tiles of one sequence and
+// for each position (table order when every non-empty item is within 2x of the largest).  Within a bucket items keep table order (tiles of one sequence and
 // KV head together, so they share its K/V through L2), and the plan is deterministic.
 // Items never leave their XCD range, so each XCD keeps its KV heads in L2.
 constexpr int kPlanThreads = 256;
@@ -646,14 +646,17 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
                     int G, int total_q, int bt_stride, int max_tiles, int padded, int real,
                     int32_t* __restrict__ order) {
   __shared__ uint64_t key[kPlanMax];
-  __shared__ int s_max;
+  __shared__ int s_max, s_min;
   const int per = padded / kNumXcd;
   const int lo = blockIdx.x * per;
   const int n = min(per, real - lo);
   if (n <= 0) return;
   int N = 1;
   while (N < n) N <<= 1;
-  if (threadIdx.x == 0) s_max = 0;
+  if (threadIdx.x == 0) {
+    s_max = 0;
+    s_min = 0x7fffffff;
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += kPlanThreads) {
     const int lid = lo + i;
@@ -666,9 +669,16 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
     const int64_t cost = v0 < nrows ? min(P0 + (min(nrows, v0 + kBM) - 1) / G + 1, (int64_t)0x3fffffff) : 0;
     key[i] = (uint64_t)cost;
     atomicMax(&s_max, (int)cost);
+    if (cost > 0) atomicMin(&s_min, (int)cost);
   }
   __syncthreads();
-  const int64_t cmax = s_max;
+  const int64_t cmax = s_max, cmin = s_min;
+  if (2 * cmin > cmax) {
+    // every tile within 2x of the largest: nothing to balance, and table order keeps
+    // the tiles of one sequence and KV head together
+    for (int i = threadIdx.x; i < n; i += kPlanThreads) order[lo + i] = lo + i;
+    return;
+  }
   for (int i = threadIdx.x; i < N; i += kPlanThreads) {
     uint64_t k = ~0ull;                 // padding sorts last
     if (i < n) {
