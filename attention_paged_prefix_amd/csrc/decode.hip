@@ -48,11 +48,14 @@ template <int D> struct DecStep {
 
 // The 8-bit pool's step: 16 codes per 16-byte chunk, so a block's K (or V) is D chunks,
 // (D + 63) / 64 per lane; plus the V scales of the lane's four keys of each block.
+// The 8-bit pool's step: 16 codes per 16-byte chunk, so a block's K (or V) is D chunks,
+// (D + 63) / 64 per lane; vsc holds the V scale of the key row each of the lane's V
+// chunks belongs to.
 template <int D> struct DecStepQ8 {
   static constexpr int NCH = (D + 63) / 64;
   uint4 k[2][NCH];
   uint4 v[2][NCH];
-  f32x4 vs[2];
+  float vsc[2][NCH];
   int rows[2];
   int pos[2];
 };
@@ -64,17 +67,18 @@ struct DecQ8 {
   const float* v_scale;
 };
 
-// 16 int8 codes -> 16 values of T in two 16-byte halves (exact: |code| <= 127 fits the
-// 8-bit significand of bf16 and the 11-bit one of fp16).
+// 16 int8 codes -> 16 values code * s of T in two 16-byte halves (s = 1: exact, since
+// |code| <= 127 fits the 8-bit significand of bf16 and the 11-bit one of fp16; otherwise
+// rounded to nearest even like any 16-bit value).
 template <typename T>
-__device__ inline void codes_to(uint4 c, uint4& lo, uint4& hi) {
+__device__ inline void codes_to(uint4 c, float s, uint4& lo, uint4& hi) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int32_t x = (int32_t)w[i];
-    o[2 * i] = pack2<T>((float)((x << 24) >> 24), (float)((x << 16) >> 24));
-    o[2 * i + 1] = pack2<T>((float)((x << 8) >> 24), (float)(x >> 24));
+    o[2 * i] = pack2<T>((float)((x << 24) >> 24) * s, (float)((x << 16) >> 24) * s);
+    o[2 * i + 1] = pack2<T>((float)((x << 8) >> 24) * s, (float)(x >> 24) * s);
   }
   lo = make_uint4(o[0], o[1], o[2], o[3]);
   hi = make_uint4(o[4], o[5], o[6], o[7]);
@@ -292,7 +296,11 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
           R.v[hb][j] = buf_load16(rv, (uint32_t)(j * 64 + lane) * 16);
         }
         const float* sb = q8.v_scale + ((int64_t)(pb >= 0 ? pb : 0) * hkv + kvh) * kBlock;
-        R.vs[hb] = __builtin_bit_cast(f32x4, buf_load16(make_rsrc(sb, (uint32_t)(rows * 4)), 16 * g4));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sb, (uint32_t)(rows * 4));
+#pragma unroll
+        for (int j = 0; j < DecStepQ8<D>::NCH; ++j)        // chunk j*64+lane: key row / (D/16)
+          R.vsc[hb][j] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) / (D / 16) * 4, 0, 0));
         continue;
       }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
@@ -308,7 +316,8 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   auto step = [&](const Step& R) {
     // V of both blocks into this wave's LDS slot, natural [key][d] layout (rows past
     // the context arrive as zeros, so NaN left in unused pool slots never reaches PV).
-    // 8-bit codes are widened to T on the way (chunk c: row c / (D/16), 16 columns).
+    // 8-bit codes are widened to T on the way (chunk c: row c / (D/16), 16 columns), V
+    // codes multiplied by their key's V scale there (dequantised in the LDS stage).
     if constexpr (Q8) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -318,10 +327,10 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
           if (c >= D) continue;                   // d = 96: the second chunk of half the lanes
           const int row = c / (D / 16), col = c - row * (D / 16);
           uint4 lo, hi;
-          codes_to<T>(R.v[hb][j], lo, hi);
+          codes_to<T>(R.v[hb][j], R.vsc[hb][j], lo, hi);
           *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16) = lo;
           *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16 + 8) = hi;
-          codes_to<T>(R.k[hb][j], lo, hi);
+          codes_to<T>(R.k[hb][j], 1.f, lo, hi);
           *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16) = lo;
           *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16 + 8) = hi;
         }
@@ -387,10 +396,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       const float p0 = fast_exp2(t[2 * e] - m_run);
       const float p1 = fast_exp2(t[2 * e + 1] - m_run);
       l_run += p0 + p1;
-      if constexpr (Q8)      // O sums p * (V scale of the key) * code
-        pw[e] = pack2<T>(p0 * R.vs[e >> 1][2 * (e & 1)], p1 * R.vs[e >> 1][2 * (e & 1) + 1]);
-      else
-        pw[e] = pack2<T>(p0, p1);
+      pw[e] = pack2<T>(p0, p1);
     }
     const s16x8 pb8 = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     __builtin_amdgcn_wave_barrier();
