@@ -1,4 +1,4 @@
-"""8-bit K/V pool: quantisation, dequantisation and decode over the quantised pool.
+"""8-bit K/V pool: quantisation, dequantisation, and decode and prefill over the pool.
 
 Test infrastructure only (see the package docstring).  The pages store cached K/V at
 8 bits with per-channel scales for K and per-token scales for V (kvboost 0.6.0,
@@ -110,3 +110,33 @@ def paged_decode_q8(k_codes, v_codes, v_scales, k_scale, q, context_lens, block_
             out[b, h] = o[0]
             lse_all[b, h] = lse[0]
     return (out, lse_all) if want_lse else out
+
+
+def paged_prefill_q8(k_codes, v_codes, v_scales, k_scale, q, k_new, v_new, cu_q_lens, prefix_lens,
+                     block_tables, num_q_heads: int, scale: float, dtype: str):
+    """Chunk prefill (as ``attention.paged_prefill``: row i of sequence b at position
+    ``P_b + i`` sees the whole cached prefix and chunk tokens ``0..i``) with the cached
+    prefix read from the 8-bit pool as the values its codes stand for; the chunk's own
+    K/V are the call's 16-bit rows.  Returns float64 ``[T][Hq][d]``."""
+    cu = np.asarray(cu_q_lens, dtype=np.int64)
+    P = np.asarray(prefix_lens, dtype=np.int64)
+    Hkv = k_codes.shape[1]
+    G = num_q_heads // Hkv
+    T, _, d = q.shape
+    out = np.zeros((T, num_q_heads, d), dtype=np.float64)
+    for b in range(len(P)):
+        C = int(cu[b + 1] - cu[b])
+        if C == 0:
+            continue
+        n = int(P[b])
+        j = np.arange(n)
+        blocks = np.asarray(block_tables[b], dtype=np.int64)[j // BLOCK_SIZE]
+        Kp = dequant_k(gather_kv(k_codes, block_tables[b], n), k_scale)
+        Vp = dequant_v(gather_kv(v_codes, block_tables[b], n), v_scales[blocks, :, j % BLOCK_SIZE])
+        K = np.concatenate([Kp, decode_bits(k_new[cu[b]:cu[b + 1]], dtype)], axis=0)
+        V = np.concatenate([Vp, decode_bits(v_new[cu[b]:cu[b + 1]], dtype)], axis=0)
+        pos = n + np.arange(C)
+        for h in range(num_q_heads):
+            o, _ = attend(decode_bits(q[cu[b]:cu[b + 1], h], dtype), K[:, h // G], V[:, h // G], pos, scale)
+            out[cu[b]:cu[b + 1], h] = o
+    return out

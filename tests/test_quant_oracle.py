@@ -138,3 +138,37 @@ def test_decode_over_exact_pool_equals_plain_decode(dtype):
     got = quant.paged_decode_q8(Kc, Vc, Vs, k_scale, q, ctx, bt, 0.125, dtype)
     assert np.array_equal(got, ref)
     assert (got[ctx == 0] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_prefill_over_exact_pool_equals_plain_prefill(dtype):
+    """Prefill whose cached prefix sits in the 8-bit pool with values exactly code x scale
+    equals the 16-bit prefill of the same values, bit for bit."""
+    rng = np.random.default_rng(5)
+    nb, hkv, hq, d = 30, 2, 6, 64
+    P = np.array([0, 40, 129, 16], np.int64)
+    C = np.array([5, 17, 3, 30], np.int64)
+    n_tok = int(P.sum())
+    k_scale, kc, vc, ve, kb, vb = _exact_pool(rng, dtype, nb, hkv, d, n_tok)
+    perm = rng.permutation(nb)
+    stride = 10
+    bt = np.full((len(P), stride), -1, np.int32)
+    slots, used = [], 0
+    for b, n in enumerate(P):
+        nblk = (n + 15) // 16
+        bt[b, :nblk] = perm[used:used + nblk]
+        used += nblk
+        slots += [int(bt[b, j // 16]) * 16 + j % 16 for j in range(n)]
+    slots = np.array(slots, np.int64)
+    K16, V16 = oracle.write_kv(np.zeros((nb, hkv, 16, d), np.uint16), np.zeros((nb, hkv, 16, d), np.uint16),
+                               kb, vb, slots)
+    Kc, Vc, Vs = quant.write_kv_q8(np.zeros((nb, hkv, 16, d), np.int8), np.zeros((nb, hkv, 16, d), np.int8),
+                                   np.zeros((nb, hkv, 16), np.float32), k_scale, kb, vb, slots, dtype)
+    T = int(C.sum())
+    cu = np.concatenate([[0], np.cumsum(C)])
+    q = bits(rng.standard_normal((T, hq, d)), dtype)
+    kn = bits(rng.standard_normal((T, hkv, d)), dtype)
+    vn = bits(rng.standard_normal((T, hkv, d)), dtype)
+    ref = oracle.paged_prefill(K16, V16, q, kn, vn, cu, P, bt, hq, 0.125, dtype)
+    got = quant.paged_prefill_q8(Kc, Vc, Vs, k_scale, q, kn, vn, cu, P, bt, hq, 0.125, dtype)
+    assert np.array_equal(got, ref)
