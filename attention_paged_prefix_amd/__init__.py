@@ -24,7 +24,7 @@ from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool, KvbPoolQ8  # noqa: F401
 
 __all__ = [
     "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_cascade", "copy_blocks",
-    "PoolQ8", "write_kv_q8", "paged_decode_q8",
+    "PoolQ8", "write_kv_q8", "paged_decode_q8", "paged_prefill_q8", "paged_prefill_q8_workspace_size",
     "gather_kv",
     "paged_prefill_workspace_size", "paged_decode_workspace_size",
     "paged_decode_cascade_workspace_size", "version", "KvbError",
@@ -315,4 +315,35 @@ def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
         int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def paged_prefill_q8_workspace_size(batch: int, num_kv_heads: int, num_q_heads: int, head_dim: int,
+                                    total_q: int, max_prefix_len: int) -> int:
+    return int(_lib.load().kvb_paged_prefill_q8_workspace_size(batch, num_kv_heads, num_q_heads,
+                                                               head_dim, total_q, max_prefix_len))
+
+
+def paged_prefill_q8(pool: PoolQ8, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                     cu_q_lens: torch.Tensor, prefix_lens: torch.Tensor, block_tables: torch.Tensor,
+                     scale: float, max_q_len: int, max_prefix_len: int,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """kvb_paged_prefill_q8: ``paged_prefill`` with the cached prefix in the 8-bit pool;
+    ``q``, ``k_new``, ``v_new``, ``out`` fp16 or bf16."""
+    lib = _lib.load()
+    if q.dtype not in _DT:
+        raise ValueError("q must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    batch = int(prefix_lens.numel())
+    T, hq, d = q.shape
+    need = paged_prefill_q8_workspace_size(batch, pool.num_kv_heads, hq, d, T, max_prefix_len)
+    workspace = _workspace(need, q.device, workspace)
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_prefill_q8", lib.kvb_paged_prefill_q8(
+        ctypes.byref(ps), _DT[q.dtype], _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
+        _ptr(cu_q_lens), _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch,
+        hq, T, int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

@@ -32,6 +32,8 @@ EXPORTS = (
     "kvb_copy_blocks",
     "kvb_write_kv_q8",
     "kvb_paged_decode_q8",
+    "kvb_paged_prefill_q8",
+    "kvb_paged_prefill_q8_workspace_size",
     "kvb_gather_kv",
     "kvb_status_str",
     "kvb_version",
@@ -118,6 +120,11 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_decode_q8.argtypes = [_PQ, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _f32, _vp, _sz, _vp]
     lib.kvb_paged_decode_q8.restype = ctypes.c_int
+    lib.kvb_paged_prefill_q8.argtypes = [_PQ, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+    lib.kvb_paged_prefill_q8.restype = ctypes.c_int
+    lib.kvb_paged_prefill_q8_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+    lib.kvb_paged_prefill_q8_workspace_size.restype = _sz
     lib.kvb_gather_kv.argtypes = [_PP, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     lib.kvb_gather_kv.restype = ctypes.c_int
     lib.kvb_status_str.argtypes = [ctypes.c_int]

@@ -294,6 +294,49 @@ kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const voi
                                              (hipStream_t)stream));
 }
 
+size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
+                                           int32_t num_q_heads, int32_t head_dim,
+                                           int32_t total_q, int32_t max_prefix_len) {
+  if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || total_q <= 0 || max_prefix_len < 0 ||
+      (head_dim != 64 && head_dim != 96 && head_dim != 128))
+    return 0;
+  return (size_t)kvb::prefill_q8_ws_bytes(batch, num_kv_heads, num_q_heads, head_dim, total_q,
+                                          max_prefix_len);
+}
+
+kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,
+                                const void* k_new, const void* v_new, void* out,
+                                const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  kvb_status st = check_pool_q8(pool);
+  if (st != KVB_OK) return st;
+  if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
+  if (batch < 0 || total_q < 0 || max_q_len < 0 || max_prefix_len < 0 || num_q_heads <= 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0 || total_q == 0) return KVB_OK;
+  if (!q || !k_new || !v_new || !out || !cu_q_lens || !prefix_lens || !block_tables)
+    return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+      ((uintptr_t)cu_q_lens & 3u) || ((uintptr_t)prefix_lens & 3u) || ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (max_q_len > total_q) return KVB_ERR_INVALID;
+  if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
+  const size_t need = kvb_paged_prefill_q8_workspace_size(batch, pool->num_kv_heads, num_q_heads,
+                                                          pool->head_dim, total_q, max_prefix_len);
+  if (!workspace || workspace_bytes < need) return KVB_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVB_ERR_INVALID;
+  if (max_q_len == 0) return KVB_OK;
+  return launch_status(kvb::launch_prefill_q8(*pool, dtype, q, k_new, v_new, out, cu_q_lens,
+                                              prefix_lens, block_tables, block_table_stride, batch,
+                                              num_q_heads, total_q, max_q_len, max_prefix_len,
+                                              scale, workspace, (hipStream_t)stream));
+}
+
 // Address the device uses for p: itself for device memory, the mapped address for pinned
 // host memory; NULL for memory the device cannot address (e.g. pageable host memory).
 static void* device_address(void* p) {

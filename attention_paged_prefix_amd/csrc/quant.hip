@@ -75,4 +75,107 @@ hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int dtype, const void* kn, c
   return hipGetLastError();
 }
 
+// Prefill over the 8-bit pool.  The prefill kernel stages 16-bit tiles straight from the
+// pool into LDS, so the 8-bit prefix is first widened: each sequence's prefix blocks go,
+// as 16-bit values (K code x channel scale, V code x token scale, rounded to nearest even),
+// into a staging pool in the workspace — staged block b * nbp + j holds logical block j of
+// sequence b — with a block table to match (-1 past the prefix or for an out-of-pool id).
+// The 16-bit prefill then runs on that pool.  Grid (nbp, batch), 256 threads; each thread
+// widens 16-code chunks of the block's K and V.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+dequant_gather_kernel(const uint8_t* __restrict__ kp, const uint8_t* __restrict__ vp,
+                      const float* __restrict__ v_scale, const float* __restrict__ k_scale,
+                      int64_t block_stride, int num_blocks, const int32_t* __restrict__ bt,
+                      int bt_stride, const int32_t* __restrict__ plen, int hkv, int nbp,
+                      uint16_t* __restrict__ sk, uint16_t* __restrict__ sv,
+                      int32_t* __restrict__ stab) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int P = min(max(plen[b], 0), bt_stride * kBlock);
+  const int64_t sidx = (int64_t)b * nbp + j;
+  int pb = -1;
+  if (j < (P + kBlock - 1) / kBlock) {
+    pb = bt[(int64_t)b * bt_stride + j];
+    if (pb < 0 || pb >= num_blocks) pb = -1;
+  }
+  if (threadIdx.x == 0) stab[sidx] = pb >= 0 ? (int32_t)sidx : -1;
+  if (pb < 0) return;
+  const int chunks = hkv * kBlock * D / 16;
+  const uint8_t* kb = kp + (int64_t)pb * block_stride;
+  const uint8_t* vb = vp + (int64_t)pb * block_stride;
+  uint16_t* dk = sk + sidx * ((int64_t)hkv * kBlock * D);
+  uint16_t* dv = sv + sidx * ((int64_t)hkv * kBlock * D);
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const int e0 = c * 16;                              // (h * 16 + row) * D + col
+    const int h = e0 / (kBlock * D);
+    const int row = (e0 - h * kBlock * D) / D;
+    const int col = e0 - (h * kBlock + row) * D;
+    const uint4 kc = *reinterpret_cast<const uint4*>(kb + e0);
+    const uint4 vc = *reinterpret_cast<const uint4*>(vb + e0);
+    const float vs = v_scale[((int64_t)pb * hkv + h) * kBlock + row];
+    const float* ks = k_scale + h * D + col;
+    const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w}, vw[4] = {vc.x, vc.y, vc.z, vc.w};
+    uint32_t ko[8], vo[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t xk = (int32_t)kw[i], xv = (int32_t)vw[i];
+      ko[2 * i] = pack2<T>((float)((xk << 24) >> 24) * ks[4 * i], (float)((xk << 16) >> 24) * ks[4 * i + 1]);
+      ko[2 * i + 1] = pack2<T>((float)((xk << 8) >> 24) * ks[4 * i + 2], (float)(xk >> 24) * ks[4 * i + 3]);
+      vo[2 * i] = pack2<T>((float)((xv << 24) >> 24) * vs, (float)((xv << 16) >> 24) * vs);
+      vo[2 * i + 1] = pack2<T>((float)((xv << 8) >> 24) * vs, (float)(xv >> 24) * vs);
+    }
+    *reinterpret_cast<uint4*>(dk + e0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+    *reinterpret_cast<uint4*>(dk + e0 + 8) = make_uint4(ko[4], ko[5], ko[6], ko[7]);
+    *reinterpret_cast<uint4*>(dv + e0) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+    *reinterpret_cast<uint4*>(dv + e0 + 8) = make_uint4(vo[4], vo[5], vo[6], vo[7]);
+  }
+}
+
+// Workspace of prefill over the 8-bit pool: staged K, staged V, staged block table, then
+// the dispatch plan of the 16-bit prefill (each part 256-byte aligned).
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+static int64_t staged_blocks(int batch, int max_prefix_len) {
+  return (int64_t)batch * std::max(1, (max_prefix_len + kBlock - 1) / kBlock);
+}
+
+int64_t prefill_q8_ws_bytes(int batch, int hkv, int hq, int d, int total_q, int max_prefix_len) {
+  if (batch <= 0 || hkv <= 0 || hq <= 0 || total_q <= 0) return 0;
+  const int64_t nb = staged_blocks(batch, max_prefix_len);
+  const int64_t stage = align256(nb * hkv * kBlock * d * 2);
+  return 2 * stage + align256(nb * 4) + prefill_plan_bytes(batch, hq, total_q);
+}
+
+hipError_t launch_prefill_q8(const kvb_pool_q8& p, int dtype, const void* q, const void* kn,
+                             const void* vn, void* out, const int32_t* cu, const int32_t* plen,
+                             const int32_t* bt, int bt_stride, int batch, int hq, int total_q,
+                             int max_q_len, int max_prefix_len, float scale, void* ws,
+                             hipStream_t s) {
+  const int nbp = std::max(1, (max_prefix_len + kBlock - 1) / kBlock);
+  const int64_t nb = staged_blocks(batch, max_prefix_len);
+  const int64_t stage = align256(nb * p.num_kv_heads * kBlock * p.head_dim * 2);
+  uint8_t* base = (uint8_t*)ws;
+  uint16_t* sk = (uint16_t*)base;
+  uint16_t* sv = (uint16_t*)(base + stage);
+  int32_t* stab = (int32_t*)(base + 2 * stage);
+  void* plan = base + 2 * stage + align256(nb * 4);
+  const dim3 grid((unsigned)nbp, (unsigned)batch);
+#define KVB_DG(TT, DD)                                                                            \
+  hipLaunchKernelGGL((dequant_gather_kernel<TT, DD>), grid, dim3(256), 0, s, (const uint8_t*)p.k,  \
+                     (const uint8_t*)p.v, p.v_scale, p.k_scale, p.block_stride, p.num_blocks, bt,   \
+                     bt_stride, plen, p.num_kv_heads, nbp, sk, sv, stab)
+  const bool bf = dtype == KVB_BF16;
+  switch (p.head_dim) {
+    case 64:  if (bf) KVB_DG(BF16, 64); else KVB_DG(F16, 64); break;
+    case 96:  if (bf) KVB_DG(BF16, 96); else KVB_DG(F16, 96); break;
+    default:  if (bf) KVB_DG(BF16, 128); else KVB_DG(F16, 128); break;
+  }
+#undef KVB_DG
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const kvb_pool staged{sk, sv, (int64_t)p.num_kv_heads * kBlock * p.head_dim, (int32_t)nb, kBlock,
+                        p.num_kv_heads, p.head_dim, dtype};
+  return launch_prefill(staged, q, kn, vn, out, cu, plen, stab, nbp, batch, hq, total_q, max_q_len,
+                        max_prefix_len, scale, plan, s);
+}
+
 }  // namespace kvb

@@ -412,6 +412,10 @@ def main(argv=None):
                           "traffic": read_traffic("paged_decode_decode_workload")}
         res["decode_workload"] = dw
 
+    if args.only == "step" and "prefill" in per_part:
+        res["prefill_q8"] = bench_prefill_q8(torch, kvb, w, k, v, q, kn, vn, cu, pl, bt, max_q, max_p,
+                                             pf, per_part["prefill"], args)
+
     if not args.no_cpu_baseline and args.only == "step":
         res["cpu_baseline"] = cpu_baseline(w)
 
@@ -486,6 +490,44 @@ def bench_copy_blocks(torch, kvb, args):
         res[name] = {"ms": ms, "gbps": moved / (ms * 1e-3) / 1e9}
     res["device_to_device"]["frac_hbm_peak"] = res["device_to_device"]["gbps"] / PEAK_GBPS
     return res
+
+
+def bench_prefill_q8(torch, kvb, w, k, v, q, kn, vn, cu, pl, bt, max_q, max_p, flops, ms16, args):
+    """The step's prefill with the cached prefix in the 8-bit pool: the prefix tokens
+    written by kvb_write_kv_q8 (K scales from their per-channel maxima), then
+    kvb_paged_prefill_q8 (prefix widened into a staging pool, then the 16-bit prefill)."""
+    slot_list = []
+    for b in range(w.batch):
+        j = np.arange(int(w.prefix_lens[b]))
+        slot_list.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    slots = torch.from_numpy(np.unique(np.concatenate(slot_list))).to("cuda:0")
+    kt = k[slots // 16, :, slots % 16, :].contiguous()
+    vt = v[slots // 16, :, slots % 16, :].contiguous()
+    k_scale = (kt.float().abs().amax(dim=0) / 127.0).contiguous()
+    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, k_scale)
+    kvb.write_kv_q8(p8, kt, vt, slots)
+    del kt, vt
+    out = torch.empty_like(q)
+    n = kvb.paged_prefill_q8_workspace_size(w.batch, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                            w.total_q, max_p)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
+
+    def run():
+        kvb.paged_prefill_q8(p8, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out, workspace=ws)
+
+    settle(torch, run, min(args.settle_ms, 200))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    steps = max(args.steps, 10)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"pool": "8-bit codes, per-channel K scales, per-token V scales",
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "ms_16bit_pool": ms16,
+            "time_vs_16bit": ms / ms16}
 
 
 def bench_decode(torch, kvb, args):

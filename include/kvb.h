@@ -230,6 +230,25 @@ kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const voi
                                int32_t max_context_len, int32_t split_blocks, float scale,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged prefill over the 8-bit pool: kvb_paged_prefill with the cached prefix read as the
+ * values its codes stand for (the chunk's own K/V are the call's 16-bit rows).  The
+ * prefix blocks of each sequence are first widened into a 16-bit staging pool inside
+ * the workspace (one staged block per sequence and logical block, shared blocks widened
+ * once per sequence that reads them), then the 16-bit prefill runs on it.  q, k_new,
+ * v_new, out in `dtype`.  workspace: (device, required) at least
+ * kvb_paged_prefill_q8_workspace_size(...) bytes; contents on entry do not matter.
+ * Other arguments as kvb_paged_prefill. */
+kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,
+                                const void* k_new, const void* v_new, void* out,
+                                const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
+                                           int32_t num_q_heads, int32_t head_dim,
+                                           int32_t total_q, int32_t max_prefix_len);
+
 /* Test helper: gather through the block tables into a contiguous layout, bit-exact.
  * For b < batch, j < seq_lens[b]:
  *   k_out[cu_seq_lens[b] + j][h][:] = pool.k[block_tables[b*stride + j/16]][h][j%16][:]

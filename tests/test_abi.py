@@ -211,6 +211,28 @@ def test_q8_validation(lib):
     assert d(pool_q8(), batch=0) == OK
 
 
+def test_prefill_q8_validation(lib):
+    def pq(p, **kw):
+        a = dict(dt=1, q=FAKE, ws=None, wsb=0, stride=4, batch=2, hq=4, total=10, maxq=6, maxp=64)
+        a.update(kw)
+        return lib.kvb_paged_prefill_q8(ctypes.byref(p), a["dt"], a["q"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, a["stride"], a["batch"], a["hq"], a["total"], a["maxq"],
+                                        a["maxp"], 0.1, a["ws"], a["wsb"], None)
+    need = lib.kvb_paged_prefill_q8_workspace_size(2, 2, 4, 128, 10, 64)
+    # two staged pools of 2 x 4 blocks x 2 heads x 16 x 128 x 2 bytes, the table, the plan
+    assert need == 2 * (8 * 2 * 16 * 128 * 2) + 256 + lib.kvb_paged_prefill_workspace_size(2, 4, 128, 10, 64)
+    p = pool_q8()
+    assert pq(p) == WS                                # the staging pool is required
+    assert pq(p, ws=FAKE, wsb=need - 1) == WS
+    assert pq(p, ws=FAKE + 8, wsb=need) == INVALID
+    assert pq(p, ws=FAKE, wsb=need, stride=3) == INVALID
+    assert pq(p, ws=FAKE, wsb=need, hq=3) == INVALID
+    assert pq(p, ws=FAKE, wsb=need, dt=4) == UNSUP
+    assert pq(p, q=None) == NULL
+    assert pq(p, batch=0) == OK
+    assert lib.kvb_paged_prefill_q8_workspace_size(2, 2, 4, 80, 10, 64) == 0
+
+
 def test_prefill_pooled_validation(lib):
     p = pool()
     def pp(**kw):

@@ -179,3 +179,49 @@ def test_decode_q8_full_size_sampled():
     ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q[seqs], w.context_lens[seqs],
                                 w.block_tables[seqs], w.scale, "bf16")
     assert u.max_err(got[seqs], ref, "bf16") <= u.TOL["bf16"]
+
+
+Q8_PREFILL_CASES = [
+    # seed, dtype, Hq, Hkv, d, prefix lengths, chunk lengths, sharing
+    (821, "bf16", 16, 2, 128, [0, 100, 513, 2048], [37, 200, 1, 64], "pairs"),
+    (822, "fp16", 40, 8, 96, [700, 33], [129, 300], "none"),
+    (823, "bf16", 8, 8, 64, [17, 1000, 256], [16, 50, 99], "all"),
+    # several rounds of work-groups: the dispatch plan runs on the staged pool
+    (824, "fp16", 32, 8, 128, [4500, 100, 0, 2047], [512, 480, 300, 511], "pairs"),
+]
+
+
+def _prefix_slots(w):
+    slots = []
+    for b in range(w.batch):
+        j = np.arange(int(w.prefix_lens[b]))
+        slots.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    return np.unique(np.concatenate(slots)) if slots else np.zeros(0, np.int64)
+
+
+@pytest.mark.parametrize("case", Q8_PREFILL_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+def test_prefill_q8_matches_oracle(case):
+    """Prefill with the cached prefix in an 8-bit pool the oracle wrote (unwritten slots
+    poisoned, NaN V scales included), against the oracle's prefill over that pool."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=False)
+    slots = _prefix_slots(w)
+    kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+    ks = quant.channel_scales(oracle_f32(kt, dt)) if len(slots) else np.full((hkv, d), 0.01, np.float32)
+    kc, vc, vs = _poisoned(w.k_pool.shape[0], hkv, d)
+    kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, kt, vt, slots, dt)
+    pool = _pool_q8(kc, vc, vs, ks)
+    mq, mp = int(w.q_lens.max()), int(w.prefix_lens.max())
+    got = u.to_bits(kvb.paged_prefill_q8(pool, u.to_dev(w.q, dt), u.to_dev(w.k_new, dt),
+                                         u.to_dev(w.v_new, dt), u.idev(w.cu_q_lens),
+                                         u.idev(w.prefix_lens), u.idev(w.block_tables), w.scale, mq, mp))
+    torch.cuda.synchronize()
+    import oracle
+    assert np.isfinite(oracle.decode_bits(got, dt)).all()
+    ref = quant.paged_prefill_q8(kc, vc, vs, ks, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens,
+                                 w.block_tables, hq, w.scale, dt)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
