@@ -1,4 +1,4 @@
-"""8-bit K/V pool: quantisation, dequantisation, and decode and prefill over the pool.
+"""8-bit and 4-bit K/V pools: quantisation, dequantisation, and decode and prefill over them.
 
 Test infrastructure only (see the package docstring).  The pages store cached K/V at
 8 bits with per-channel scales for K and per-token scales for V (kvboost 0.6.0,
@@ -14,9 +14,13 @@ axes and nothing else; the readings taken here:
   stored codes never change when tokens are appended;
 * V: one scale per (token, KV head) = max_c |v_c| / 127 (float32), computed when the
   token is written;
-* the value a code stands for is ``code * scale``, exact in float64.
+* the value a code stands for is ``code * scale``, exact in float64;
+* 4 bits (the pages' "kv_cache_bits=4"): the same rules with codes in [-7, 7] and the V
+  scale max |v| / 7; two codes per byte, channel 2i in the low nibble and 2i+1 in the
+  high one, each as a 4-bit two's complement.
 
-Pool arrays: codes int8 ``[num_blocks][num_kv_heads][16][d]``, V scales float32
+Pool arrays: codes int8 ``[num_blocks][num_kv_heads][16][d]`` (unpacked here, also for 4
+bits; ``pack_nibbles`` gives the stored bytes), V scales float32
 ``[num_blocks][num_kv_heads][16]``, K scales float32 ``[num_kv_heads][d]``.
 """
 from __future__ import annotations
@@ -28,38 +32,59 @@ import numpy as np
 from .attention import BLOCK_SIZE, attend, decode_bits, gather_kv
 
 CODE_MAX = 127
+CODE_MAX4 = 7
 
 
-def quantize(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+def quantize(x: np.ndarray, s: np.ndarray, code_max: int = CODE_MAX) -> np.ndarray:
     """int8 codes of float32 values ``x`` at float32 scales ``s`` (broadcast):
-    ``rint(x / s)`` in float32, clamped to [-127, 127]; 0 where s == 0."""
+    ``rint(x / s)`` in float32, clamped to [-code_max, code_max]; 0 where s == 0."""
     x = np.asarray(x, dtype=np.float32)
     s = np.broadcast_to(np.asarray(s, dtype=np.float32), x.shape)
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.rint(np.divide(x, s, dtype=np.float32))
     r = np.where(s == 0, np.float32(0), r)
-    return np.clip(r, -CODE_MAX, CODE_MAX).astype(np.int8)
+    return np.clip(r, -code_max, code_max).astype(np.int8)
 
 
-def token_scale(v: np.ndarray) -> np.ndarray:
-    """Per-token V scale over the last axis: max |v| / 127 in float32."""
+def token_scale(v: np.ndarray, code_max: int = CODE_MAX) -> np.ndarray:
+    """Per-token V scale over the last axis: max |v| / code_max in float32."""
     a = np.abs(np.asarray(v, dtype=np.float32)).max(axis=-1)
-    return np.divide(a, np.float32(CODE_MAX), dtype=np.float32)
+    return np.divide(a, np.float32(code_max), dtype=np.float32)
 
 
-def channel_scales(k_tokens: np.ndarray) -> np.ndarray:
+def channel_scales(k_tokens: np.ndarray, code_max: int = CODE_MAX) -> np.ndarray:
     """A K scale per (KV head, channel) from example tokens ``[n][Hkv][d]`` (float32):
-    max over the tokens of |k| / 127.  One way a caller can pick the pool's K scales."""
+    max over the tokens of |k| / code_max.  One way a caller can pick the pool's K scales."""
     a = np.abs(np.asarray(k_tokens, dtype=np.float32)).max(axis=0)
-    return np.divide(a, np.float32(CODE_MAX), dtype=np.float32)
+    return np.divide(a, np.float32(code_max), dtype=np.float32)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes ``[..][d]`` (int8 in [-7, 7]) as stored bytes ``[..][d/2]``: channel 2i
+    in the low nibble, 2i+1 in the high nibble, each a 4-bit two's complement."""
+    c = np.asarray(codes, dtype=np.int16) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_nibbles``: bytes ``[..][d/2]`` -> int8 codes ``[..][d]``."""
+    b = np.asarray(packed, dtype=np.uint8).astype(np.int16)
+    lo, hi = b & 0xF, b >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
 
 
 def write_kv_q8(k_codes: np.ndarray, v_codes: np.ndarray, v_scales: np.ndarray,
                 k_scale: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, slot_mapping: np.ndarray,
-                dtype: str) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                dtype: str, code_max: int = CODE_MAX) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Quantise each new token and scatter it into its pool slot; negative slots are
     skipped (the slot rule of ``write_kv``: block ``slot // 16``, row ``slot % 16``).
-    ``k_new``/``v_new`` are 16-bit payloads ``[T][Hkv][d]``.  Returns new arrays."""
+    ``k_new``/``v_new`` are 16-bit payloads ``[T][Hkv][d]``.  ``code_max`` 127 (8 bits)
+    or 7 (4 bits; codes kept unpacked).  Returns new arrays."""
     kc = np.array(k_codes, copy=True)
     vc = np.array(v_codes, copy=True)
     vs = np.array(v_scales, copy=True)
@@ -69,10 +94,10 @@ def write_kv_q8(k_codes: np.ndarray, v_codes: np.ndarray, v_scales: np.ndarray,
         if slot < 0:
             continue
         blk, row = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
-        kc[blk, :, row, :] = quantize(kf[t], k_scale)
-        s = token_scale(vf[t])                              # [Hkv]
+        kc[blk, :, row, :] = quantize(kf[t], k_scale, code_max)
+        s = token_scale(vf[t], code_max)                    # [Hkv]
         vs[blk, :, row] = s
-        vc[blk, :, row, :] = quantize(vf[t], s[:, None])
+        vc[blk, :, row, :] = quantize(vf[t], s[:, None], code_max)
     return kc, vc, vs
 
 

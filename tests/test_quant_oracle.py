@@ -172,3 +172,59 @@ def test_prefill_over_exact_pool_equals_plain_prefill(dtype):
     ref = oracle.paged_prefill(K16, V16, q, kn, vn, cu, P, bt, hq, 0.125, dtype)
     got = quant.paged_prefill_q8(Kc, Vc, Vs, k_scale, q, kn, vn, cu, P, bt, hq, 0.125, dtype)
     assert np.array_equal(got, ref)
+
+
+def test_4bit_codes_and_nibbles():
+    """4-bit codes of hand examples (tests/golden/quant_codes.json) and their packing two
+    per byte, even channel in the low nibble."""
+    g = json.load(open(GOLDEN))
+    for case in g["v_tokens_4bit"]:
+        x = np.asarray(case["values"], dtype=np.float32)
+        s = quant.token_scale(x, quant.CODE_MAX4)
+        assert s == np.float32(case["scale"])
+        assert quant.quantize(x, s, quant.CODE_MAX4).tolist() == case["codes"]
+    nb = g["nibbles"]
+    packed = quant.pack_nibbles(np.asarray(nb["codes"], np.int8))
+    assert packed.tolist() == nb["bytes"]
+    assert quant.unpack_nibbles(packed).tolist() == nb["codes"]
+    rng = np.random.default_rng(9)
+    c = rng.integers(-7, 8, size=(5, 3, 64)).astype(np.int8)
+    assert np.array_equal(quant.unpack_nibbles(quant.pack_nibbles(c)), c)
+
+
+def test_4bit_error_bound_and_exact_reduction():
+    """4-bit: |x - s*code| <= s/2, and decode over a 4-bit pool whose values are exactly
+    code x scale equals the 16-bit decode bit for bit."""
+    rng = np.random.default_rng(10)
+    v = rng.standard_normal((100, 2, 64)).astype(np.float32)
+    s = quant.token_scale(v, quant.CODE_MAX4)
+    c = quant.quantize(v, s[..., None], quant.CODE_MAX4)
+    assert np.abs(c).max() == 7
+    assert (np.abs(v.astype(np.float64) - quant.dequant_v(c, s)) <= s.astype(np.float64)[..., None] * (0.5 + 1e-6)).all()
+    nb, hkv, hq, d, dtype = 20, 2, 4, 64, "bf16"
+    ctx = np.array([33, 100, 1], np.int32)
+    n_tok = int(ctx.sum())
+    k_scale = (2.0 ** rng.integers(-4, 0, size=(hkv, d))).astype(np.float32)
+    kc = rng.integers(-7, 8, size=(n_tok, hkv, d))
+    vc = rng.integers(-7, 8, size=(n_tok, hkv, d))
+    vc[np.arange(n_tok)[:, None], np.arange(hkv)[None, :], rng.integers(0, d, size=(n_tok, hkv))] = 7
+    ve = 2.0 ** rng.integers(-6, -2, size=(n_tok, hkv))
+    kb, vb = bits(kc * k_scale.astype(np.float64), dtype), bits(vc * ve[..., None], dtype)
+    perm = rng.permutation(nb)
+    bt = np.full((3, 8), -1, np.int32)
+    slots, used = [], 0
+    for b, n in enumerate(ctx):
+        nblk = (n + 15) // 16
+        bt[b, :nblk] = perm[used:used + nblk]
+        used += nblk
+        slots += [int(bt[b, j // 16]) * 16 + j % 16 for j in range(n)]
+    slots = np.array(slots, np.int64)
+    K16, V16 = oracle.write_kv(np.zeros((nb, hkv, 16, d), np.uint16), np.zeros((nb, hkv, 16, d), np.uint16),
+                               kb, vb, slots)
+    Kc, Vc, Vs = quant.write_kv_q8(np.zeros((nb, hkv, 16, d), np.int8), np.zeros((nb, hkv, 16, d), np.int8),
+                                   np.zeros((nb, hkv, 16), np.float32), k_scale, kb, vb, slots, dtype,
+                                   quant.CODE_MAX4)
+    q = bits(rng.standard_normal((3, hq, d)), dtype)
+    ref = oracle.paged_decode(K16, V16, q, ctx, bt, 0.125, dtype)
+    got = quant.paged_decode_q8(Kc, Vc, Vs, k_scale, q, ctx, bt, 0.125, dtype)
+    assert np.array_equal(got, ref)
