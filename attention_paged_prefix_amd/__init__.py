@@ -25,6 +25,7 @@ from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool, KvbPoolQ8  # noqa: F401
 __all__ = [
     "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_cascade", "copy_blocks",
     "PoolQ8", "write_kv_q8", "paged_decode_q8", "paged_prefill_q8", "paged_prefill_q8_workspace_size",
+    "PoolQ4", "write_kv_q4", "paged_decode_q4", "paged_prefill_q4",
     "gather_kv",
     "paged_prefill_workspace_size", "paged_decode_workspace_size",
     "paged_decode_cascade_workspace_size", "version", "KvbError",
@@ -240,23 +241,29 @@ def copy_blocks(src: Pool, dst: Pool, src_ids: torch.Tensor, dst_ids: torch.Tens
 
 @dataclass
 class PoolQ8:
-    """8-bit K/V pool (kvb_pool_q8): int8 codes ``k``/``v`` ``[num_blocks][num_kv_heads][16]
-    [head_dim]``, per-token V scales ``v_scale`` float32 ``[num_blocks][num_kv_heads][16]``
-    and the pool's per-channel K scales ``k_scale`` float32 ``[num_kv_heads][head_dim]``.
-    A code c stands for c * scale (kvboost 0.6.0, "Optional: KV quantization")."""
+    """Quantised K/V pool (kvb_pool_q8, or kvb_pool_q4 with ``bits=4``): codes ``k``/``v``
+    ``[num_blocks][num_kv_heads][16][head_dim]`` int8 (8 bits) or ``[..][head_dim/2]`` uint8
+    holding two 4-bit codes per byte (even channel in the low nibble), per-token V scales
+    ``v_scale`` float32 ``[num_blocks][num_kv_heads][16]`` and the pool's per-channel K
+    scales ``k_scale`` float32 ``[num_kv_heads][head_dim]``.  A code c stands for c * scale
+    (kvboost 0.6.0, "Optional: KV quantization")."""
     k: torch.Tensor
     v: torch.Tensor
     v_scale: torch.Tensor
     k_scale: torch.Tensor
+    bits: int = 8
 
     @classmethod
     def empty(cls, num_blocks: int, num_kv_heads: int, head_dim: int, k_scale: torch.Tensor,
-              device="cuda") -> "PoolQ8":
-        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
-        return cls(torch.zeros(shape, dtype=torch.int8, device=device),
-                   torch.zeros(shape, dtype=torch.int8, device=device),
+              device="cuda", bits: int = 8) -> "PoolQ8":
+        if bits not in (8, 4):
+            raise ValueError("bits must be 8 or 4")
+        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim * bits // 8)
+        dt = torch.int8 if bits == 8 else torch.uint8
+        return cls(torch.zeros(shape, dtype=dt, device=device),
+                   torch.zeros(shape, dtype=dt, device=device),
                    torch.zeros(shape[:3], dtype=torch.float32, device=device),
-                   k_scale.to(device=device, dtype=torch.float32).contiguous())
+                   k_scale.to(device=device, dtype=torch.float32).contiguous(), bits)
 
     @property
     def num_blocks(self) -> int:
@@ -268,19 +275,30 @@ class PoolQ8:
 
     @property
     def head_dim(self) -> int:
-        return int(self.k.shape[3])
+        return int(self.k.shape[3]) * 8 // self.bits
 
     def c_struct(self) -> KvbPoolQ8:
-        nb, hkv, bs, d = self.k.shape
-        for t, dt in ((self.k, torch.int8), (self.v, torch.int8), (self.v_scale, torch.float32),
+        nb, hkv, bs, row_bytes = self.k.shape
+        d = self.head_dim
+        code_dt = torch.int8 if self.bits == 8 else torch.uint8
+        for t, dt in ((self.k, code_dt), (self.v, code_dt), (self.v_scale, torch.float32),
                       (self.k_scale, torch.float32)):
             if t.dtype != dt or not t.is_contiguous():
-                raise ValueError("PoolQ8 tensors: contiguous int8 codes and float32 scales")
+                raise ValueError("quantised pool tensors: contiguous codes and float32 scales")
         if self.v.shape != self.k.shape or self.v_scale.shape != (nb, hkv, bs) or \
                 self.k_scale.shape != (hkv, d):
-            raise ValueError("PoolQ8 tensor shapes do not match")
+            raise ValueError("quantised pool tensor shapes do not match")
         return KvbPoolQ8(self.k.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(),
-                         self.k_scale.data_ptr(), hkv * bs * d, nb, bs, hkv, d)
+                         self.k_scale.data_ptr(), hkv * bs * row_bytes, nb, bs, hkv, d)
+
+
+def PoolQ4(k: torch.Tensor, v: torch.Tensor, v_scale: torch.Tensor, k_scale: torch.Tensor) -> PoolQ8:
+    """4-bit pool (kvb_pool_q4): ``k``/``v`` uint8 ``[num_blocks][num_kv_heads][16][head_dim/2]``."""
+    return PoolQ8(k, v, v_scale, k_scale, 4)
+
+
+def _qfn(lib, name: str, pool: PoolQ8):
+    return getattr(lib, name.replace("_q8", "_q4") if pool.bits == 4 else name)
 
 
 def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
@@ -291,7 +309,7 @@ def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_map
     if k_new.dtype not in _DT or v_new.dtype != k_new.dtype:
         raise ValueError("k_new/v_new must both be float16 or bfloat16")
     ps = pool.c_struct()
-    _lib.check("kvb_write_kv_q8", lib.kvb_write_kv_q8(
+    _lib.check("kvb_write_kv_q8", _qfn(lib, "kvb_write_kv_q8", pool)(
         ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], _ptr(slot_mapping),
         int(slot_mapping.numel()), _stream(stream)))
 
@@ -310,7 +328,7 @@ def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
     need = paged_decode_workspace_size(B, pool.num_kv_heads, hq, d, max_context_len, split_blocks)
     workspace = _workspace(need, q.device, workspace)
     ps = pool.c_struct()
-    _lib.check("kvb_paged_decode_q8", lib.kvb_paged_decode_q8(
+    _lib.check("kvb_paged_decode_q8", _qfn(lib, "kvb_paged_decode_q8", pool)(
         ctypes.byref(ps), _DT[q.dtype], _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
         int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
@@ -341,9 +359,15 @@ def paged_prefill_q8(pool: PoolQ8, q: torch.Tensor, k_new: torch.Tensor, v_new: 
     need = paged_prefill_q8_workspace_size(batch, pool.num_kv_heads, hq, d, T, max_prefix_len)
     workspace = _workspace(need, q.device, workspace)
     ps = pool.c_struct()
-    _lib.check("kvb_paged_prefill_q8", lib.kvb_paged_prefill_q8(
+    _lib.check("kvb_paged_prefill_q8", _qfn(lib, "kvb_paged_prefill_q8", pool)(
         ctypes.byref(ps), _DT[q.dtype], _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out),
         _ptr(cu_q_lens), _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch,
         hq, T, int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+# The same calls on a 4-bit pool (PoolQ4); the functions above dispatch on ``pool.bits``.
+write_kv_q4 = write_kv_q8
+paged_decode_q4 = paged_decode_q8
+paged_prefill_q4 = paged_prefill_q8

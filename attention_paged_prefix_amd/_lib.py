@@ -34,6 +34,9 @@ EXPORTS = (
     "kvb_paged_decode_q8",
     "kvb_paged_prefill_q8",
     "kvb_paged_prefill_q8_workspace_size",
+    "kvb_write_kv_q4",
+    "kvb_paged_decode_q4",
+    "kvb_paged_prefill_q4",
     "kvb_gather_kv",
     "kvb_status_str",
     "kvb_version",
@@ -125,6 +128,12 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_prefill_q8.restype = ctypes.c_int
     lib.kvb_paged_prefill_q8_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
     lib.kvb_paged_prefill_q8_workspace_size.restype = _sz
+    lib.kvb_write_kv_q4.argtypes = lib.kvb_write_kv_q8.argtypes
+    lib.kvb_write_kv_q4.restype = ctypes.c_int
+    lib.kvb_paged_decode_q4.argtypes = lib.kvb_paged_decode_q8.argtypes
+    lib.kvb_paged_decode_q4.restype = ctypes.c_int
+    lib.kvb_paged_prefill_q4.argtypes = lib.kvb_paged_prefill_q8.argtypes
+    lib.kvb_paged_prefill_q4.restype = ctypes.c_int
     lib.kvb_gather_kv.argtypes = [_PP, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]
     lib.kvb_gather_kv.restype = ctypes.c_int
     lib.kvb_status_str.argtypes = [ctypes.c_int]

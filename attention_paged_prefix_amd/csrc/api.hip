@@ -22,13 +22,13 @@ kvb_status check_pool(const kvb_pool* p) {
   return KVB_OK;
 }
 
-kvb_status check_pool_q8(const kvb_pool_q8* p) {
+kvb_status check_pool_q8(const kvb_pool_q8* p, int bits = 8) {
   if (!p) return KVB_ERR_NULL;
   if (!p->k || !p->v || !p->v_scale || !p->k_scale) return KVB_ERR_NULL;
   if (p->block_size != 16) return KVB_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 96 && p->head_dim != 128) return KVB_ERR_UNSUPPORTED;
   if (p->num_kv_heads <= 0 || p->num_blocks <= 0) return KVB_ERR_INVALID;
-  if (p->block_stride < (int64_t)p->num_kv_heads * 16 * p->head_dim) return KVB_ERR_INVALID;
+  if (p->block_stride < (int64_t)p->num_kv_heads * 16 * p->head_dim * bits / 8) return KVB_ERR_INVALID;
   if (p->block_stride % 16 != 0) return KVB_ERR_INVALID;
   if (p->block_stride > 0x7fffffffLL) return KVB_ERR_INVALID;
   if (!aligned16(p->k) || !aligned16(p->v) || !aligned16(p->v_scale) || !aligned16(p->k_scale))
@@ -250,26 +250,38 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
                                                   (hipStream_t)stream));
 }
 
-kvb_status kvb_write_kv_q8(const kvb_pool_q8* pool, const void* k_new, const void* v_new,
-                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
-                           void* stream) {
-  kvb_status st = check_pool_q8(pool);
+static kvb_status write_kv_quant(const kvb_pool_q8* pool, int bits, const void* k_new,
+                                 const void* v_new, int32_t dtype, const int64_t* slot_mapping,
+                                 int32_t num_tokens, void* stream) {
+  kvb_status st = check_pool_q8(pool, bits);
   if (st != KVB_OK) return st;
   if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
   if (num_tokens < 0) return KVB_ERR_INVALID;
   if (num_tokens == 0) return KVB_OK;
   if (!k_new || !v_new || !slot_mapping) return KVB_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)slot_mapping & 7u)) return KVB_ERR_INVALID;
-  return launch_status(kvb::launch_write_kv_q8(*pool, dtype, k_new, v_new, slot_mapping, num_tokens,
-                                               (hipStream_t)stream));
+  return launch_status(kvb::launch_write_kv_q8(*pool, bits, dtype, k_new, v_new, slot_mapping,
+                                               num_tokens, (hipStream_t)stream));
 }
 
-kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q, void* out,
-                               const int32_t* context_lens, const int32_t* block_tables,
+kvb_status kvb_write_kv_q8(const kvb_pool_q8* pool, const void* k_new, const void* v_new,
+                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* stream) {
+  return write_kv_quant(pool, 8, k_new, v_new, dtype, slot_mapping, num_tokens, stream);
+}
+
+kvb_status kvb_write_kv_q4(const kvb_pool_q4* pool, const void* k_new, const void* v_new,
+                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* stream) {
+  return write_kv_quant(pool, 4, k_new, v_new, dtype, slot_mapping, num_tokens, stream);
+}
+
+static kvb_status decode_quant(const kvb_pool_q8* pool, int bits, int32_t dtype, const void* q,
+                               void* out, const int32_t* context_lens, const int32_t* block_tables,
                                int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
                                int32_t max_context_len, int32_t split_blocks, float scale,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  kvb_status st = check_pool_q8(pool);
+  kvb_status st = check_pool_q8(pool, bits);
   if (st != KVB_OK) return st;
   if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
   if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || split_blocks < 0)
@@ -288,10 +300,30 @@ kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const voi
   const size_t need = (size_t)kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return KVB_ERR_INVALID;
-  return launch_status(kvb::launch_decode_q8(*pool, dtype, q, out, context_lens, block_tables,
+  return launch_status(kvb::launch_decode_q8(*pool, bits, dtype, q, out, context_lens, block_tables,
                                              block_table_stride, batch, num_q_heads,
                                              max_context_len, sb, ns, scale, workspace,
                                              (hipStream_t)stream));
+}
+
+kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q, void* out,
+                               const int32_t* context_lens, const int32_t* block_tables,
+                               int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t split_blocks, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_quant(pool, 8, dtype, q, out, context_lens, block_tables, block_table_stride, batch,
+                      num_q_heads, max_context_len, split_blocks, scale, workspace,
+                      workspace_bytes, stream);
+}
+
+kvb_status kvb_paged_decode_q4(const kvb_pool_q4* pool, int32_t dtype, const void* q, void* out,
+                               const int32_t* context_lens, const int32_t* block_tables,
+                               int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t split_blocks, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_quant(pool, 4, dtype, q, out, context_lens, block_tables, block_table_stride, batch,
+                      num_q_heads, max_context_len, split_blocks, scale, workspace,
+                      workspace_bytes, stream);
 }
 
 size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
@@ -304,14 +336,14 @@ size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
                                           max_prefix_len);
 }
 
-kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,
+static kvb_status prefill_quant(const kvb_pool_q8* pool, int bits, int32_t dtype, const void* q,
                                 const void* k_new, const void* v_new, void* out,
                                 const int32_t* cu_q_lens, const int32_t* prefix_lens,
                                 const int32_t* block_tables, int32_t block_table_stride,
                                 int32_t batch, int32_t num_q_heads, int32_t total_q,
                                 int32_t max_q_len, int32_t max_prefix_len, float scale,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  kvb_status st = check_pool_q8(pool);
+  kvb_status st = check_pool_q8(pool, bits);
   if (st != KVB_OK) return st;
   if (dtype != KVB_FP16 && dtype != KVB_BF16) return KVB_ERR_UNSUPPORTED;
   if (batch < 0 || total_q < 0 || max_q_len < 0 || max_prefix_len < 0 || num_q_heads <= 0)
@@ -331,10 +363,34 @@ kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const vo
   if (!workspace || workspace_bytes < need) return KVB_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVB_ERR_INVALID;
   if (max_q_len == 0) return KVB_OK;
-  return launch_status(kvb::launch_prefill_q8(*pool, dtype, q, k_new, v_new, out, cu_q_lens,
+  return launch_status(kvb::launch_prefill_q8(*pool, bits, dtype, q, k_new, v_new, out, cu_q_lens,
                                               prefix_lens, block_tables, block_table_stride, batch,
                                               num_q_heads, total_q, max_q_len, max_prefix_len,
                                               scale, workspace, (hipStream_t)stream));
+}
+
+kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,
+                                const void* k_new, const void* v_new, void* out,
+                                const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_quant(pool, 8, dtype, q, k_new, v_new, out, cu_q_lens, prefix_lens, block_tables,
+                       block_table_stride, batch, num_q_heads, total_q, max_q_len, max_prefix_len,
+                       scale, workspace, workspace_bytes, stream);
+}
+
+kvb_status kvb_paged_prefill_q4(const kvb_pool_q4* pool, int32_t dtype, const void* q,
+                                const void* k_new, const void* v_new, void* out,
+                                const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_quant(pool, 4, dtype, q, k_new, v_new, out, cu_q_lens, prefix_lens, block_tables,
+                       block_table_stride, batch, num_q_heads, total_q, max_q_len, max_prefix_len,
+                       scale, workspace, workspace_bytes, stream);
 }
 
 // Address the device uses for p: itself for device memory, the mapped address for pinned

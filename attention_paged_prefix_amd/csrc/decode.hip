@@ -46,13 +46,13 @@ template <int D> struct DecStep {
   int pos[2];                               // position of each block's first key
 };
 
-// The 8-bit pool's step: 16 codes per 16-byte chunk, so a block's K (or V) is D chunks,
-// (D + 63) / 64 per lane; plus the V scales of the lane's four keys of each block.
-// The 8-bit pool's step: 16 codes per 16-byte chunk, so a block's K (or V) is D chunks,
-// (D + 63) / 64 per lane; vsc holds the V scale of the key row each of the lane's V
-// chunks belongs to.
-template <int D> struct DecStepQ8 {
-  static constexpr int NCH = (D + 63) / 64;
+// A quantised pool's step (QB bits per code): a 16-byte chunk holds 128/QB codes of one
+// key row, a block's K (or V) is CH = D*QB/8 chunks, NCH per lane; vsc holds the V scale
+// of the key row each of the lane's V chunks belongs to.
+template <int D, int QB> struct DecStepQ {
+  static constexpr int CH = D * QB / 8;          // chunks per block (K or V)
+  static constexpr int CPRQ = D * QB / 128;      // chunks per key row
+  static constexpr int NCH = (CH + 63) / 64;
   uint4 k[2][NCH];
   uint4 v[2][NCH];
   float vsc[2][NCH];
@@ -84,6 +84,23 @@ __device__ inline void codes_to(uint4 c, float s, uint4& lo, uint4& hi) {
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// 32 4-bit codes (two per byte, the even channel in the low nibble, 4-bit two's
+// complement) -> 32 values code * s of T in four 16-byte quarters (s = 1: exact).
+template <typename T>
+__device__ inline void nibbles_to(uint4 c, float s, uint4 (&o4)[4]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t x = (int32_t)w[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[4 * i + k] = pack2<T>((float)((x << (28 - 8 * k)) >> 28) * s, (float)((x << (24 - 8 * k)) >> 28) * s);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o4[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+}
+
 // Shared-prefix part of a grouped cascade decode (ignored by the plain form).  A group
 // work-group fills its 16 query columns with `cols` heads of each of `seqs` sequences,
 // so every shared block it reads serves all of them.
@@ -105,7 +122,7 @@ __device__ inline int se_period(int nsplit) {
   return (nsplit & 3) == 0 ? 1 : (nsplit & 1) ? 4 : 2;
 }
 
-template <typename T, int D, bool GROUP, bool Q8>
+template <typename T, int D, bool GROUP, int QB>
 __global__ void __launch_bounds__(kDecThreads, 2)
 decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                     int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -115,8 +132,10 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
                     float* __restrict__ ws_o, float* __restrict__ ws_ml, int padded, int real,
                     int blk_first, int slot0, int ws_slots, int force_partial, DecGroup grp,
                     DecQ8 q8) {
-  static_assert(!(GROUP && Q8), "the 8-bit pool has the plain form only");
-  using Step = std::conditional_t<Q8, DecStepQ8<D>, DecStep<D>>;
+  constexpr bool Q8 = QB != 0;              // a quantised pool (8 or 4 bits per code)
+  static_assert(!(GROUP && Q8), "quantised pools have the plain form only");
+  using QStep = DecStepQ<D, (QB ? QB : 8)>;
+  using Step = std::conditional_t<Q8, QStep, DecStep<D>>;
   constexpr int NKK = D / 32;
   constexpr int NDB = D / 16;               // 16-row d blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -285,22 +304,23 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       R.pos[hb] = blk * kBlock;
       const int64_t off = (int64_t)(pb >= 0 ? pb : 0) * block_stride + head_off;
       if constexpr (Q8) {
-        // codes: one byte per element, so the same offsets count bytes
-        const uint8_t* kb = reinterpret_cast<const uint8_t*>(kp) + off;
-        const uint8_t* vb = reinterpret_cast<const uint8_t*>(vp) + off;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)(rows * D));
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)(rows * D));
+        // codes: D*QB/8 bytes per key row; block_stride counts bytes
+        const int64_t qoff = (int64_t)(pb >= 0 ? pb : 0) * block_stride + (int64_t)kvh * kBlock * D * QB / 8;
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(kp) + qoff;
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(vp) + qoff;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)(rows * D * QB / 8));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)(rows * D * QB / 8));
 #pragma unroll
-        for (int j = 0; j < DecStepQ8<D>::NCH; ++j) {
+        for (int j = 0; j < QStep::NCH; ++j) {
           R.k[hb][j] = buf_load16(rk, (uint32_t)(j * 64 + lane) * 16);
           R.v[hb][j] = buf_load16(rv, (uint32_t)(j * 64 + lane) * 16);
         }
         const float* sb = q8.v_scale + ((int64_t)(pb >= 0 ? pb : 0) * hkv + kvh) * kBlock;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(sb, (uint32_t)(rows * 4));
 #pragma unroll
-        for (int j = 0; j < DecStepQ8<D>::NCH; ++j)        // chunk j*64+lane: key row / (D/16)
+        for (int j = 0; j < QStep::NCH; ++j)           // chunk j*64+lane: key row chunk / CPRQ
           R.vsc[hb][j] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) / (D / 16) * 4, 0, 0));
+              float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) / QStep::CPRQ * 4, 0, 0));
         continue;
       }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
@@ -316,23 +336,35 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   auto step = [&](const Step& R) {
     // V of both blocks into this wave's LDS slot, natural [key][d] layout (rows past
     // the context arrive as zeros, so NaN left in unused pool slots never reaches PV).
-    // 8-bit codes are widened to T on the way (chunk c: row c / (D/16), 16 columns), V
+    // Codes are widened to T on the way (chunk c: key row c / CPRQ, 128/QB columns), V
     // codes multiplied by their key's V scale there (dequantised in the LDS stage).
     if constexpr (Q8) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int j = 0; j < DecStepQ8<D>::NCH; ++j) {
+        for (int j = 0; j < QStep::NCH; ++j) {
           const int c = j * 64 + lane;
-          if (c >= D) continue;                   // d = 96: the second chunk of half the lanes
-          const int row = c / (D / 16), col = c - row * (D / 16);
-          uint4 lo, hi;
-          codes_to<T>(R.v[hb][j], R.vsc[hb][j], lo, hi);
-          *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16) = lo;
-          *reinterpret_cast<uint4*>(slot + (hb * 16 + row) * VROW + col * 16 + 8) = hi;
-          codes_to<T>(R.k[hb][j], 1.f, lo, hi);
-          *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16) = lo;
-          *reinterpret_cast<uint4*>(kslot + (hb * 16 + row) * KROW + col * 16 + 8) = hi;
+          if (c >= QStep::CH) continue;           // chunks past the block (some lanes)
+          const int row = c / QStep::CPRQ, col = (c - row * QStep::CPRQ) * (128 / QB);
+          uint16_t* vrow = slot + (hb * 16 + row) * VROW + col;
+          uint16_t* krow = kslot + (hb * 16 + row) * KROW + col;
+          if constexpr (QB == 8) {
+            uint4 lo, hi;
+            codes_to<T>(R.v[hb][j], R.vsc[hb][j], lo, hi);
+            *reinterpret_cast<uint4*>(vrow) = lo;
+            *reinterpret_cast<uint4*>(vrow + 8) = hi;
+            codes_to<T>(R.k[hb][j], 1.f, lo, hi);
+            *reinterpret_cast<uint4*>(krow) = lo;
+            *reinterpret_cast<uint4*>(krow + 8) = hi;
+          } else {
+            uint4 o4[4];
+            nibbles_to<T>(R.v[hb][j], R.vsc[hb][j], o4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vrow + 8 * i) = o4[i];
+            nibbles_to<T>(R.k[hb][j], 1.f, o4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(krow + 8 * i) = o4[i];
+          }
         }
     } else
 #pragma unroll
@@ -598,7 +630,7 @@ void decode_plan(int batch, int hkv, int hq, int max_ctx, int split_blocks_req, 
   *nsplit = (max_blocks + sb - 1) / sb;
 }
 
-template <typename T, int D, bool Q8 = false>
+template <typename T, int D, int QB = 0>
 static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, const int32_t* ctx,
                                   const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx,
                                   int sb, int ns, float scale, float* ws_o, float* ws_ml,
@@ -609,7 +641,7 @@ static hipError_t launch_decode_t(const kvb_pool& p, const void* q, void* out, c
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
   const float c = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, false, Q8>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, false, QB>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                      (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                      (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                      nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, 0, 0, ns, 0,
@@ -638,7 +670,7 @@ static hipError_t launch_decode_private_t(const kvb_pool& p, const void* q, void
   if (real > 0) {
     const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, false, 0>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                        nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
@@ -728,7 +760,7 @@ static hipError_t launch_decode_grouped_t(const kvb_pool& p, const void* q, void
   if (real > 0) {
     const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
     const float c = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true, 0>), dim3((unsigned)padded), dim3(kDecThreads), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (uint16_t*)out, ctx, bt, bt_stride, hq, p.num_kv_heads,
                        nchunks, sb, ns, max_ctx, c, ws_o, ws_ml, (int)padded, (int)real, blk_first,
@@ -778,10 +810,10 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
   }
 }
 
-// Decode over the 8-bit pool: the split kernel's Q8 form (codes widened in the LDS
-// stage, K scales folded into the queries, V scales into the probabilities), then the
-// same merge.  The workspace layout is the 16-bit decode's.
-hipError_t launch_decode_q8(const kvb_pool_q8& p8, int dtype, const void* q, void* out,
+// Decode over a quantised pool (8 or 4 bits per code): the split kernel's quantised form
+// (codes widened in the LDS stage, V codes times their key's scale there, K scales folded
+// into the queries), then the same merge.  The workspace layout is the 16-bit decode's.
+hipError_t launch_decode_q8(const kvb_pool_q8& p8, int bits, int dtype, const void* q, void* out,
                             const int32_t* ctx, const int32_t* bt, int bt_stride, int batch, int hq,
                             int max_ctx, int sb, int ns, float scale, void* ws, hipStream_t s) {
   const kvb_pool p{p8.k, p8.v, p8.block_stride, p8.num_blocks, kBlock, p8.num_kv_heads,
@@ -790,14 +822,17 @@ hipError_t launch_decode_q8(const kvb_pool_q8& p8, int dtype, const void* q, voi
   float* ws_o = (float*)ws;
   float* ws_ml = ws_o + decode_ws_o_floats(batch, hq, p.head_dim, ns);
   const bool bf = dtype == KVB_BF16;
-#define KVB_DQ8(TT, DD) launch_decode_t<TT, DD, true>(p, q, out, ctx, bt, bt_stride, batch, hq, \
+#define KVB_DQ(TT, DD, QQ) launch_decode_t<TT, DD, QQ>(p, q, out, ctx, bt, bt_stride, batch, hq, \
     max_ctx, sb, ns, scale, ws_o, ws_ml, s, q8)
+#define KVB_DQB(DD) (bits == 4 ? (bf ? KVB_DQ(BF16, DD, 4) : KVB_DQ(F16, DD, 4)) \
+                               : (bf ? KVB_DQ(BF16, DD, 8) : KVB_DQ(F16, DD, 8)))
   switch (p.head_dim) {
-    case 64:  return bf ? KVB_DQ8(BF16, 64) : KVB_DQ8(F16, 64);
-    case 96:  return bf ? KVB_DQ8(BF16, 96) : KVB_DQ8(F16, 96);
-    default:  return bf ? KVB_DQ8(BF16, 128) : KVB_DQ8(F16, 128);
+    case 64:  return KVB_DQB(64);
+    case 96:  return KVB_DQB(96);
+    default:  return KVB_DQB(128);
   }
-#undef KVB_DQ8
+#undef KVB_DQB
+#undef KVB_DQ
 }
 
 }  // namespace kvb

@@ -43,16 +43,17 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
                          const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
                          int ns, float scale, void* ws, hipStream_t s);
 
-// 8-bit pool: quantising slot scatter and decode (workspace as launch_decode's).
-hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int dtype, const void* kn, const void* vn,
-                              const int64_t* slots, int num_tokens, hipStream_t s);
-hipError_t launch_decode_q8(const kvb_pool_q8& p, int dtype, const void* q, void* out,
+// Quantised pools (bits = 8 or 4 per code; the 4-bit pool uses the same descriptor):
+// quantising slot scatter and decode (workspace as launch_decode's).
+hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int bits, int dtype, const void* kn,
+                              const void* vn, const int64_t* slots, int num_tokens, hipStream_t s);
+hipError_t launch_decode_q8(const kvb_pool_q8& p, int bits, int dtype, const void* q, void* out,
                             const int32_t* ctx, const int32_t* bt, int bt_stride, int batch, int hq,
                             int max_ctx, int sb, int ns, float scale, void* ws, hipStream_t s);
 // Prefill over the 8-bit pool: prefix blocks widened into a staging pool in the
 // workspace (prefill_q8_ws_bytes), then the 16-bit prefill.
 int64_t prefill_q8_ws_bytes(int batch, int hkv, int hq, int d, int total_q, int max_prefix_len);
-hipError_t launch_prefill_q8(const kvb_pool_q8& p, int dtype, const void* q, const void* kn,
+hipError_t launch_prefill_q8(const kvb_pool_q8& p, int bits, int dtype, const void* q, const void* kn,
                              const void* vn, void* out, const int32_t* cu, const int32_t* plen,
                              const int32_t* bt, int bt_stride, int batch, int hq, int total_q,
                              int max_q_len, int max_prefix_len, float scale, void* ws,

@@ -67,11 +67,11 @@ def decode_bytes(w, ctx, tables) -> float:
     return float(kv + qo + tab)
 
 
-def decode_bytes_q8(w, ctx, tables) -> float:
-    """Algorithmic bytes of decode over the 8-bit pool: one byte per K and V element plus
-    a float32 V scale per (token, KV head)."""
+def decode_bytes_q8(w, ctx, tables, bits: int = 8) -> float:
+    """Algorithmic bytes of decode over a quantised pool: bits/8 bytes per K and V element
+    plus a float32 V scale per (token, KV head)."""
     B = len(ctx)
-    kv = unique_kv_tokens(tables, ctx) * w.num_kv_heads * (2 * w.head_dim + 4)
+    kv = unique_kv_tokens(tables, ctx) * w.num_kv_heads * (2 * w.head_dim * bits // 8 + 4)
     qo = 2 * B * w.num_q_heads * w.head_dim * ESZ
     tab = sum((int(n) + 15) // 16 for n in ctx) * 4 + B * 4
     return float(kv + qo + tab)
@@ -575,25 +575,34 @@ def bench_decode(torch, kvb, args):
     slots = torch.from_numpy(np.unique(np.concatenate(slot_list))).to("cuda:0")
     kt = k[slots // 16, :, slots % 16, :].contiguous()
     vt = v[slots // 16, :, slots % 16, :].contiguous()
-    k_scale = (kt.float().abs().amax(dim=0) / 127.0).contiguous()
-    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, k_scale)
+    amax = kt.float().abs().amax(dim=0)
+    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, (amax / 127.0).contiguous())
     kvb.write_kv_q8(p8, kt, vt, slots)
-    del kt, vt
+    p4 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, (amax / 7.0).contiguous(),
+                          bits=4)
+    kvb.write_kv_q4(p4, kt, vt, slots)
+    del kt, vt, amax
 
     def run_q8():
         kvb.paged_decode_q8(p8, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
 
-    settle(torch, lambda: (run(), run_cascade(), run_q8()), args.settle_ms)
+    def run_q4():
+        kvb.paged_decode_q4(p4, q, ctx, bt, w.scale, max_ctx, split_blocks=sb, out=out, workspace=ws)
+
+    settle(torch, lambda: (run(), run_cascade(), run_q8(), run_q4()), args.settle_ms)
     for _ in range(args.warmup):
         run()
         run_cascade()
         run_q8()
+        run_q4()
     torch.cuda.synchronize()
     steps = max(args.steps, 10)
     tw, tc = _time_warm_cold(torch, run, steps, flush)
     cw, cc = _time_warm_cold(torch, run_cascade, steps, flush)
     qw, qc = _time_warm_cold(torch, run_q8, steps, flush)
+    q4w, q4c = _time_warm_cold(torch, run_q4, steps, flush)
     by8 = decode_bytes_q8(w, w.context_lens, w.block_tables)
+    by4 = decode_bytes_q8(w, w.context_lens, w.block_tables, 4)
     by = decode_bytes(w, w.context_lens, w.block_tables)
     logical = float(np.sum(w.context_lens)) * w.num_kv_heads * w.head_dim * 2 * ESZ
     return {"workload": "paged decode, 64 sequences, contexts 512..4096, first 1024 tokens shared",
@@ -610,7 +619,12 @@ def bench_decode(torch, kvb, args):
                    "algorithmic_bytes": by8, "ms_back_to_back": qw, "ms_cold_cache": qc,
                    "gbps_cold_cache": by8 / (qc * 1e-3) / 1e9,
                    "frac_hbm_peak_cold": by8 / (qc * 1e-3) / 1e9 / PEAK_GBPS,
-                   "speedup_vs_16bit_cold": tc / qc}}
+                   "speedup_vs_16bit_cold": tc / qc},
+            "q4": {"pool": "4-bit codes (two per byte), per-channel K scales, per-token V scales",
+                   "algorithmic_bytes": by4, "ms_back_to_back": q4w, "ms_cold_cache": q4c,
+                   "gbps_cold_cache": by4 / (q4c * 1e-3) / 1e9,
+                   "frac_hbm_peak_cold": by4 / (q4c * 1e-3) / 1e9 / PEAK_GBPS,
+                   "speedup_vs_16bit_cold": tc / q4c}}
 
 
 if __name__ == "__main__":

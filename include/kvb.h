@@ -249,6 +249,34 @@ size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
                                            int32_t num_q_heads, int32_t head_dim,
                                            int32_t total_q, int32_t max_prefix_len);
 
+/* 4-bit K/V pool (kvboost 0.6.0, "Optional: KV quantization": kv_cache_bits=4).  The
+ * 8-bit pool's rules with codes in [-7, 7] (V scale max |v| / 7; K scales chosen by the
+ * caller, for instance max |k| / 7) and two codes per byte: channel 2i in the low nibble,
+ * 2i+1 in the high nibble, each a 4-bit two's complement.  The fields are kvb_pool_q8's,
+ * with k and v (device) holding code bytes (block, kv_head, row, e/2) at
+ *   block*block_stride + ((kv_head*16 + row)*head_dim + e)/2
+ * and block_stride (bytes) >= num_kv_heads*16*head_dim/2, a multiple of 16. */
+typedef kvb_pool_q8 kvb_pool_q4;
+
+/* As kvb_write_kv_q8, kvb_paged_decode_q8 and kvb_paged_prefill_q8 for the 4-bit pool
+ * (decode: the same workspace as kvb_paged_decode; prefill:
+ * kvb_paged_prefill_q8_workspace_size(...) bytes). */
+kvb_status kvb_write_kv_q4(const kvb_pool_q4* pool, const void* k_new, const void* v_new,
+                           int32_t dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* stream);
+kvb_status kvb_paged_decode_q4(const kvb_pool_q4* pool, int32_t dtype, const void* q, void* out,
+                               const int32_t* context_lens, const int32_t* block_tables,
+                               int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, int32_t split_blocks, float scale,
+                               void* workspace, size_t workspace_bytes, void* stream);
+kvb_status kvb_paged_prefill_q4(const kvb_pool_q4* pool, int32_t dtype, const void* q,
+                                const void* k_new, const void* v_new, void* out,
+                                const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                const int32_t* block_tables, int32_t block_table_stride,
+                                int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Test helper: gather through the block tables into a contiguous layout, bit-exact.
  * For b < batch, j < seq_lens[b]:
  *   k_out[cu_seq_lens[b] + j][h][:] = pool.k[block_tables[b*stride + j/16]][h][j%16][:]

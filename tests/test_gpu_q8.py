@@ -225,3 +225,117 @@ def test_prefill_q8_matches_oracle(case):
                                  w.block_tables, hq, w.scale, dt)
     err = u.max_err(got, ref, dt)
     assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+# ------------------------------------------------------------------ 4-bit pool
+
+def _pool_q4(kc, vc, vs, ks):
+    """Upload the oracle's (unpacked) 4-bit codes as stored bytes."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    dev = "cuda:0"
+    return kvb.PoolQ4(torch.from_numpy(np.ascontiguousarray(quant.pack_nibbles(kc))).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(quant.pack_nibbles(vc))).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(vs)).to(dev),
+                      torch.from_numpy(np.ascontiguousarray(ks)).to(dev))
+
+
+def _poisoned4(nb, hkv, d):
+    return (np.full((nb, hkv, 16, d), 7, np.int8), np.full((nb, hkv, 16, d), -7, np.int8),
+            np.full((nb, hkv, 16), np.nan, np.float32))
+
+
+@pytest.mark.parametrize("dt,d,hkv", [("bf16", 128, 8), ("fp16", 96, 2), ("bf16", 64, 1)])
+def test_write_kv_q4_bit_exact(dt, d, hkv):
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    rng = np.random.default_rng(831 + d)
+    nb, T = 12, 150
+    mag = rng.uniform(0.05, 20.0, size=(T, hkv, 1))
+    kb = round_to_bits(rng.standard_normal((T, hkv, d)) * mag, dt)
+    V = rng.standard_normal((T, hkv, d)) * mag
+    V[9] = 0.0
+    vb = round_to_bits(V, dt)
+    ks = quant.channel_scales(oracle_f32(kb, dt), quant.CODE_MAX4) * np.float32(0.7)
+    ks[0, 5] = 0.0
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[[3, 40]] = -1
+    kc0 = rng.integers(-7, 8, size=(nb, hkv, 16, d)).astype(np.int8)
+    vc0 = rng.integers(-7, 8, size=(nb, hkv, 16, d)).astype(np.int8)
+    vs0 = rng.uniform(0, 1, size=(nb, hkv, 16)).astype(np.float32)
+    ref = quant.write_kv_q8(kc0, vc0, vs0, ks, kb, vb, slots, dt, quant.CODE_MAX4)
+    pool = _pool_q4(kc0, vc0, vs0, ks)
+    kvb.write_kv_q4(pool, u.to_dev(kb, dt), u.to_dev(vb, dt), u.idev(slots, torch.int64))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.k.cpu().numpy(), quant.pack_nibbles(ref[0]))
+    assert np.array_equal(pool.v.cpu().numpy(), quant.pack_nibbles(ref[1]))
+    assert np.array_equal(pool.v_scale.cpu().numpy().view(np.uint32), ref[2].view(np.uint32))
+
+
+def _oracle_q4_pool(w, slots):
+    from oracle import quant
+    kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+    ks = quant.channel_scales(oracle_f32(kt, w.dtype), quant.CODE_MAX4) if len(slots) \
+        else np.full((w.num_kv_heads, w.head_dim), 0.1, np.float32)
+    kc, vc, vs = _poisoned4(w.k_pool.shape[0], w.num_kv_heads, w.head_dim)
+    kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, kt, vt, slots, w.dtype, quant.CODE_MAX4)
+    return kc, vc, vs, ks, kt, vt
+
+
+@pytest.mark.parametrize("case", Q8_DECODE_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+@pytest.mark.parametrize("split", [0, 3])
+def test_decode_q4_matches_oracle(case, split):
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    seed, dt, hq, hkv, d, ctx = case
+    w = make_custom(seed, dt, hq, hkv, d, ctx, kind="decode", share="all", poison=False)
+    kc, vc, vs, ks, _, _ = _oracle_q4_pool(w, _context_slots(w))
+    pool = _pool_q4(kc, vc, vs, ks)
+    got = u.to_bits(kvb.paged_decode_q4(pool, u.to_dev(w.q, dt), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(max(ctx)),
+                                        split_blocks=split))
+    torch.cuda.synchronize()
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, dt)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("case", Q8_PREFILL_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
+def test_prefill_q4_matches_oracle(case):
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=False)
+    kc, vc, vs, ks, _, _ = _oracle_q4_pool(w, _prefix_slots(w))
+    pool = _pool_q4(kc, vc, vs, ks)
+    got = u.to_bits(kvb.paged_prefill_q4(pool, u.to_dev(w.q, dt), u.to_dev(w.k_new, dt),
+                                         u.to_dev(w.v_new, dt), u.idev(w.cu_q_lens),
+                                         u.idev(w.prefix_lens), u.idev(w.block_tables), w.scale,
+                                         int(w.q_lens.max()), int(w.prefix_lens.max())))
+    torch.cuda.synchronize()
+    ref = quant.paged_prefill_q8(kc, vc, vs, ks, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens,
+                                 w.block_tables, hq, w.scale, dt)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
+def test_write_then_decode_q4_end_to_end():
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    w = make_custom(835, "fp16", 32, 8, 128, [700, 2049, 16, 1333], kind="decode", share="pairs",
+                    poison=False)
+    slots = _context_slots(w)
+    kc, vc, vs, ks, kt, vt = _oracle_q4_pool(w, slots)
+    pk, pv, ps = _poisoned4(w.k_pool.shape[0], 8, 128)
+    pool = _pool_q4(pk, pv, ps, ks)
+    kvb.write_kv_q4(pool, u.to_dev(kt, "fp16"), u.to_dev(vt, "fp16"), u.idev(slots, torch.int64))
+    got = u.to_bits(kvb.paged_decode_q4(pool, u.to_dev(w.q, "fp16"), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(w.context_lens.max())))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.k.cpu().numpy(), quant.pack_nibbles(kc))
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, "fp16")
+    assert u.max_err(got, ref, "fp16") <= u.TOL["fp16"]
