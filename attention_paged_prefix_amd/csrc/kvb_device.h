@@ -74,6 +74,7 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Two fp32 values rounded (nearest even) into one packed 16-bit pair (v_cvt_pk_*_f32).
 template <typename T> __device__ inline uint32_t pack2(float a, float b);

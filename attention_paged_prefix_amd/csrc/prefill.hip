@@ -226,16 +226,24 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // that block; lane L's chunk holds row (64m+L)/CPR, logical chunk inv(row, (64m+L)%CPR).
   // Byte offset = row * (source row pitch) + column bytes; the pitch is D*2 in the pool
   // and hkv*D*2 in the chunk's own K/V.
+  // ld_offK/V[m]: the byte offset for a pool block (row pitch D*2); a source with another
+  // pitch adds row * (pitch - D*2).  The row of instruction m is ld_row0 + m * 64/CPR
+  // where CPR divides 64 (head dims 64, 128), else kept per instruction.
   const int ld_blk = w & (kRowWaves - 1);
-  uint32_t ld_row[NLD], ld_colK[NLD], ld_colV[NLD];
+  constexpr bool kRowAffine = 64 % CPR == 0;
+  uint32_t ld_offK[NLD], ld_offV[NLD], ld_rows[kRowAffine ? 1 : NLD];
 #pragma unroll
   for (int m = 0; m < NLD; ++m) {
     const int pos = 64 * m + lane;
     const int rb = pos / CPR, cp = pos - (pos / CPR) * CPR;
-    ld_row[m] = (uint32_t)rb;
-    ld_colK[m] = (uint32_t)L::invK(rb, cp) * 16;
-    ld_colV[m] = (uint32_t)L::invV(rb, cp) * 16;
+    if (!kRowAffine || m == 0) ld_rows[m] = (uint32_t)rb;
+    ld_offK[m] = (uint32_t)rb * (uint32_t)(D * 2) + (uint32_t)L::invK(rb, cp) * 16;
+    ld_offV[m] = (uint32_t)rb * (uint32_t)(D * 2) + (uint32_t)L::invV(rb, cp) * 16;
   }
+  auto ld_row = [&](int m) -> uint32_t {
+    if constexpr (kRowAffine) return ld_rows[0] + (uint32_t)(m * (64 / CPR));
+    else return ld_rows[m];
+  };
   const uint32_t ld_dst = part_base + (uint32_t)(kBlock * ld_blk * CPR * 16);
   const int32_t* bt_row = bt + (int64_t)b * bt_stride;
   const int64_t head_off = (int64_t)kvh * kBlock * D;
@@ -288,7 +296,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   };
   struct LdDesc {
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t pitch;
+    uint32_t dpitch;                                // row pitch - D*2 (bytes)
     uint32_t dst;                                   // LDS byte address of the block
   };
   auto desc = [&](int li, bool is_v, uint32_t buf_off) -> LdDesc {
@@ -297,18 +305,23 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int nb = __builtin_amdgcn_readlane((int)t_nb, li);
     LdDesc d;
     d.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, nb, kBufDword3);
-    d.pitch = ((pre_bits >> li) & 1) ? (uint32_t)(D * 2) : self_row_bytes;
+    d.dpitch = ((pre_bits >> li) & 1) ? 0u : self_row_bytes - (uint32_t)(D * 2);
     d.dst = ld_dst + buf_off;
     return d;
   };
-  // load instruction m (1 KiB) of a part
-  auto issue = [&](const LdDesc& d, const uint32_t* col, int m) {
-    buf_load16_lds(d.rs, ld_row[m] * d.pitch + col[m], lds + d.dst + 64 * 16 * m);
+  // load instruction m (1 KiB) of a part; `pre` (compile-time): the tile is known to be
+  // a prefix tile, whose offsets are precomputed
+  auto issue = [&](const LdDesc& d, bool is_v, int m, auto pre_c) {
+    const uint32_t base = is_v ? ld_offV[m] : ld_offK[m];
+    const uint32_t off = decltype(pre_c)::value ? base : base + ld_row(m) * d.dpitch;
+    buf_load16_lds(d.rs, off, lds + d.dst + 64 * 16 * m);
   };
-  auto issue_all = [&](const LdDesc& d, const uint32_t* col) {
+  auto issue_all = [&](const LdDesc& d, bool is_v, auto pre_c) {
 #pragma unroll
-    for (int m = 0; m < NLD; ++m) issue(d, col, m);
+    for (int m = 0; m < NLD; ++m) issue(d, is_v, m, pre_c);
   };
+  using Gen = std::false_type;
+  using Pre = std::true_type;
 
   // ---- per-lane LDS read addresses (bytes, including this key part's base)
   // K operand: row 32*half + lr, logical chunk 2*kk + hf
@@ -371,23 +384,23 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 #pragma unroll
     for (int kp4 = 0; kp4 < 4; ++kp4) {
       const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
-      uint32_t pw[4];
+      u32x4 pw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pw[e] = pack2<T>(fast_exp2(x[mb][r0 + 2 * e]), fast_exp2(x[mb][r0 + 2 * e + 1]));
         if (e & 1) ls1 = T::dot2(pw[e], T::kOnePair, ls1);
         else ls0 = T::dot2(pw[e], T::kOnePair, ls0);
       }
-      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      pk[kp4] = __builtin_bit_cast(s16x8, pw);
     }
     l_run += ls0 + ls1;
   };
 
   // ---- prologue: K and V of step 0, K of step 1; scores of step 0
   refill(0);
-  issue_all(desc(0, false, kOffK0), ld_colK);
-  issue_all(desc(0, true, kOffV0), ld_colV);
-  issue_all(desc(1, false, kOffK1), ld_colK);
+  issue_all(desc(0, false, kOffK0), false, Gen{});
+  issue_all(desc(0, true, kOffV0), true, Gen{});
+  issue_all(desc(1, false, kOffK1), false, Gen{});
   f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -417,7 +430,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // ((j+1)&1); S MFMAs of tile j+1 from K buffer ((j+1)&1); PV MFMAs of tile j from V
   // buffer (j&1).  The buffer parity is a compile-time constant (the loop is unrolled by
   // two), so every LDS address is a register plus an immediate.
-  auto step = [&](int j, auto par_c) {
+  auto step = [&](int j, auto par_c, auto pre_c) {
     constexpr int PAR = decltype(par_c)::value;
     constexpr uint32_t offK_ld = PAR ? kOffK1 : kOffK0, offV_ld = PAR ? kOffV0 : kOffV1;
     constexpr uint32_t offK_rd = PAR ? kOffK0 : kOffK1, offV_rd = PAR ? kOffV1 : kOffV0;
@@ -431,8 +444,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const LdDesc dv = desc(lv, true, offV_ld);
     const bool need_mask = (mask_bits >> lv) & 1;
     if (!wave_active) {
-      issue_all(dk, ld_colK);
-      issue_all(dv, ld_colV);
+      issue_all(dk, false, pre_c);
+      issue_all(dv, true, pre_c);
       return;
     }
     // Hand-interleaved: each step of a phase is a scheduling region of its own, so
@@ -441,7 +454,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack), loads.
     f32x16 s_nxt[2] = {f32x16{}, f32x16{}};
     s16x8 ka[NKK][2];
-    uint32_t pw[16];
+    // probabilities of tile j, written in place as the four B operands of the PV product
+    u32x4 pw[4];
 #pragma unroll
     for (int kk = 0; kk < 2 && kk < NKK; ++kk) {
       ka[kk][0] = k_operand(offK_rd, kk, 0);
@@ -452,8 +466,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       __builtin_amdgcn_sched_barrier(0);
       // one load per step: bunched at the step start, the loads of all waves queue at
       // the memory pipeline and stall the issuing waves
-      if (kk < NLD) issue(dk, ld_colK, kk);
-      else issue(dv, ld_colV, kk - NLD);
+      if (kk < NLD) issue(dk, false, kk, pre_c);
+      else issue(dv, true, kk - NLD, pre_c);
       if (kk + 2 < NKK) {
         ka[kk + 2][0] = k_operand(offK_rd, kk + 2, 0);
         ka[kk + 2][1] = k_operand(offK_rd, kk + 2, 1);
@@ -464,16 +478,18 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       for (int e = 0; e < 16; ++e)                // pair e = (kp4 = e/4, element e%4)
         if (e * NKK / 16 == kk) {
           const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
-          pw[e] = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
+          // each packed word is pinned here, in phase 1: pinning the assembled operand
+          // instead made the compiler rebuild it with copies before the PV product
+          uint32_t w2 = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
+          asm volatile("" : "+v"(w2));
+          pw[kp4][ee] = w2;
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+
     s16x8 pk[4];
 #pragma unroll
-    for (int kp4 = 0; kp4 < 4; ++kp4)
-      pk[kp4] = __builtin_bit_cast(s16x8, make_uint4(pw[4 * kp4], pw[4 * kp4 + 1], pw[4 * kp4 + 2], pw[4 * kp4 + 3]));
-    // keep the probabilities in phase 1: otherwise they sink past the mask branch
-    asm volatile("" ::"v"(pk[0]), "v"(pk[1]), "v"(pk[2]), "v"(pk[3]));
+    for (int kp4 = 0; kp4 < 4; ++kp4) pk[kp4] = __builtin_bit_cast(s16x8, pw[kp4]);
     if (need_mask) {
       keep_branch();
       mask(t_begin + KS * (j + 1) + kh, s_nxt);
@@ -513,7 +529,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
           const int k0 = (u - 13) * 4;
           float a = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 + e], T::kOnePair, a);
+          for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 >> 2][e], T::kOnePair, a);
           ls[u - 13] = a;
         }
       }
@@ -533,15 +549,28 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     __builtin_amdgcn_s_waitcnt(0);                  // this wave's LDS-direct loads have landed
     __syncthreads();
   };
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  // Steps j, j+1 whose loads (K of tile j+3 at the latest) are prefix tiles of this key
+  // part take the precomputed offsets; the chunk's own tiles and the tail the general
+  // form.  Every step ends in one barrier in both loops, so the key parts may switch
+  // loops at different steps.
+  const int n_pre_part = max(0, (n_pre - t_begin - kh + KS - 1) / KS);
   int j = 0;
-  for (; j + 2 < nstage; j += 2) {
-    step(j, std::integral_constant<int, 0>{});
+  for (; j + 3 < n_pre_part && j + 2 < nstage; j += 2) {
+    step(j, Par0{}, Pre{});
     sync();
-    step(j + 1, std::integral_constant<int, 1>{});
+    step(j + 1, Par1{}, Pre{});
+    sync();
+  }
+  for (; j + 2 < nstage; j += 2) {
+    step(j, Par0{}, Gen{});
+    sync();
+    step(j + 1, Par1{}, Gen{});
     sync();
   }
   if (j + 1 < nstage) {
-    step(j, std::integral_constant<int, 0>{});
+    step(j, Par0{}, Gen{});
     sync();
     ++j;
   }
