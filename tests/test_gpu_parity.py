@@ -83,6 +83,10 @@ PREFILL_CASES = [
     (206, "bf16", 4, 4, 128, [0, 0], [200, 3], "none"),        # MHA, no prefix
     (207, "fp16", 8, 1, 64, [1, 15, 16, 17], [7, 9, 16, 31], "none"),  # MQA, block edges
     (214, "bf16", 8, 2, 128, [9000, 8300], [70, 33], "pairs"),  # > 128 tiles: key-split waves refill
+    # 15 prefix tiles: the two key parts leave the prefix-only loop at different steps
+    (216, "bf16", 16, 2, 128, [930, 1000, 450], [33, 64, 100], "none"),
+    (217, "fp16", 32, 8, 96, [930, 510, 575], [20, 129, 3], "pairs"),
+    (218, "bf16", 8, 2, 64, [960, 961, 1023], [64, 1, 65], "none"),
 ]
 
 
@@ -278,6 +282,8 @@ CASCADE_CASES = [
     (406, "bf16", 40, 2, 64, [700, 1600, 33], 48),                  # G=20: two head chunks
     # 10 sequence groups x 128 shared blocks: the separate shared pass, not the grouped form
     (407, "bf16", 32, 8, 128, [2048 + 37 * i for i in range(39)] + [1500], 128),
+    # 512 shared blocks: the separate pass with key splits of 8 tiles (prefix-only loop)
+    (408, "fp16", 32, 8, 128, [8192 + 37 * i for i in range(39)] + [6000], 512),
 ]
 
 
