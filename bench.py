@@ -223,7 +223,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by sequence and KV head but no multi-GPU run is provided.",
               file=sys.stderr)
         return 2
