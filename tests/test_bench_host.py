@@ -2,8 +2,6 @@
 rule that a committed HBM-traffic figure is used only while its kernel sources are unchanged."""
 import hashlib
 
-import pytest
-
 import bench
 
 
