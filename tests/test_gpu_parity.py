@@ -87,6 +87,9 @@ PREFILL_CASES = [
     (216, "bf16", 16, 2, 128, [930, 1000, 450], [33, 64, 100], "none"),
     (217, "fp16", 32, 8, 96, [930, 510, 575], [20, 129, 3], "pairs"),
     (218, "bf16", 8, 2, 64, [960, 961, 1023], [64, 1, 65], "none"),
+    # G = 20: one row tile mixes several chunk rows of 20 heads; MHA at head dim 96
+    (219, "fp16", 40, 2, 128, [100, 700], [50, 33], "none"),
+    (220, "bf16", 6, 6, 96, [333, 0, 64], [7, 130, 64], "none"),
 ]
 
 
