@@ -31,6 +31,11 @@
 
 namespace kvb {
 
+// 16 bytes per lane with the non-temporal (streaming) cache policy (operand 2 = nt).
+__device__ inline uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
+}
+
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kMaxSplitBlocks = 256;
@@ -291,6 +296,12 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   const int v_st = (lane / CPR) * VROW + (lane % CPR) * 8;
   const int k_st = (lane / CPR) * KROW + (lane % CPR) * 8;
 
+  // In the grouped shared-prefix form, the private splits' blocks (read once) are loaded
+  // with the non-temporal policy, so that they evict less of the shared blocks the group
+  // work-groups re-read from L2.  The plain form cannot tell shared blocks from private
+  // ones and reads normally (its kernel has no such branch: GROUP is a template argument).
+  const bool stream_loads = GROUP && !group_wg;
+
   // Both blocks of a step through buffer resources sized to their valid rows: rows past
   // the context, blocks past the split and blocks outside the pool read as zero and
   // cost no memory traffic, and every load is issued unconditionally.
@@ -325,10 +336,18 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + off, (uint32_t)(rows * D * 2));
+      if (stream_loads) {
 #pragma unroll
-      for (int j = 0; j < VCH; ++j) {
-        R.k[hb][j] = buf_load16(rk, (uint32_t)(8 * (j * 64 + lane)) * 2);
-        R.v[hb][j] = buf_load16(rv, (uint32_t)(8 * (j * 64 + lane)) * 2);
+        for (int j = 0; j < VCH; ++j) {
+          R.k[hb][j] = buf_load16_nt(rk, (uint32_t)(8 * (j * 64 + lane)) * 2);
+          R.v[hb][j] = buf_load16_nt(rv, (uint32_t)(8 * (j * 64 + lane)) * 2);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+          R.k[hb][j] = buf_load16(rk, (uint32_t)(8 * (j * 64 + lane)) * 2);
+          R.v[hb][j] = buf_load16(rv, (uint32_t)(8 * (j * 64 + lane)) * 2);
+        }
       }
     }
   };
