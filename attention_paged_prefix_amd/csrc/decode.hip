@@ -296,16 +296,19 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   const int v_st = (lane / CPR) * VROW + (lane % CPR) * 8;
   const int k_st = (lane / CPR) * KROW + (lane % CPR) * 8;
 
-  // In the grouped shared-prefix form, the private splits' blocks (read once) are loaded
-  // with the non-temporal policy, so that they evict less of the shared blocks the group
-  // work-groups re-read from L2.  The plain form cannot tell shared blocks from private
-  // ones and reads normally (its kernel has no such branch: GROUP is a template argument).
-  const bool stream_loads = GROUP && !group_wg;
+  // Blocks that are read once are loaded with the non-temporal policy, so that they evict
+  // less of the shared-prefix blocks other work-groups re-read from L2: in the grouped
+  // shared-prefix form the private splits; in the plain form every split after a
+  // sequence's first (and a whole private pass after a shared prefix).  The plain form
+  // cannot see which blocks are shared; prefixes shared between requests start their
+  // sequences, so its first split keeps the normal policy.  The choice is made once per
+  // work-group: the main loop is compiled for both policies.
+  const bool stream_loads = !Q8 && (GROUP ? !group_wg : (blk_first > 0 || split > 0));
 
   // Both blocks of a step through buffer resources sized to their valid rows: rows past
   // the context, blocks past the split and blocks outside the pool read as zero and
   // cost no memory traffic, and every load is issued unconditionally.
-  auto load = [&](int blk0, Step& R) {
+  auto load = [&](int blk0, Step& R, auto nt_c) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int blk = blk0 + hb;
@@ -336,7 +339,7 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
       }
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + off, (uint32_t)(rows * D * 2));
-      if (stream_loads) {
+      if constexpr (decltype(nt_c)::value) {
 #pragma unroll
         for (int j = 0; j < VCH; ++j) {
           R.k[hb][j] = buf_load16_nt(rk, (uint32_t)(8 * (j * 64 + lane)) * 2);
@@ -469,19 +472,23 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
   // named buffers in ping-pong so that no register copy forces a wait on loads that are
   // still in flight.
   const int nsteps = (blk_end - blk_begin - 2 * w + 2 * kDecWaves - 1) / (2 * kDecWaves);
-  if (nsteps > 0) {
+  auto main_loop = [&](auto nt_c) {
     constexpr int kStride = 2 * kDecWaves;
     int blk0 = blk_begin + 2 * w;
     Step A, B;
-    load(blk0, A);
+    load(blk0, A, nt_c);
     for (int it = 0; it < nsteps; it += 2) {
-      load(blk0 + kStride, B);
+      load(blk0 + kStride, B, nt_c);
       step(A);
       if (it + 1 >= nsteps) break;
-      load(blk0 + 2 * kStride, A);
+      load(blk0 + 2 * kStride, A, nt_c);
       step(B);
       blk0 += 2 * kStride;
     }
+  };
+  if (nsteps > 0) {
+    if (stream_loads) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
   }
 
   // row sums over the four key groups of the wave
