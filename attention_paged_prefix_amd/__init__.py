@@ -129,11 +129,14 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
                   cu_q_lens: torch.Tensor, prefix_lens: torch.Tensor, block_tables: torch.Tensor,
                   scale: float, max_q_len: int, max_prefix_len: int,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None, dispatch_plan: bool = True) -> torch.Tensor:
+                  stream=None, dispatch_plan: bool = True,
+                  slot_mapping: Optional[torch.Tensor] = None) -> torch.Tensor:
     """kvb_paged_prefill.  ``q [T][Hq][d]``, ``k_new/v_new [T][Hkv][d]``, ``cu_q_lens`` int32
     [B+1], ``prefix_lens`` int32 [B], ``block_tables`` int32 [B][stride].
     ``dispatch_plan=False`` passes no workspace: work-groups start in table order instead
-    of longest first (same results)."""
+    of longest first (same results).  With ``slot_mapping`` (int64 [T]) the call is
+    kvb_paged_prefill_write: the chunk's K/V is also written into the pool at those slots,
+    as write_kv would, in the same launch."""
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -145,11 +148,18 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     else:
         workspace = None
     ps = pool.c_struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if slot_mapping is not None:
+        _lib.check("kvb_paged_prefill_write", lib.kvb_paged_prefill_write(
+            ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(slot_mapping),
+            _ptr(cu_q_lens), _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch,
+            hq, T, int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace), ws_bytes,
+            _stream(stream)))
+        return out
     _lib.check("kvb_paged_prefill", lib.kvb_paged_prefill(
         ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(cu_q_lens),
         _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch, hq, T,
-        int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+        int(max_q_len), int(max_prefix_len), float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

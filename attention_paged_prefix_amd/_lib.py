@@ -23,6 +23,7 @@ STATUS = {
 EXPORTS = (
     "kvb_write_kv",
     "kvb_paged_prefill",
+    "kvb_paged_prefill_write",
     "kvb_paged_prefill_pooled",
     "kvb_paged_decode",
     "kvb_paged_decode_cascade",
@@ -101,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_prefill.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, _vp, _sz, _vp]
     lib.kvb_paged_prefill.restype = ctypes.c_int
+    lib.kvb_paged_prefill_write.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]
+    lib.kvb_paged_prefill_write.restype = ctypes.c_int
     lib.kvb_paged_prefill_pooled.argtypes = [_PP, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _f32, _vp]
     lib.kvb_paged_prefill_pooled.restype = ctypes.c_int

@@ -79,12 +79,18 @@ size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int3
   return (size_t)kvb::prefill_plan_bytes(batch, num_q_heads, total_q);
 }
 
-kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
-                             const void* v_new, void* out, const int32_t* cu_q_lens,
-                             const int32_t* prefix_lens, const int32_t* block_tables,
-                             int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
-                             int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
-                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kvb_paged_prefill, with `slots` (NULL: none) the chunk's slot scatter fused in
+kvb_status paged_prefill_impl(const kvb_pool* pool, const void* q, const void* k_new,
+                              const void* v_new, void* out, const int64_t* slots, bool want_slots,
+                              const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                              const int32_t* block_tables, int32_t block_table_stride, int32_t batch,
+                              int32_t num_q_heads, int32_t total_q, int32_t max_q_len,
+                              int32_t max_prefix_len, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   kvb_status st = check_pool(pool);
   if (st != KVB_OK) return st;
   if (batch < 0 || total_q < 0 || max_q_len < 0 || max_prefix_len < 0 || num_q_heads <= 0)
@@ -94,8 +100,10 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
   if (batch == 0 || total_q == 0) return KVB_OK;
   if (!q || !k_new || !v_new || !out || !cu_q_lens || !prefix_lens || !block_tables)
     return KVB_ERR_NULL;
+  if (want_slots && !slots) return KVB_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
-      ((uintptr_t)cu_q_lens & 3u) || ((uintptr_t)prefix_lens & 3u) || ((uintptr_t)block_tables & 3u))
+      ((uintptr_t)cu_q_lens & 3u) || ((uintptr_t)prefix_lens & 3u) || ((uintptr_t)block_tables & 3u) ||
+      ((uintptr_t)slots & 7u))
     return KVB_ERR_INVALID;
   if (max_q_len > total_q) return KVB_ERR_INVALID;
   if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
@@ -108,7 +116,35 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
   return launch_status(kvb::launch_prefill(*pool, q, k_new, v_new, out, cu_q_lens, prefix_lens,
                                            block_tables, block_table_stride, batch, num_q_heads,
                                            total_q, max_q_len, max_prefix_len, scale,
-                                           need > 0 ? workspace : nullptr, (hipStream_t)stream));
+                                           need > 0 ? workspace : nullptr, (hipStream_t)stream,
+                                           want_slots ? slots : nullptr));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
+                             const void* v_new, void* out, const int32_t* cu_q_lens,
+                             const int32_t* prefix_lens, const int32_t* block_tables,
+                             int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                             int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
+                             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_prefill_impl(pool, q, k_new, v_new, out, nullptr, false, cu_q_lens, prefix_lens,
+                            block_tables, block_table_stride, batch, num_q_heads, total_q, max_q_len,
+                            max_prefix_len, scale, workspace, workspace_bytes, stream);
+}
+
+kvb_status kvb_paged_prefill_write(const kvb_pool* pool, const void* q, const void* k_new,
+                                   const void* v_new, void* out, const int64_t* slot_mapping,
+                                   const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                   int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_prefill_impl(pool, q, k_new, v_new, out, slot_mapping, true, cu_q_lens, prefix_lens,
+                            block_tables, block_table_stride, batch, num_q_heads, total_q, max_q_len,
+                            max_prefix_len, scale, workspace, workspace_bytes, stream);
 }
 
 kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* out,

@@ -90,11 +90,12 @@ hipError_t launch_prefill_pooled(const kvb_pool& p, const void* q, void* out, co
                                  const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
                                  int hq, int total_q, int max_q_len, float scale, hipStream_t s);
 // Prefill: `plan_ws` (may be NULL) holds prefill_plan_bytes(...) bytes for the
-// longest-first dispatch plan of a grid of several rounds.
+// longest-first dispatch plan of a grid of several rounds; `slots` (may be NULL): also
+// scatter the chunk's K/V into the pool at these slots in the same launch.
 int64_t prefill_plan_bytes(int batch, int hq, int total_q);
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
-                          float scale, void* plan_ws, hipStream_t s);
+                          float scale, void* plan_ws, hipStream_t s, const int64_t* slots = nullptr);
 
 }  // namespace kvb

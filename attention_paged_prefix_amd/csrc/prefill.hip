@@ -88,6 +88,16 @@ struct PfCascade {
   int ws_slots;
 };
 
+// Fused slot scatter (ordinary prefill only): with `slots` set, the chunk's own K/V rows
+// are also written into the pool at their slots, as kvb_write_kv would, in the same launch.
+// The prefill never reads those slots (its prefix rows are below P_b, the chunk's keys
+// come from k_new/v_new), so the writes need no ordering against its reads.
+struct PfWrite {
+  const int64_t* slots;                      // [total_q]; slot = block*16 + row, < 0 = skip
+  uint16_t* k;                               // the pool (same storage as kp / vp)
+  uint16_t* v;
+};
+
 // Work-group = 4 * KS waves.  Wave w handles the 32 virtual rows 32*(w & 3) .. +31 of
 // the work-group's 128 and the key tiles t with t % KS == (w >> 2) ("key part").  With
 // KS = 2 (small grids: 8 waves, one work-group per CU) the two waves of a row group split
@@ -113,7 +123,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                uint16_t* __restrict__ out, const int32_t* __restrict__ cu,
                const int32_t* __restrict__ plen, const int32_t* __restrict__ bt, int bt_stride,
                int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
-               int real, const int32_t* __restrict__ order, PfCascade cas) {
+               int real, const int32_t* __restrict__ order, PfCascade cas, PfWrite wr) {
   using L = PfLayout<D>;
   constexpr int CPR = L::CPR;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
@@ -587,6 +597,25 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     else last(std::integral_constant<int, 0>{});
   }
 
+  // Fused slot scatter: token i of the chunk is written by the work-group holding its first
+  // virtual row i*G, so each token is written exactly once; 16 bytes per thread and item.
+  if (MODE == kModePrefill && wr.slots) {
+    const int i_lo = (v0 + G - 1) / G;
+    const int i_hi = min(C, (v0 + kBM + G - 1) / G);
+    const int n_items = max(0, i_hi - i_lo) * 2 * CPR;
+    for (int it = (int)threadIdx.x; it < n_items; it += (int)blockDim.x) {
+      const int tok = i_lo + it / (2 * CPR);
+      const int part = (it / CPR) & 1;                // 0: K, 1: V
+      const int ch = it - (it / CPR) * CPR;
+      const int64_t slot = wr.slots[cu_b + tok];
+      if (slot < 0) continue;
+      const int64_t src = ((int64_t)(cu_b + tok) * hkv + kvh) * D + 8 * ch;
+      const int64_t dst = (slot >> 4) * block_stride + ((int64_t)kvh * kBlock + (slot & 15)) * D + 8 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>((part ? vn : kn) + src);
+      *reinterpret_cast<uint4*>((part ? wr.v : wr.k) + dst) = val;
+    }
+  }
+
   // Output row of this lane, recomputed from an opaque copy of the thread id so that the
   // pre-loop values need not stay live (in registers) across the main loop.
   int tid_e = threadIdx.x;
@@ -746,7 +775,8 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
                                    int total_q, int max_q_len, float scale, const PfCascade& cas,
-                                   int32_t* plan_ws, hipStream_t s) {
+                                   int32_t* plan_ws, hipStream_t s, const int64_t* slots = nullptr) {
+  const PfWrite wr{slots, (uint16_t*)p.k, (uint16_t*)p.v};
   const int G = hq / p.num_kv_heads;
   const long long rows = (long long)max_q_len * G;
   const int max_tiles = (int)((rows + kBM - 1) / kBM);
@@ -772,13 +802,13 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, order, cas);
+                       (int)padded, (int)real, order, cas, wr);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, order, cas);
+                       (int)padded, (int)real, order, cas, wr);
   return hipGetLastError();
 }
 
@@ -795,13 +825,13 @@ static hipError_t dispatch_prefill(const kvb_pool& p, F&& f) {
 hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, const void* vn, void* out,
                           const int32_t* cu, const int32_t* plen, const int32_t* bt, int bt_stride,
                           int batch, int hq, int total_q, int max_q_len, int max_prefix_len,
-                          float scale, void* plan_ws, hipStream_t s) {
+                          float scale, void* plan_ws, hipStream_t s, const int64_t* slots) {
   (void)max_prefix_len;
   const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
   return dispatch_prefill(p, [&](auto t, auto d) {
     return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
                                                              batch, hq, total_q, max_q_len, scale, none,
-                                                             (int32_t*)plan_ws, s);
+                                                             (int32_t*)plan_ws, s, slots);
   });
 }
 

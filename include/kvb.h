@@ -106,6 +106,25 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
                              int32_t total_q, int32_t max_q_len, int32_t max_prefix_len,
                              float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* kvb_paged_prefill and kvb_write_kv of the same chunk in one launch: the same output, and
+ * the chunk's K/V rows written into the pool at slot_mapping[t] as kvb_write_kv writes them
+ * (kvboost 0.6.0, "How it works" step 5: the live suffix's KV is stored for reuse while the
+ * suffix is computed; kvstream 0.1.0, "Request lifecycle" step 2: one slot per token).
+ * Each token is written by the work-group that holds its first query row, after that
+ * work-group's attention work, so every row is written once.
+ * slot_mapping: (device) int64 [total_q], 8-byte aligned; slot = block*16 + row, < 0 skips
+ * the token.  The slots must not lie in rows this call reads as prefix (rows below
+ * prefix_lens[b] of the table's blocks) nor repeat within the call; out-of-range slots are
+ * undefined behaviour, as for kvb_write_kv.  Other arguments, errors and the workspace as
+ * kvb_paged_prefill (KVB_ERR_NULL also for a missing slot_mapping). */
+kvb_status kvb_paged_prefill_write(const kvb_pool* pool, const void* q, const void* k_new,
+                                   const void* v_new, void* out, const int64_t* slot_mapping,
+                                   const int32_t* cu_q_lens, const int32_t* prefix_lens,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   int32_t batch, int32_t num_q_heads, int32_t total_q,
+                                   int32_t max_q_len, int32_t max_prefix_len, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Paged prefill with every key read from the pool: the same result as kvb_paged_prefill,
  * but the chunk's own K/V is read back through the block table (positions
  * prefix_lens[b] .. prefix_lens[b] + C_b - 1 of sequence b), after kvb_write_kv has put it

@@ -99,6 +99,28 @@ def test_prefill_validation(lib):
     assert prefill(lib, p, total=0, maxq=0) == OK
 
 
+def prefill_write(lib, p, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, slots=FAKE, cu=FAKE, pl=FAKE, bt=FAKE, stride=4,
+             batch=2, hq=4, total=10, maxq=6, maxp=64, scale=0.1, ws=None, wsb=0)
+    a.update(kw)
+    return lib.kvb_paged_prefill_write(ctypes.byref(p), a["q"], a["kn"], a["vn"], a["out"], a["slots"],
+                                       a["cu"], a["pl"], a["bt"], a["stride"], a["batch"], a["hq"],
+                                       a["total"], a["maxq"], a["maxp"], a["scale"], a["ws"], a["wsb"],
+                                       None)
+
+
+def test_prefill_write_validation(lib):
+    p = pool()
+    assert prefill_write(lib, p, slots=None) == NULL          # the slot mapping is required
+    assert prefill_write(lib, p, slots=FAKE + 4) == INVALID    # int64: 8-byte aligned
+    assert prefill_write(lib, p, hq=3) == INVALID
+    assert prefill_write(lib, p, q=None) == NULL
+    assert prefill_write(lib, p, stride=3) == INVALID
+    assert prefill_write(lib, pool(head_dim=256)) == UNSUP
+    assert prefill_write(lib, p, batch=0) == OK
+    assert prefill_write(lib, p, total=0, maxq=0, slots=None) == OK
+
+
 def decode(lib, p, **kw):
     a = dict(q=FAKE, out=FAKE, ctx=FAKE, bt=FAKE, stride=256, batch=4, hq=8, maxc=4000, sb=0,
              scale=0.1, ws=None, wsb=0)

@@ -134,6 +134,30 @@ def test_prefill_large_grid_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+@pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:2],
+                         ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
+def test_prefill_write_equals_prefill_and_write_kv(case):
+    """kvb_paged_prefill_write: the prefill's output bit for bit, and the pool exactly as
+    the oracle's slot scatter leaves it (skipped slots included)."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share = case
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
+    slots = w.slot_mapping.copy()
+    slots[::7] = -1
+    dev = u.Dev(w)
+    ref_out = u.to_bits(dev.prefill())
+    out = kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,
+                            int(w.q_lens.max()), int(w.prefix_lens.max()),
+                            slot_mapping=u.idev(slots, torch.int64))
+    torch.cuda.synchronize()
+    assert np.array_equal(u.to_bits(out), ref_out)
+    ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, slots)
+    assert np.array_equal(u.to_bits(dev.k), ek)
+    assert np.array_equal(u.to_bits(dev.v), ev)
+
+
 def test_prefill_dispatch_plan_gives_same_bits():
     """Longest-first dispatch (the plan kernel writes the order into the workspace) and
     table order (no workspace) give the same bits, and match the oracle, on a ragged grid
