@@ -217,8 +217,11 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0, help="decode split size (0 = auto)")
     ap.add_argument("--no-decode", action="store_true", help="skip the separate decode workload")
-    ap.add_argument("--only", choices=["step", "prefill", "decode", "write_kv", "copy", "decode_workload",
-                                       "copy_blocks"],
+    ap.add_argument("--separate-write", action="store_true",
+                    help="step with kvb_write_kv of the chunk before kvb_paged_prefill instead of "
+                         "kvb_paged_prefill_write (prefill and slot scatter in one launch)")
+    ap.add_argument("--only", choices=["step", "prefill", "prefill_write", "decode", "write_kv", "copy",
+                                       "decode_workload", "copy_blocks"],
                     default="step", help="profiling aid: time only one part")
     args = ap.parse_args(argv)
 
@@ -285,13 +288,17 @@ def main(argv=None):
         elif name == "prefill":
             kvb.paged_prefill(pool, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out,
                               workspace=pws)
+        elif name == "prefill_write":
+            kvb.paged_prefill(pool, q, kn, vn, cu, pl, bt, w.scale, max_q, max_p, out=out,
+                              workspace=pws, slot_mapping=slots)
         elif name == "write_kv_dec":
             kvb.write_kv(pool, dk, dv, dslots)
         elif name == "decode":
             kvb.paged_decode(pool, dq, dctx, bt, w.scale, max_ctx, out=dout, workspace=dws)
 
-    parts = ["write_kv", "prefill", "write_kv_dec", "decode"]
-    if args.only in ("prefill", "decode", "write_kv"):
+    parts = (["write_kv", "prefill", "write_kv_dec", "decode"] if args.separate_write
+             else ["prefill_write", "write_kv_dec", "decode"])
+    if args.only in ("prefill", "prefill_write", "decode", "write_kv"):
         parts = [args.only] if args.only != "decode" else ["write_kv", "write_kv_dec", "decode"]
         if args.only == "decode":
             for p_ in parts[:2]:
@@ -355,19 +362,22 @@ def main(argv=None):
     # spin kernel (the eager pass above also counts the GPU's wait for the host between
     # launches).
     kernel_ms = {}
-    for p_ in parts:
+    timed = parts + (["prefill"] if "prefill_write" in parts else [])   # the plain prefill too
+    for p_ in timed:
         settle(torch, lambda: part(p_), min(args.settle_ms, 100.0))
         kernel_ms[p_] = time_launches(torch, lambda: part(p_), max(args.steps, 10))
 
     pf = prefill_flops(w)
     df = decode_flops(w.dec_context_lens, w)
-    step_flops = (pf if "prefill" in parts else 0.0) + (df if "decode" in parts else 0.0)
+    step_flops = (pf if ("prefill" in parts or "prefill_write" in parts) else 0.0) + \
+        (df if "decode" in parts else 0.0)
     kernels = {}
-    if "prefill" in kernel_ms:
-        t = kernel_ms["prefill"] * 1e-3
-        kernels["paged_prefill"] = {"ms": kernel_ms["prefill"], "ms_in_eager_step": per_part["prefill"],
-                                    "tflops": pf / t / 1e12, "gbps": prefill_bytes(w) / t / 1e9,
-                                    "frac_mfma_peak": pf / t / 1e12 / PEAK_TFLOPS}
+    for nm, key in (("prefill", "paged_prefill"), ("prefill_write", "paged_prefill_write")):
+        if nm in kernel_ms:
+            t = kernel_ms[nm] * 1e-3
+            kernels[key] = {"ms": kernel_ms[nm], "ms_in_eager_step": per_part.get(nm),
+                            "tflops": pf / t / 1e12, "gbps": prefill_bytes(w) / t / 1e9,
+                            "frac_mfma_peak": pf / t / 1e12 / PEAK_TFLOPS}
     if "decode" in kernel_ms:
         t = kernel_ms["decode"] * 1e-3
         db = decode_bytes(w, w.dec_context_lens, w.block_tables)
@@ -405,11 +415,13 @@ def main(argv=None):
                    "num_blocks": w.num_blocks, "seed": w.seed, "parallelism": "single GPU"},
         "kernels": kernels,
     }
-    if "prefill" in per_part:
-        ach = kernels["paged_prefill"]["tflops"]
-        res["roofline"] = {"bound": "mfma", "kernel": "paged_prefill", "achieved": ach,
+    # the step's dominant kernel: the prefill launch the step runs
+    pk = "paged_prefill_write" if "prefill_write" in kernel_ms else "paged_prefill"
+    if pk in kernels:
+        ach = kernels[pk]["tflops"]
+        res["roofline"] = {"bound": "mfma", "kernel": pk, "achieved": ach,
                            "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_TFLOPS,
-                           "traffic": read_traffic(f"paged_prefill_{args.config}"),
+                           "traffic": read_traffic(f"{pk}_{args.config}"),
                            "algorithmic_flops_per_launch": pf,
                            "algorithmic_bytes_per_launch": prefill_bytes(w)}
 
@@ -420,7 +432,7 @@ def main(argv=None):
                           "traffic": read_traffic("paged_decode_decode_workload")}
         res["decode_workload"] = dw
 
-    if args.only == "step" and "prefill" in per_part:
+    if args.only == "step" and "prefill" in kernel_ms:
         res["prefill_q8"] = bench_prefill_q8(torch, kvb, w, k, v, q, kn, vn, cu, pl, bt, max_q, max_p,
                                              pf, kernel_ms["prefill"], args)
 
