@@ -103,3 +103,23 @@ def test_cascade_decode_full_size_sampled():
                               w.dtype, seqs=seqs)
     err = float(np.max(np.abs(vals[seqs] - ref[seqs])))
     assert err <= u.TOL[w.dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("name", ["shared_prompt", "long_prefix"])
+def test_prefill_write_full_size(name):
+    """kvb_paged_prefill_write as the benchmark step runs it: the output bits of the plain
+    prefill (checked against the oracle above) and the whole pool as the oracle's slot
+    scatter leaves it."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    w = make_config(name, poison=True)
+    dev = u.Dev(w)
+    ref = u.to_bits(dev.prefill())
+    out = kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,
+                            int(w.q_lens.max()), int(w.prefix_lens.max()), slot_mapping=dev.slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(u.to_bits(out), ref)
+    ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping)
+    assert np.array_equal(u.to_bits(dev.k), ek)
+    assert np.array_equal(u.to_bits(dev.v), ev)
