@@ -17,7 +17,10 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_graph_replays_match_eager(fused):
+    """fused: the chunk's prefill and slot scatter in one launch (kvb_paged_prefill_write),
+    as the benchmark step runs it; replays must give the bits of the four-call step."""
     import attention_paged_prefix_amd as kvb
     import gpu_util as u
     w = make_custom(601, "bf16", 16, 2, 128, [300, 64, 1000], [40, 130, 77], share="pairs",
@@ -35,12 +38,22 @@ def test_step_graph_replays_match_eager():
     ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda:0")
     k0, v0 = dev.k.clone(), dev.v.clone()
 
-    def step():
+    def step_serial():
         kvb.write_kv(dev.pool, dev.k_new, dev.v_new, dev.slots)
         dev.prefill(out=out)
         kvb.write_kv(dev.pool, dk, dv, dslots)
         kvb.paged_decode(dev.pool, dq, dctx, dev.bt, w.scale, max_ctx, split_blocks=2, out=dout,
                          workspace=ws)
+
+    def step_fused():
+        kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,
+                          int(w.q_lens.max()), int(w.prefix_lens.max()), out=out,
+                          slot_mapping=dev.slots)
+        kvb.write_kv(dev.pool, dk, dv, dslots)
+        kvb.paged_decode(dev.pool, dq, dctx, dev.bt, w.scale, max_ctx, split_blocks=2, out=dout,
+                         workspace=ws)
+
+    step = step_fused if fused else step_serial
 
     def reset():
         dev.k.copy_(k0)
@@ -48,7 +61,7 @@ def test_step_graph_replays_match_eager():
         out.zero_()
         dout.zero_()
 
-    step()
+    step_serial()                                   # the reference: four separate calls
     torch.cuda.synchronize()
     ref = (u.to_bits(out), u.to_bits(dout), u.to_bits(dev.k), u.to_bits(dev.v))
 
