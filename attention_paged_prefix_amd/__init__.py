@@ -150,6 +150,11 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     ps = pool.c_struct()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if slot_mapping is not None:
+        # the kernel reads total_q int64 slots through this pointer
+        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T or \
+                slot_mapping.device != q.device or not slot_mapping.is_contiguous():
+            raise ValueError("slot_mapping must be a contiguous int64 tensor of total_q entries "
+                             "on q's device")
         _lib.check("kvb_paged_prefill_write", lib.kvb_paged_prefill_write(
             ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(slot_mapping),
             _ptr(cu_q_lens), _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch,

@@ -608,7 +608,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       const int part = (it / CPR) & 1;                // 0: K, 1: V
       const int ch = it - (it / CPR) * CPR;
       const int64_t slot = wr.slots[cu_b + tok];
-      if (slot < 0) continue;
+      if (slot < 0 || (slot >> 4) >= num_blocks) continue;     // outside the pool: skipped
       const int64_t src = ((int64_t)(cu_b + tok) * hkv + kvh) * D + 8 * ch;
       const int64_t dst = (slot >> 4) * block_stride + ((int64_t)kvh * kBlock + (slot & 15)) * D + 8 * ch;
       const uint4 val = *reinterpret_cast<const uint4*>((part ? vn : kn) + src);

@@ -112,10 +112,10 @@ kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_
  * suffix is computed; kvstream 0.1.0, "Request lifecycle" step 2: one slot per token).
  * Each token is written by the work-group that holds its first query row, after that
  * work-group's attention work, so every row is written once.
- * slot_mapping: (device) int64 [total_q], 8-byte aligned; slot = block*16 + row, < 0 skips
- * the token.  The slots must not lie in rows this call reads as prefix (rows below
- * prefix_lens[b] of the table's blocks) nor repeat within the call; out-of-range slots are
- * undefined behaviour, as for kvb_write_kv.  Other arguments, errors and the workspace as
+ * slot_mapping: (device) int64 [total_q], 8-byte aligned; slot = block*16 + row; a negative
+ * slot or one at or past num_blocks*16 skips the token, as in kvb_write_kv.  The slots must
+ * not lie in rows this call reads as prefix (rows below prefix_lens[b] of the table's
+ * blocks) nor repeat within the call.  Other arguments, errors and the workspace as
  * kvb_paged_prefill (KVB_ERR_NULL also for a missing slot_mapping). */
 kvb_status kvb_paged_prefill_write(const kvb_pool* pool, const void* q, const void* k_new,
                                    const void* v_new, void* out, const int64_t* slot_mapping,

@@ -27,16 +27,19 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
              slot_mapping: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Scatter each new token's K/V into its pool slot; negative slots are skipped.
+    """Scatter each new token's K/V into its pool slot; slots that name no row of the
+    pool (negative, or at or past ``num_blocks * 16``) are skipped.
 
     One slot per token in a fixed pool of pages (kvstream 0.1.0, "Why KVStream?",
     streaming KV allocation; "Request lifecycle" step 2).  A slot names physical
-    block ``slot // 16`` and row ``slot % 16`` inside it.  Returns new arrays.
+    block ``slot // 16`` and row ``slot % 16`` inside it; the pool is fixed, so a
+    slot outside it names no page at all.  Returns new arrays.
     """
     kp = np.array(k_pool, copy=True)
     vp = np.array(v_pool, copy=True)
+    n_slots = kp.shape[0] * BLOCK_SIZE
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
+        if slot < 0 or slot >= n_slots:
             continue
         blk, row = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
         kp[blk, :, row, :] = k_new[t]

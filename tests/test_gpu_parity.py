@@ -35,6 +35,8 @@ def test_write_kv_bit_exact(dt, d, hkv, layout):
     slots = w.slot_mapping.copy()
     slots[3] = -1
     slots[7] = -5
+    slots[9] = w.num_blocks * 16          # first slot past the pool
+    slots[12] = 1 << 40
     dev = u.Dev(w, layout)
     dev.slots = u.idev(slots, torch.int64)
     import attention_paged_prefix_amd as kvb
@@ -146,6 +148,9 @@ def test_prefill_write_equals_prefill_and_write_kv(case):
     w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
     slots = w.slot_mapping.copy()
     slots[::7] = -1
+    # slots at or past the end of the pool are skipped too, as kvb_write_kv skips them
+    slots[3::11] = w.num_blocks * 16 + np.arange(len(slots[3::11]))
+    slots[5::13] = 1 << 40
     dev = u.Dev(w)
     ref_out = u.to_bits(dev.prefill())
     out = kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,

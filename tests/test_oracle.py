@@ -346,6 +346,27 @@ def test_write_kv_matches_slot_semantics():
     assert np.array_equal(kp[s4 // 16, :, s4 % 16], w.k_pool[s4 // 16, :, s4 % 16])
 
 
+def test_write_kv_skips_slots_outside_the_pool():
+    """A slot at or past num_blocks * 16 names no row of the fixed pool: the token is
+    skipped and the pool is bit-for-bit unchanged; the other tokens land as usual."""
+    w = make_custom(43, "fp16", 2, 1, 8, [5], [6])
+    nb = w.k_pool.shape[0]
+    slots = w.slot_mapping.copy()
+    slots[1] = nb * 16                  # first slot past the pool
+    slots[2] = nb * 16 + 17
+    slots[3] = 1 << 40
+    kp, vp = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, slots)
+    keep = [0, 4, 5]
+    ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new[keep], w.v_new[keep], slots[keep])
+    assert np.array_equal(kp, ek) and np.array_equal(vp, ev)
+    for t in keep:
+        s = int(slots[t])
+        assert np.array_equal(kp[s // 16, :, s % 16], w.k_new[t])
+    # only the three in-pool slots' rows changed
+    diff = (kp != w.k_pool).any(axis=(1, 3)) | (vp != w.v_pool).any(axis=(1, 3))
+    assert {(int(a), int(b)) for a, b in np.argwhere(diff)} <= {(int(slots[t]) // 16, int(slots[t]) % 16) for t in keep}
+
+
 def test_selected_rows_equal_full_result():
     w = make_custom(42, "bf16", 8, 2, 32, [40, 0, 17], [9, 12, 3])
     full = _prefill(w)
