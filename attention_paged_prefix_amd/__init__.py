@@ -23,7 +23,8 @@ from . import _lib
 from ._lib import KVB_BF16, KVB_FP16, KvbError, KvbPool, KvbPoolQ8  # noqa: F401
 
 __all__ = [
-    "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_cascade", "copy_blocks",
+    "Pool", "write_kv", "paged_prefill", "paged_prefill_pooled", "paged_decode", "paged_decode_noalloc",
+    "paged_decode_cascade", "copy_blocks",
     "PoolQ8", "write_kv_q8", "paged_decode_q8", "paged_prefill_q8", "paged_prefill_q8_workspace_size",
     "PoolQ4", "write_kv_q4", "paged_decode_q4", "paged_prefill_q4",
     "gather_kv",
@@ -204,6 +205,22 @@ def paged_decode(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
         ctypes.byref(ps), _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
         int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out
+
+
+def paged_decode_noalloc(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
+                         block_tables: torch.Tensor, scale: float, max_context_len: int,
+                         out: torch.Tensor, split_blocks: int = 0, stream=None) -> torch.Tensor:
+    """kvb_paged_decode_noalloc: ``paged_decode`` with the split partials in the library's
+    static device scratch instead of a workspace.  ``out`` is required: this call allocates
+    nothing.  Calls that overlap on one GPU share the scratch and race."""
+    lib = _lib.load()
+    B, hq, d = q.shape
+    ps = pool.c_struct()
+    _lib.check("kvb_paged_decode_noalloc", lib.kvb_paged_decode_noalloc(
+        ctypes.byref(ps), _ptr(q), _ptr(out), _ptr(context_lens), _ptr(block_tables),
+        int(block_tables.shape[1]), B, hq, int(max_context_len), int(split_blocks), float(scale),
         _stream(stream)))
     return out
 

@@ -17,6 +17,7 @@ STATUS = {
     3: "KVB_ERR_UNSUPPORTED",
     4: "KVB_ERR_WORKSPACE",
     5: "KVB_ERR_LAUNCH",
+    6: "KVB_ERR_TOO_LARGE",
 }
 
 # every symbol include/kvb.h declares
@@ -26,6 +27,7 @@ EXPORTS = (
     "kvb_paged_prefill_write",
     "kvb_paged_prefill_pooled",
     "kvb_paged_decode",
+    "kvb_paged_decode_noalloc",
     "kvb_paged_decode_cascade",
     "kvb_paged_prefill_workspace_size",
     "kvb_paged_decode_workspace_size",
@@ -111,6 +113,9 @@ def load() -> ctypes.CDLL:
     lib.kvb_paged_decode.argtypes = [_PP, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _vp, _sz, _vp]
     lib.kvb_paged_decode.restype = ctypes.c_int
+    lib.kvb_paged_decode_noalloc.argtypes = [_PP, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                             _f32, _vp]
+    lib.kvb_paged_decode_noalloc.restype = ctypes.c_int
     lib.kvb_paged_decode_cascade.argtypes = [_PP, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                              _i32, _i32, _f32, _vp, _sz, _vp]
     lib.kvb_paged_decode_cascade.restype = ctypes.c_int

@@ -1,6 +1,7 @@
 // C ABI: host-side validation (before any HIP call), launch planning and dispatch.
 #include <math.h>
 #include <stdint.h>
+#include <mutex>
 #include "kvb.h"
 #include "kvb_launch.h"
 
@@ -55,6 +56,7 @@ const char* kvb_status_str(kvb_status s) {
     case KVB_ERR_UNSUPPORTED: return "unsupported configuration";
     case KVB_ERR_WORKSPACE: return "workspace missing or too small";
     case KVB_ERR_LAUNCH: return "kernel launch failed";
+    case KVB_ERR_TOO_LARGE: return "needs more scratch than the static device buffer holds";
   }
   return "unknown status";
 }
@@ -212,6 +214,70 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
   return launch_status(kvb::launch_decode(*pool, q, out, context_lens, block_tables,
                                           block_table_stride, batch, num_q_heads, max_context_len,
                                           sb, ns, scale, workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// Scratch of kvb_paged_decode_noalloc: the split partials live in this file-scope device
+// array instead of a caller workspace.  In host code `scratch` only names the symbol; its
+// device address (one copy per GPU) comes from hipGetSymbolAddress, taken once per device
+// with that device current and kept in scratch_dev[].
+static __device__ __align__(256) unsigned char scratch[KVB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch array (NULL if it cannot be obtained).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    scratch_dev[dev] = ptr;
+  }
+  return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+kvb_status kvb_paged_decode_noalloc(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, int32_t split_blocks, float scale,
+                                    void* stream) {
+  kvb_status st = check_pool(pool);
+  if (st != KVB_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || split_blocks < 0)
+    return KVB_ERR_INVALID;
+  if (num_q_heads % pool->num_kv_heads != 0) return KVB_ERR_INVALID;
+  if ((st = check_scale(scale)) != KVB_OK) return st;
+  if (batch == 0) return KVB_OK;
+  if (!q || !out || !context_lens || !block_tables) return KVB_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)context_lens & 3u) ||
+      ((uintptr_t)block_tables & 3u))
+    return KVB_ERR_INVALID;
+  if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
+    return KVB_ERR_INVALID;
+  int sb = 0, ns = 0;
+  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
+  const int64_t need = kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
+  if (need > (int64_t)KVB_NOALLOC_SCRATCH_BYTES) return KVB_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_address())) return KVB_ERR_LAUNCH;
+  // the split kernels write every partial the merge reads: nothing needs clearing
+  return launch_status(kvb::launch_decode(*pool, q, out, context_lens, block_tables,
+                                          block_table_stride, batch, num_q_heads, max_context_len,
+                                          sb, ns, scale, ws, (hipStream_t)stream));
 }
 
 // Plan of a cascade decode: the private splits, and the shared prefix either in group

@@ -45,7 +45,8 @@ typedef enum {
   KVB_ERR_INVALID = 2,      /* inconsistent sizes, negative counts, misalignment        */
   KVB_ERR_UNSUPPORTED = 3,  /* head_dim not in {64,96,128}, block_size != 16, bad dtype */
   KVB_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query returns */
-  KVB_ERR_LAUNCH = 5        /* the HIP runtime reported an error at launch              */
+  KVB_ERR_LAUNCH = 5,       /* the HIP runtime reported an error at launch              */
+  KVB_ERR_TOO_LARGE = 6     /* kvb_paged_decode_noalloc: more scratch than it holds     */
 } kvb_status;
 
 typedef enum { KVB_FP16 = 0, KVB_BF16 = 1 } kvb_dtype;
@@ -158,6 +159,27 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
                             int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
                             int32_t max_context_len, int32_t split_blocks, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free paged decode, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, split plan and result bits as kvb_paged_decode, with the split partials kept in
+ * a static device array of KVB_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a
+ * caller workspace.  Each GPU the library runs on holds its own copy of that array from
+ * the first call on it until the process ends; that first call on a device also looks up
+ * the array's address (no allocation call is made by this entry point at any time).
+ * Every call on one GPU shares the array and it keeps the last call's contents (nothing in
+ * it needs clearing: every partial the merge reads is written by the same call), so calls
+ * that overlap on one GPU (different streams, or threads) race and must be serialised by
+ * the caller.  A call whose split plan needs more than KVB_NOALLOC_SCRATCH_BYTES
+ * (kvb_paged_decode_workspace_size for the same arguments) returns KVB_ERR_TOO_LARGE and
+ * launches nothing; a plan without splits needs no scratch.  Arguments, layouts and the
+ * other errors as kvb_paged_decode. */
+#define KVB_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvb_status kvb_paged_decode_noalloc(const kvb_pool* pool, const void* q, void* out,
+                                    const int32_t* context_lens, const int32_t* block_tables,
+                                    int32_t block_table_stride, int32_t batch, int32_t num_q_heads,
+                                    int32_t max_context_len, int32_t split_blocks, float scale,
+                                    void* stream);
 
 /* Shared-prefix (cascade) decode: the same result as kvb_paged_decode, but the first
  * shared_len tokens of every sequence are one shared prefix, read once for all sequences'

@@ -149,6 +149,34 @@ def test_decode_validation_and_workspace(lib):
     assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 16 * 4 * 8 * (128 + 2) * 4
 
 
+def decode_noalloc(lib, p, **kw):
+    a = dict(q=FAKE, out=FAKE, ctx=FAKE, bt=FAKE, stride=256, batch=4, hq=8, maxc=4000, sb=0,
+             scale=0.1)
+    a.update(kw)
+    return lib.kvb_paged_decode_noalloc(ctypes.byref(p), a["q"], a["out"], a["ctx"], a["bt"],
+                                        a["stride"], a["batch"], a["hq"], a["maxc"], a["sb"],
+                                        a["scale"], None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode validates like kvb_paged_decode and refuses, before any
+    launch, a split plan whose partials exceed its static scratch (16 MiB)."""
+    p = pool(num_kv_heads=8, block_stride=8 * 16 * 128)
+    assert decode_noalloc(lib, p, hq=5) == INVALID
+    assert decode_noalloc(lib, p, q=None) == NULL
+    assert decode_noalloc(lib, p, out=FAKE + 2) == INVALID
+    assert decode_noalloc(lib, p, stride=249) == INVALID
+    assert decode_noalloc(lib, p, sb=-1) == INVALID
+    assert decode_noalloc(lib, p, scale=float("inf")) == INVALID
+    assert decode_noalloc(lib, pool(head_dim=80)) == UNSUP
+    assert decode_noalloc(lib, p, batch=0) == OK
+    # 64 sequences x 32 heads x 250 one-block splits x (128 + 2) floats > 16 MiB
+    need = lib.kvb_paged_decode_workspace_size(64, 8, 32, 128, 4000, 1)
+    assert need > 16 << 20
+    assert decode_noalloc(lib, p, batch=64, hq=32, sb=1) == 6
+    assert lib.kvb_status_str(6).startswith(b"needs more scratch")
+
+
 def cascade(lib, p, **kw):
     a = dict(q=FAKE, out=FAKE, ctx=FAKE, bt=FAKE, stride=256, shared=FAKE, slen=1024, batch=4,
              hq=8, maxc=4000, sb=0, scale=0.1, ws=None, wsb=0)
