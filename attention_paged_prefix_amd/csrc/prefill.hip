@@ -22,10 +22,14 @@
 //  * Software pipelined inside each wave: while the S MFMAs of tile j+1 run, the VALU
 //    turns tile j's scores into probabilities; while the PV MFMAs of tile j run, it takes
 //    tile j+1's row max.  K is staged one tile ahead of V.
-//  * Online softmax in the exp2 domain with scale*log2(e) folded into one FMA; the
-//    running max only moves (and the output is only rescaled) when a score exceeds it
-//    by more than 2^8.  Only tiles crossing the causal diagonal or the end of the keys
-//    are masked; tiles entirely in the future of every row are never visited.
+//  * Online softmax in the exp2 domain, x = scale*log2(e)*q.k - m in one FMA (fp32; the
+//    queries are not rescaled in 16 bits, which would cost precision at large scores).
+//    The reference m is the first tile's row maximum; it only moves (and the output is
+//    only rescaled) when a tile's partial row sum of probabilities exceeds 2^8 (a score
+//    more than about 2^8 above it), which the sums already computed for the denominator
+//    reveal, so no per-tile row maximum is taken.  Only tiles crossing the causal
+//    diagonal or the end of the keys are masked; tiles entirely in the future of every
+//    row are never visited.
 #include <type_traits>
 
 #include "kvb_device.h"
@@ -37,7 +41,10 @@ constexpr int kRowWaves = 4;             // waves along the rows (32 rows each)
 constexpr int kBM = 32 * kRowWaves;      // virtual rows per work-group
 constexpr int kKT = 64;                  // keys per tile
 constexpr float kPfNegBig = -1.0e30f;
-constexpr float kPfRescale = 8.0f;       // log2 units
+// A lane's partial row sum of one tile's probabilities (32 keys) above this means some
+// score is more than about 2^8 above the reference: the reference moves up.  Inf (an
+// fp16 probability that overflowed) compares above it too.
+constexpr float kPfSumLimit = 256.0f;
 
 // LDS tile = K rows then V rows, 64 x D each, unpadded.  Tiles are written by
 // LDS-direct buffer loads (16 bytes per lane, lanes contiguous), so rows cannot be
@@ -223,7 +230,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m_run = kPfNegBig, l_run = 0.f;
+  // m_run: the row's reference (exp2 domain); l_run: this lane's half of the row sum
+  float m_run = 0.f, l_run = 0.f;
 
   // ---- LDS: key part kh owns 4 tile buffers (bytes): K parity 0, V parity 0, K parity 1,
   // V parity 1.  All read and write addresses are a per-lane register plus a constant.
@@ -379,34 +387,49 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       s[1][rr] = kl + 32 < lim ? s[1][rr] : -INFINITY;
     }
   };
-  auto rescale = [&](float m_new) {
-    const float alpha = fast_exp2(m_run - m_new);
+  // exp2 of the two scores of pair e (kp4 = e/4, element e%4) of a tile, packed
+  auto pack_pair = [&](const f32x16 (&x)[2], int e) -> uint32_t {
+    const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+    return pack2<T>(fast_exp2(x[mb][r0 + 2 * ee]), fast_exp2(x[mb][r0 + 2 * ee + 1]));
+  };
+  // Probabilities of tile x (packed as the four B operands of the PV product) and this
+  // lane's half of their row sum, which adds the rounded values (the ones PV uses) two
+  // at a time with a dot product against (1, 1).
+  auto probs = [&](const f32x16 (&x)[2], u32x4 (&pw)[4]) -> float {
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      pw[e >> 2][e & 3] = pack_pair(x, e);
+      if (e & 1) ls1 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls1);
+      else ls0 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls0);
+    }
+    return ls0 + ls1;
+  };
+  // Rare path: some score of tile x lies more than about 2^8 above the row's reference.
+  // The reference moves up to the tile's row maximum: the output and the sum so far are
+  // rescaled and the tile's probabilities recomputed.
+  auto raise_reference = [&](f32x16 (&x)[2], u32x4 (&pw)[4]) -> float {
+    float mx = fmaxf(x[0][0], x[1][0]);
+#pragma unroll
+    for (int rr = 1; rr < 16; ++rr) mx = fmaxf(mx, fmaxf(x[0][rr], x[1][rr]));
+    const float d = fmaxf(halves_max(mx), 0.f);     // rows that stay below keep their reference
+    const float alpha = fast_exp2(-d);
     l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) o[db][rr] *= alpha;
-  };
-  // probabilities, packed as the B operand of the PV product; row sums add the rounded
-  // values (the ones PV uses) two at a time with a dot product against (1, 1)
-  auto probs = [&](const f32x16* x, s16x8* pk) {
-    float ls0 = 0.f, ls1 = 0.f;
+    m_run += d;
 #pragma unroll
-    for (int kp4 = 0; kp4 < 4; ++kp4) {
-      const int mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
-      u32x4 pw;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pw[e] = pack2<T>(fast_exp2(x[mb][r0 + 2 * e]), fast_exp2(x[mb][r0 + 2 * e + 1]));
-        if (e & 1) ls1 = T::dot2(pw[e], T::kOnePair, ls1);
-        else ls0 = T::dot2(pw[e], T::kOnePair, ls0);
-      }
-      pk[kp4] = __builtin_bit_cast(s16x8, pw);
+    for (int rr = 0; rr < 16; ++rr) {
+      x[0][rr] -= d;
+      x[1][rr] -= d;
     }
-    l_run += ls0 + ls1;
+    return probs(x, pw);
   };
 
-  // ---- prologue: K and V of step 0, K of step 1; scores of step 0
+  // ---- prologue: K and V of step 0, K of step 1; scores of step 0, whose row maximum is
+  // the first reference
   refill(0);
   issue_all(desc(0, false, kOffK0), false, Gen{});
   issue_all(desc(0, true, kOffV0), true, Gen{});
@@ -426,8 +449,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     float m = fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
     for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s_cur[0][rr], s_cur[1][rr]));
-    // the first tile always sets the reference (m_run starts far below any score)
-    m_run = fmaxf(m_run, halves_max(m) * c_log2);
+    m = halves_max(m) * c_log2;
+    // a row with no visible key in its first tile has none in the later ones either
+    // (visibility only shrinks with the key index); its reference stays 0
+    m_run = m == -INFINITY ? 0.f : m;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       s_cur[0][rr] = fmaf(s_cur[0][rr], c_log2, -m_run);
@@ -461,11 +486,13 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     // Hand-interleaved: each step of a phase is a scheduling region of its own, so
     // operand reads issued there stay two MFMA steps ahead of their use and the VALU
     // work of the other tile fills the MFMA shadow.
-    // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack), loads.
+    // Phase 1: S MFMAs of tile j+1, probabilities of tile j (exp + pack) and their row
+    // sums, loads.
     f32x16 s_nxt[2] = {f32x16{}, f32x16{}};
     s16x8 ka[NKK][2];
     // probabilities of tile j, written in place as the four B operands of the PV product
     u32x4 pw[4];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2 && kk < NKK; ++kk) {
       ka[kk][0] = k_operand(offK_rd, kk, 0);
@@ -485,32 +512,42 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       s_nxt[0] = T::mfma32(ka[kk][0], qreg[kk], s_nxt[0]);
       s_nxt[1] = T::mfma32(ka[kk][1], qreg[kk], s_nxt[1]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e)                // pair e = (kp4 = e/4, element e%4)
+      for (int e = 0; e < 16; ++e) {              // pair e = (kp4 = e/4, element e%4)
         if (e * NKK / 16 == kk) {
-          const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
           // each packed word is pinned here, in phase 1: pinning the assembled operand
           // instead made the compiler rebuild it with copies before the PV product
-          uint32_t w2 = pack2<T>(fast_exp2(s_cur[mb][r0 + 2 * ee]), fast_exp2(s_cur[mb][r0 + 2 * ee + 1]));
+          uint32_t w2 = pack_pair(s_cur, e);
           asm volatile("" : "+v"(w2));
-          pw[kp4][ee] = w2;
+          pw[e >> 2][e & 3] = w2;
         }
+        if (kk > 0 && e * NKK / 16 == kk - 1) {   // row sums one MFMA step behind
+          if (e & 1) ls1 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls1);
+          else ls0 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls0);
+        }
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    s16x8 pk[4];
 #pragma unroll
-    for (int kp4 = 0; kp4 < 4; ++kp4) pk[kp4] = __builtin_bit_cast(s16x8, pw[kp4]);
+    for (int e = 0; e < 16; ++e)
+      if (e * NKK / 16 == NKK - 1) {
+        if (e & 1) ls1 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls1);
+        else ls0 = T::dot2(pw[e >> 2][e & 3], T::kOnePair, ls0);
+      }
     if (need_mask) {
       keep_branch();
       mask(t_begin + KS * (j + 1) + kh, s_nxt);
     }
-    // Phase 2: PV MFMAs of tile j; row sums of tile j, row max and exp2 arguments of
-    // tile j+1.  VALU work units: 0-3 partial maxima, 4 the wave-wide max and the new
-    // reference, 5-12 scaled scores (4 each), 13-16 row sums (4 dot products each).
-    constexpr int NU = 17;
+    float ls = ls0 + ls1;
+    if (__any(!(ls <= kPfSumLimit))) {
+      keep_branch();
+      ls = raise_reference(s_cur, pw);
+    }
+    l_run += ls;
+    s16x8 pk[4];
+#pragma unroll
+    for (int kp4 = 0; kp4 < 4; ++kp4) pk[kp4] = __builtin_bit_cast(s16x8, pw[kp4]);
+    // Phase 2: PV MFMAs of tile j; exp2 arguments of tile j+1 (four per unit).
     s16x8 va[NPV];
-    float pmax[4], m_new = m_run, ls[4];
-    bool any = false;
 #pragma unroll
     for (int i = 0; i < 2; ++i) va[i] = v_operand(offV_rd, i >> 2, i & 3);
 #pragma unroll
@@ -519,39 +556,15 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       if (i + 2 < NPV) va[i + 2] = v_operand(offV_rd, (i + 2) >> 2, (i + 2) & 3);
       o[i >> 2] = T::mfma32(va[i], pk[i & 3], o[i >> 2]);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (u * NPV / NU != i) continue;
-        if (u < 4) {
-          const int h = u >> 1, r0 = (u & 1) * 8;
-          float m = fmaxf(s_nxt[h][r0], s_nxt[h][r0 + 1]);
+      for (int u = 0; u < 8; ++u) {
+        if (u * NPV / 8 != i) continue;
+        const int h = u >> 2, r0 = (u & 3) * 4;
 #pragma unroll
-          for (int rr = 2; rr < 8; ++rr) m = fmaxf(m, s_nxt[h][r0 + rr]);
-          pmax[u] = m;
-        } else if (u == 4) {
-          const float mx = halves_max(fmaxf(fmaxf(pmax[0], pmax[1]), fmaxf(pmax[2], pmax[3]))) * c_log2;
-          any = __any(mx > m_run + kPfRescale);
-          m_new = any ? fmaxf(m_run, mx) : m_run;
-        } else if (u < 13) {
-          const int h = (u - 5) >> 2, r0 = ((u - 5) & 3) * 4;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_new);
-        } else {
-          const int k0 = (u - 13) * 4;
-          float a = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a = T::dot2(pw[k0 >> 2][e], T::kOnePair, a);
-          ls[u - 13] = a;
-        }
+        for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_run);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));   // scaled scores stay in phase 2
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    if (any) {
-      keep_branch();
-      rescale(m_new);
-    }
-    m_run = m_new;
 #pragma unroll
     for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
   };
@@ -587,10 +600,16 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // last tile: probabilities and PV (V buffer parity of the last step)
   auto last = [&](auto par_c) {
     constexpr uint32_t off = decltype(par_c)::value ? kOffV1 : kOffV0;
-    s16x8 pk[4];
-    probs(s_cur, pk);
+    u32x4 pw[4];
+    float ls = probs(s_cur, pw);
+    if (__any(!(ls <= kPfSumLimit))) {
+      keep_branch();
+      ls = raise_reference(s_cur, pw);
+    }
+    l_run += ls;
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) o[i >> 2] = T::mfma32(v_operand(off, i >> 2, i & 3), pk[i & 3], o[i >> 2]);
+    for (int i = 0; i < NPV; ++i)
+      o[i >> 2] = T::mfma32(v_operand(off, i >> 2, i & 3), __builtin_bit_cast(s16x8, pw[i & 3]), o[i >> 2]);
   };
   if (wave_active) {
     if (j & 1) last(std::integral_constant<int, 1>{});
@@ -663,9 +682,12 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr int OPW = NDB * 16;                    // output floats per lane
   static_assert(KS == 1 || (kRowWaves * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
   float* my = mbuf + rw * (OPW + 2) * 64;
+  // a row that saw no key here (sum 0) takes a reference far below any other, so a merge
+  // with another part of its keys gives it no weight
+  const float l_row = halves_sum(l_run);
+  if (l_row == 0.f) m_run = kPfNegBig;
   if (KS == 1) {
-    const float lt = halves_sum(l_run);
-    emit([&](int db, int rr) { return o[db][rr]; }, m_run, lt);
+    emit([&](int db, int rr) { return o[db][rr]; }, m_run, l_row);
     return;
   }
   __syncthreads();                                  // every wave is done with the tiles
