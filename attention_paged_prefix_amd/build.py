@@ -17,6 +17,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvb.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "scatter_gather.hip", "quant.hip", "decode.hip", "prefill.hip"]
+# benchmark probes (peak MFMA rate, HBM read stream, cache flush): a library of their own,
+# not part of the kvb C ABI
+PROBE_SOURCE = "probe.hip"
+PROBE_OUT = os.path.join(PKG, "libkvb_probe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -58,16 +62,18 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC] + flags + KERNEL_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
+    probe_obj = os.path.join(BUILD_DIR, PROBE_SOURCE.replace(".hip", ".o"))
+    cmds.append([HIPCC] + flags + ["-c", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_obj])
     with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
         for cmd, _ in zip(cmds, ex.map(_run, cmds)):
             if verbose:
                 print(" ".join(cmd))
-    tmp = OUT + ".tmp"
-    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
-    _run(link)
-    os.replace(tmp, OUT)
-    if verbose:
-        print("built", OUT)
+    for out, ob in ((OUT, objs), (PROBE_OUT, [probe_obj])):
+        tmp = out + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + ob)
+        os.replace(tmp, out)
+        if verbose:
+            print("built", out)
     return OUT
 
 

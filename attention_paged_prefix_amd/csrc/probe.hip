@@ -1,0 +1,90 @@
+// Measurement probes for the benchmark (libkvb_probe.so; not part of the kvb C ABI):
+//  * kvb_probe_read: every byte of a device buffer read once with 16-byte loads, the
+//    HBM read stream the decode kernel is bounded by (also used to evict L2 and the
+//    Infinity Cache between timed launches; reading, unlike writing, leaves no dirty
+//    lines whose write-back would be charged to the next kernel);
+//  * kvb_probe_mfma: independent v_mfma_f32_32x32x16_bf16 chains on every SIMD, the dense
+//    16-bit matrix rate the chip sustains at the clocks it holds under that load.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kReadThreads = 256;
+
+__global__ void __launch_bounds__(kReadThreads)
+read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kReadThreads;
+  uint64_t i = (uint64_t)blockIdx.x * kReadThreads + threadIdx.x;
+  // four loads in flight per lane
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  // the sum is kept alive by a store that never happens for real data (sink[0] is the
+  // caller's; a single lane writes only if the xor equals a value it cannot predict)
+  if (acc == 0x9e3779b9u && threadIdx.x == 0) sink[0] = acc;
+}
+
+constexpr int kMfmaChains = 4;
+
+__global__ void __launch_bounds__(256)
+mfma_kernel(int iters, uint32_t* __restrict__ sink) {
+  const int t = threadIdx.x;
+  s16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (short)(0x3c00 + ((t + e) & 7));       // small finite bf16 values
+    b[e] = (short)(0x3c00 + ((t * 3 + e) & 7));
+  }
+  f32x16 acc[kMfmaChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kMfmaChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (s == -1.0f) sink[0] = 1u;                     // keeps the chains alive; never true
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) at `buf` (16-byte aligned, device).  `sink`: one
+// device uint32 that is written only in a case that cannot occur for real data.
+int kvb_probe_read(const void* buf, uint64_t bytes, uint32_t* sink, int blocks, void* stream) {
+  if (!buf || !sink || (bytes & 15) || ((uintptr_t)buf & 15) || blocks <= 0) return 2;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, (hipStream_t)stream,
+                     (const uint4*)buf, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// `blocks` work-groups of 4 waves, each wave `iters` x 4 MFMAs of 32x32x16 (32768 flops
+// each).  Returns 0 on a successful launch.
+int kvb_probe_mfma(int iters, int blocks, uint32_t* sink, void* stream) {
+  if (iters <= 0 || blocks <= 0 || !sink) return 2;
+  hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// Flops of one kvb_probe_mfma launch.
+double kvb_probe_mfma_flops(int iters, int blocks) {
+  return (double)blocks * 4.0 * iters * kMfmaChains * 32768.0;
+}
+
+}  // extern "C"
