@@ -3,8 +3,9 @@
 //    HBM read stream the decode kernel is bounded by (also used to evict L2 and the
 //    Infinity Cache between timed launches; reading, unlike writing, leaves no dirty
 //    lines whose write-back would be charged to the next kernel);
-//  * kvb_probe_mfma: independent v_mfma_f32_32x32x16_bf16 chains on every SIMD, the dense
-//    16-bit matrix rate the chip sustains at the clocks it holds under that load.
+//  * kvb_probe_mfma: independent v_mfma_f32_32x32x16_bf16 chains on every SIMD over random
+//    operand data, the dense 16-bit matrix rate the chip sustains at the clocks it holds
+//    under that load.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,30 +36,39 @@ read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* __restrict__ si
 }
 
 constexpr int kMfmaChains = 4;
+constexpr int kMfmaSets = 8;         // operand register sets cycled through
 
+// Independent MFMA chains.  The operands are `kMfmaSets` pairs of 16-byte fragments per
+// lane taken from `ops` (random 16-bit data from the caller), cycled every MFMA, so the
+// matrix core switches realistic bit patterns; constant operands draw far less power and
+// let the chip hold clocks that real data does not.
 __global__ void __launch_bounds__(256)
-mfma_kernel(int iters, uint32_t* __restrict__ sink) {
+mfma_kernel(int iters, const uint4* __restrict__ ops, uint32_t* __restrict__ sink) {
   const int t = threadIdx.x;
-  s16x8 a, b;
+  s16x8 a[kMfmaSets], b[kMfmaSets];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    a[e] = (short)(0x3c00 + ((t + e) & 7));       // small finite bf16 values
-    b[e] = (short)(0x3c00 + ((t * 3 + e) & 7));
+  for (int k = 0; k < kMfmaSets; ++k) {
+    a[k] = __builtin_bit_cast(s16x8, ops[(2 * k) * 256 + t]);
+    b[k] = __builtin_bit_cast(s16x8, ops[(2 * k + 1) * 256 + t]);
   }
   f32x16 acc[kMfmaChains];
 #pragma unroll
   for (int c = 0; c < kMfmaChains; ++c) acc[c] = f32x16{};
-  for (int i = 0; i < iters; ++i) {
+  for (int i = 0; i < iters; i += 2) {
 #pragma unroll
-    for (int c = 0; c < kMfmaChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < kMfmaChains; ++c) {
+        const int k = (u * kMfmaChains + c) % kMfmaSets;
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[(k + 3) % kMfmaSets], acc[c], 0, 0, 0);
+      }
   }
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kMfmaChains; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
-  if (s == -1.0f) sink[0] = 1u;                     // keeps the chains alive; never true
+  if (s == 1.2345e30f) sink[0] = 1u;                // keeps the chains alive; never true
 }
 
 }  // namespace
@@ -74,11 +84,13 @@ int kvb_probe_read(const void* buf, uint64_t bytes, uint32_t* sink, int blocks, 
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
-// `blocks` work-groups of 4 waves, each wave `iters` x 4 MFMAs of 32x32x16 (32768 flops
-// each).  Returns 0 on a successful launch.
-int kvb_probe_mfma(int iters, int blocks, uint32_t* sink, void* stream) {
-  if (iters <= 0 || blocks <= 0 || !sink) return 2;
-  hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, iters, sink);
+// `blocks` work-groups of 4 waves, each wave `iters` (even) x 4 MFMAs of 32x32x16 (32768
+// flops each) on operands read from `ops`: (device) 16 x 256 x 16 bytes of 16-bit data.
+// Returns 0 on a successful launch.
+int kvb_probe_mfma(int iters, int blocks, const void* ops, uint32_t* sink, void* stream) {
+  if (iters <= 0 || (iters & 1) || blocks <= 0 || !sink || !ops || ((uintptr_t)ops & 15)) return 2;
+  hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, iters,
+                     (const uint4*)ops, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

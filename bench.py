@@ -268,13 +268,17 @@ class Probe:
         lib = ctypes.CDLL(path)
         lib.kvb_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p]
-        lib.kvb_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.kvb_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         lib.kvb_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.kvb_probe_mfma_flops.restype = ctypes.c_double
         self.lib = lib
         self.torch = torch
         self.buf = torch.ones(FLUSH_BYTES // 2, dtype=torch.int16, device="cuda:0")
         self.sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+        # MFMA operands: N(0,1) values rounded to bf16 (realistic bit toggling)
+        g = torch.Generator().manual_seed(0)
+        self.ops = torch.randn(16 * 256 * 8, generator=g).to(torch.bfloat16).to("cuda:0")
         self.cus = torch.cuda.get_device_properties(0).multi_processor_count
 
     def _stream(self):
@@ -288,7 +292,8 @@ class Probe:
             raise RuntimeError(f"kvb_probe_read failed ({rc})")
 
     def mfma(self, iters, blocks):
-        rc = self.lib.kvb_probe_mfma(iters, blocks, self.sink.data_ptr(), self._stream())
+        rc = self.lib.kvb_probe_mfma(iters, blocks, self.ops.data_ptr(), self.sink.data_ptr(),
+                                     self._stream())
         if rc:
             raise RuntimeError(f"kvb_probe_mfma failed ({rc})")
 
@@ -305,8 +310,8 @@ class Probe:
         rms = time_each(torch, self.flush, 10)
         return {"mfma_bf16_tflops": fl / (np.median(ms) * 1e-3) / 1e12,
                 "mfma_probe": f"{blocks} work-groups x 4 waves x {iters} x 4 independent "
-                              f"v_mfma_f32_32x32x16_bf16, median of 10 launches of "
-                              f"{np.median(ms):.3f} ms",
+                              f"v_mfma_f32_32x32x16_bf16 on random N(0,1) bf16 operands, median "
+                              f"of 10 launches of {np.median(ms):.3f} ms",
                 "hbm_read_gbps": FLUSH_BYTES / (np.median(rms) * 1e-3) / 1e9,
                 "hbm_probe": f"1 GiB read with 16-byte loads, median of 10 launches of "
                              f"{np.median(rms):.3f} ms",
