@@ -19,9 +19,13 @@
  *     The library allocates nothing, never synchronises, never reads device memory
  *     on the host and keeps no state: calls are thread-safe and asynchronous on
  *     `stream` (a hipStream_t; NULL = the null stream).
- *   - Arguments are validated on the host before any HIP call.  A failed check
+ *   - Arguments are validated on the host before any launch.  A failed check
  *     returns KVB_ERR_NULL / KVB_ERR_INVALID / KVB_ERR_UNSUPPORTED /
- *     KVB_ERR_WORKSPACE and launches nothing.  A failed launch returns KVB_ERR_LAUNCH.
+ *     KVB_ERR_WORKSPACE and launches nothing.  The only HIP calls validation and
+ *     planning make are queries: the current device and its compute-unit count (the
+ *     decode split plan and the prefill's grid form depend on it) and, in
+ *     kvb_copy_blocks, the attributes of the pool pointers.  A failed launch returns
+ *     KVB_ERR_LAUNCH.
  *   - Device pointers must be 16-byte aligned (KVB_ERR_INVALID otherwise).
  *   - Device-side index contents are the caller's contract (no device-to-host read
  *     checks them).  The kernels are nevertheless memory-safe against bad indices:
@@ -201,7 +205,11 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
                                     int32_t max_context_len, int32_t split_blocks, float scale,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace sizes in bytes (0 = none needed).  Pure host arithmetic. */
+/* Workspace sizes in bytes (0 = none needed).  Host arithmetic on the arguments and the
+ * current device's compute-unit count (the decode split plan aims at a number of
+ * work-groups per compute unit), so a size holds for the device that is current when it
+ * is queried; call the size query and the decode with the same device current.  The
+ * decode sizes take num_kv_heads too: the split plan counts (sequence, KV head) units. */
 size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                         int32_t total_q, int32_t max_prefix_len);
 size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,

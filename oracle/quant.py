@@ -52,13 +52,6 @@ def token_scale(v: np.ndarray, code_max: int = CODE_MAX) -> np.ndarray:
     return np.divide(a, np.float32(code_max), dtype=np.float32)
 
 
-def channel_scales(k_tokens: np.ndarray, code_max: int = CODE_MAX) -> np.ndarray:
-    """A K scale per (KV head, channel) from example tokens ``[n][Hkv][d]`` (float32):
-    max over the tokens of |k| / code_max.  One way a caller can pick the pool's K scales."""
-    a = np.abs(np.asarray(k_tokens, dtype=np.float32)).max(axis=0)
-    return np.divide(a, np.float32(code_max), dtype=np.float32)
-
-
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
     """4-bit codes ``[..][d]`` (int8 in [-7, 7]) as stored bytes ``[..][d/2]``: channel 2i
     in the low nibble, 2i+1 in the high nibble, each a 4-bit two's complement."""

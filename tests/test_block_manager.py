@@ -25,6 +25,23 @@ def test_fork_shares_blocks_and_append_copies_on_write():
     assert s["used_blocks"] == 4 and s["shared_blocks"] == 2 and s["free_blocks"] == 12
 
 
+def test_stats_match_the_pages_pool_example():
+    """kvboost 0.6.0, "CPU paged attention": a pool of 8192 16-token blocks with 1024 of
+    them in use reports a block utilisation of 0.12 (printed to two places; 1024/8192 is
+    0.125), 7168 free blocks and 1024 used ones."""
+    m = BlockManager(8192)
+    m.allocate("prompt", 2048 * 16)                  # 2048 blocks, then fork: shared, not new
+    m.fork("prompt", "request")
+    m.free("prompt")
+    m.free("request")
+    for i in range(8):
+        m.allocate(i, 128 * 16)                      # 8 x 128 blocks
+    s = m.stats()
+    assert s["used_blocks"] == 1024
+    assert s["free_blocks"] == 7168
+    assert s["block_utilization"] == 0.125 and round(s["block_utilization"], 2) == 0.12
+
+
 def test_append_at_block_boundary_takes_a_new_block():
     m = BlockManager(4)
     m.allocate("a", 32)

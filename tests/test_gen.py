@@ -82,3 +82,21 @@ def test_ragged_statistics(name, stats):
     assert int(w.q_lens.sum()) == stats[1]
     assert (w.q_lens % 16 != 0).all() and w.q_lens.min() >= 1 and w.q_lens.max() <= 512
     assert round(w.shared_fraction, 3) == stats[2]
+
+
+def test_channel_scales_hand_values():
+    """The K scales picked from example tokens: per (head, channel) the largest |k| over
+    the tokens divided by the largest code, in float32 (values chosen so the quotients
+    are exact)."""
+    from workloads import channel_scales
+    k = np.zeros((3, 2, 4), np.float32)
+    k[0, 0] = [127.0, -254.0, 0.0, 63.5]
+    k[1, 0] = [-12.0, 100.0, 0.0, -63.5]
+    k[2, 1] = [7.0, -3.5, 0.875, 0.0]
+    s8 = channel_scales(k)
+    assert s8.dtype == np.float32
+    assert s8[0].tolist() == [1.0, 2.0, 0.0, 0.5]
+    assert s8[1].tolist() == [np.float32(7.0) / np.float32(127), np.float32(3.5) / np.float32(127),
+                              np.float32(0.875) / np.float32(127), 0.0]
+    s4 = channel_scales(k, 7)
+    assert s4[1].tolist() == [1.0, 0.5, 0.125, 0.0]

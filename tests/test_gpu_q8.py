@@ -5,7 +5,7 @@ Every expected value comes from the oracle's own quantisation of the 16-bit inpu
 import numpy as np
 import pytest
 
-from workloads import make_config, make_custom
+from workloads import make_config, make_custom, channel_scales
 from workloads.gen import round_to_bits
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +65,7 @@ def test_write_kv_q8_bit_exact(dt, d, hkv):
     V = rng.standard_normal((T, hkv, d)) * mag
     V[7] = 0.0                                            # a zero token: scale 0, codes 0
     kb, vb = round_to_bits(K, dt), round_to_bits(V, dt)
-    k_scale = quant.channel_scales(oracle_f32(kb, dt)) * np.float32(0.8)   # some codes clamp
+    k_scale = channel_scales(oracle_f32(kb, dt)) * np.float32(0.8)   # some codes clamp
     k_scale[0, 3] = 0.0                                   # a zero channel scale
     slots = rng.permutation(nb * 16)[:T].astype(np.int64)
     slots[[2, 50]] = -1
@@ -101,7 +101,7 @@ def _oracle_q8_pool(w, slots):
     every context slot written by the oracle, the other slots poisoned."""
     from oracle import quant
     kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
-    k_scale = quant.channel_scales(oracle_f32(kt, w.dtype))
+    k_scale = channel_scales(oracle_f32(kt, w.dtype))
     kc, vc, vs = _poisoned(w.k_pool.shape[0], w.num_kv_heads, w.head_dim)
     kc, vc, vs = quant.write_kv_q8(kc, vc, vs, k_scale, kt, vt, slots, w.dtype)
     return kc, vc, vs, k_scale, kt, vt
@@ -164,7 +164,7 @@ def test_decode_q8_full_size_sampled():
     w = make_config("decode")
     slots = _context_slots(w)
     kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
-    ks = quant.channel_scales(oracle_f32(kt, "bf16"))
+    ks = channel_scales(oracle_f32(kt, "bf16"))
     pk, pv, ps = _poisoned(w.k_pool.shape[0], 8, 128)
     pool = _pool_q8(pk, pv, ps, ks)
     kvb.write_kv_q8(pool, u.to_dev(kt, "bf16"), u.to_dev(vt, "bf16"), u.idev(slots, torch.int64))
@@ -210,7 +210,7 @@ def test_prefill_q8_matches_oracle(case):
     w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=False)
     slots = _prefix_slots(w)
     kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
-    ks = quant.channel_scales(oracle_f32(kt, dt)) if len(slots) else np.full((hkv, d), 0.01, np.float32)
+    ks = channel_scales(oracle_f32(kt, dt)) if len(slots) else np.full((hkv, d), 0.01, np.float32)
     kc, vc, vs = _poisoned(w.k_pool.shape[0], hkv, d)
     kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, kt, vt, slots, dt)
     pool = _pool_q8(kc, vc, vs, ks)
@@ -257,7 +257,7 @@ def test_write_kv_q4_bit_exact(dt, d, hkv):
     V = rng.standard_normal((T, hkv, d)) * mag
     V[9] = 0.0
     vb = round_to_bits(V, dt)
-    ks = quant.channel_scales(oracle_f32(kb, dt), quant.CODE_MAX4) * np.float32(0.7)
+    ks = channel_scales(oracle_f32(kb, dt), quant.CODE_MAX4) * np.float32(0.7)
     ks[0, 5] = 0.0
     slots = rng.permutation(nb * 16)[:T].astype(np.int64)
     slots[[3, 40]] = -1
@@ -276,7 +276,7 @@ def test_write_kv_q4_bit_exact(dt, d, hkv):
 def _oracle_q4_pool(w, slots):
     from oracle import quant
     kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
-    ks = quant.channel_scales(oracle_f32(kt, w.dtype), quant.CODE_MAX4) if len(slots) \
+    ks = channel_scales(oracle_f32(kt, w.dtype), quant.CODE_MAX4) if len(slots) \
         else np.full((w.num_kv_heads, w.head_dim), 0.1, np.float32)
     kc, vc, vs = _poisoned4(w.k_pool.shape[0], w.num_kv_heads, w.head_dim)
     kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, kt, vt, slots, w.dtype, quant.CODE_MAX4)

@@ -66,7 +66,6 @@ def test_channel_scale_only_moves_its_channel():
     c2 = quant.quantize(x, s2)
     diff = np.argwhere(c1 != c2)
     assert len(diff) > 0 and (diff[:, 1] == 1).all() and (diff[:, 2] == 7).all()
-    assert np.array_equal(quant.channel_scales(x), (np.abs(x).max(axis=0) / np.float32(127)).astype(np.float32))
 
 
 def _exact_pool(rng, dtype, nb, hkv, d, n_tok):

@@ -333,3 +333,11 @@ def make_custom(seed: int, dtype: str, num_q_heads: int, num_kv_heads: int, head
 
 def make(name: str, **kw) -> Workload:
     return make_config(name, **kw)
+
+
+def channel_scales(k_tokens: np.ndarray, code_max: int = 127) -> np.ndarray:
+    """Input choice for a quantised pool: a K scale per (KV head, channel) from example
+    tokens ``[n][Hkv][d]`` (float32), the largest |k| over the tokens divided by the
+    largest code (127 for 8-bit codes, 7 for 4-bit ones), in float32."""
+    a = np.abs(np.asarray(k_tokens, dtype=np.float32)).max(axis=0)
+    return np.divide(a, np.float32(code_max), dtype=np.float32)
