@@ -123,3 +123,56 @@ def test_prefill_write_full_size(name):
     ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping)
     assert np.array_equal(u.to_bits(dev.k), ek)
     assert np.array_equal(u.to_bits(dev.v), ev)
+
+
+def _tile_edge_rows(C, G, tile_rows=128):
+    """First and last virtual row (v = i*G + g) of every tile of `tile_rows` virtual rows
+    of one (sequence, KV head): the prefill's work items."""
+    n = C * G
+    rows = set()
+    for t0 in range(0, n, tile_rows):
+        rows.add(t0)
+        rows.add(min(n, t0 + tile_rows) - 1)
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["ragged_d96", "long_prefix", "ragged_d64", "shared_prompt"])
+def test_prefill_full_size_every_work_item(name):
+    """Every (sequence, KV head, 128-row tile) work item that the dispatch plan orders is
+    checked at its first and last row, with the fused slot scatter and the dispatch plan
+    as the benchmark step runs them (ragged_d96 with the benchmark's decode-step layout)."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    w = make_config(name, poison=True, with_decode=(name == "ragged_d96"))
+    dev = u.Dev(w)
+    out = kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,
+                            int(w.q_lens.max()), int(w.prefix_lens.max()), slot_mapping=dev.slots)
+    torch.cuda.synchronize()
+    vals = oracle.decode_bits(u.to_bits(out), w.dtype)
+    assert np.isfinite(vals).all()
+    G = w.num_q_heads // w.num_kv_heads
+    worst, checked = 0.0, 0
+    for b in range(w.batch):
+        C, P = int(w.q_lens[b]), int(w.prefix_lens[b])
+        if C == 0:
+            continue
+        c0 = int(w.cu_q_lens[b])
+        for kvh in range(w.num_kv_heads):
+            # the sequence's keys for this KV head: cached prefix through the table, then
+            # the chunk's own rows
+            K = np.concatenate([oracle.decode_bits(oracle.gather_kv(w.k_pool, w.block_tables[b], P)[:, kvh], w.dtype),
+                                oracle.decode_bits(w.k_new[c0:c0 + C, kvh], w.dtype)])
+            V = np.concatenate([oracle.decode_bits(oracle.gather_kv(w.v_pool, w.block_tables[b], P)[:, kvh], w.dtype),
+                                oracle.decode_bits(w.v_new[c0:c0 + C, kvh], w.dtype)])
+            by_head = {}
+            for v in _tile_edge_rows(C, G):
+                by_head.setdefault(kvh * G + v % G, []).append(v // G)
+            for h, rows in by_head.items():
+                rows = np.asarray(rows)
+                ref, _ = oracle.attend(oracle.decode_bits(w.q[c0 + rows, h], w.dtype), K, V, P + rows,
+                                       w.scale)
+                worst = max(worst, float(np.max(np.abs(vals[c0 + rows, h] - ref))))
+                checked += len(rows)
+    assert checked > 0
+    assert worst <= u.TOL[w.dtype], f"max abs err {worst} over {checked} rows"
