@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvb.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "scatter_gather.hip", "quant.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "scatter_gather.hip", "quant.hip", "decode.hip", "decode_stream.hip",
+           "prefill.hip"]
 # benchmark probes (peak MFMA rate, HBM read stream, cache flush): a library of their own,
 # not part of the kvb C ABI
 PROBE_SOURCE = "probe.hip"
@@ -43,6 +44,7 @@ FLAGS = [
 KERNEL_FLAGS = {
     "prefill.hip": ["-fno-honor-nans"],
     "decode.hip": ["-fno-honor-nans"],
+    "decode_stream.hip": ["-fno-honor-nans"],
 }
 
 

@@ -44,6 +44,35 @@ kvb_status check_scale(float scale) {
 
 kvb_status launch_status(hipError_t e) { return e == hipSuccess ? KVB_OK : KVB_ERR_LAUNCH; }
 
+// Decode plan: the balanced stream form for batches it covers, else the split form.
+struct DecodePlan {
+  bool stream;
+  int sb, ns;             // split form
+  kvb::StreamPlan sp;     // stream form
+  int64_t bytes;          // workspace
+};
+DecodePlan decode_plan_for(int batch, int hkv, int hq, int d, int max_ctx, int split_blocks) {
+  DecodePlan r{};
+  r.stream = kvb::decode_use_stream(batch);
+  if (r.stream) {
+    r.sp = kvb::decode_stream_plan(batch, hkv, hq, d, max_ctx, split_blocks);
+    r.bytes = r.sp.bytes;
+  } else {
+    kvb::decode_plan(batch, hkv, hq, max_ctx, split_blocks, &r.sb, &r.ns);
+    r.bytes = kvb::decode_ws_bytes(batch, hq, d, r.ns);
+  }
+  return r;
+}
+hipError_t launch_decode_plan(const DecodePlan& pl, const kvb_pool& p, const void* q, void* out,
+                              const int32_t* ctx, const int32_t* bt, int bt_stride, int batch,
+                              int hq, int max_ctx, float scale, void* ws, hipStream_t s) {
+  if (pl.stream)
+    return kvb::launch_decode_stream(p, 0, kvb::DecScales{nullptr, nullptr}, q, out, ctx, bt,
+                                     bt_stride, batch, hq, max_ctx, pl.sp, scale, ws, s);
+  return kvb::launch_decode(p, q, out, ctx, bt, bt_stride, batch, hq, max_ctx, pl.sb, pl.ns, scale,
+                           ws, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,9 +212,8 @@ size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int3
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
       max_context_len <= 0 || split_blocks < 0)
     return 0;
-  int sb = 0, ns = 0;
-  kvb::decode_plan(batch, num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
-  return (size_t)kvb::decode_ws_bytes(batch, num_q_heads, head_dim, ns);
+  return (size_t)decode_plan_for(batch, num_kv_heads, num_q_heads, head_dim, max_context_len,
+                                 split_blocks).bytes;
 }
 
 kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
@@ -206,14 +234,14 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
     return KVB_ERR_INVALID;
   if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
     return KVB_ERR_INVALID;
-  int sb = 0, ns = 0;
-  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
-  const size_t need = (size_t)kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
+  const DecodePlan pl = decode_plan_for(batch, pool->num_kv_heads, num_q_heads, pool->head_dim,
+                                        max_context_len, split_blocks);
+  const size_t need = (size_t)pl.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return KVB_ERR_INVALID;
-  return launch_status(kvb::launch_decode(*pool, q, out, context_lens, block_tables,
+  return launch_status(launch_decode_plan(pl, *pool, q, out, context_lens, block_tables,
                                           block_table_stride, batch, num_q_heads, max_context_len,
-                                          sb, ns, scale, workspace, (hipStream_t)stream));
+                                          scale, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -268,16 +296,16 @@ kvb_status kvb_paged_decode_noalloc(const kvb_pool* pool, const void* q, void* o
     return KVB_ERR_INVALID;
   if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
     return KVB_ERR_INVALID;
-  int sb = 0, ns = 0;
-  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
-  const int64_t need = kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
-  if (need > (int64_t)KVB_NOALLOC_SCRATCH_BYTES) return KVB_ERR_TOO_LARGE;
+  const DecodePlan pl = decode_plan_for(batch, pool->num_kv_heads, num_q_heads, pool->head_dim,
+                                        max_context_len, split_blocks);
+  if (pl.bytes > (int64_t)KVB_NOALLOC_SCRATCH_BYTES) return KVB_ERR_TOO_LARGE;
   void* ws = nullptr;
-  if (need > 0 && !(ws = scratch_address())) return KVB_ERR_LAUNCH;
-  // the split kernels write every partial the merge reads: nothing needs clearing
-  return launch_status(kvb::launch_decode(*pool, q, out, context_lens, block_tables,
+  if (pl.bytes > 0 && !(ws = scratch_address())) return KVB_ERR_LAUNCH;
+  // the decode kernels write everything the merge reads (header and partial records)
+  // before it runs: nothing needs clearing
+  return launch_status(launch_decode_plan(pl, *pool, q, out, context_lens, block_tables,
                                           block_table_stride, batch, num_q_heads, max_context_len,
-                                          sb, ns, scale, ws, (hipStream_t)stream));
+                                          scale, ws, (hipStream_t)stream));
 }
 
 // Plan of a cascade decode: the private splits, and the shared prefix either in group
@@ -397,14 +425,22 @@ static kvb_status decode_quant(const kvb_pool_q8* pool, int bits, int32_t dtype,
     return KVB_ERR_INVALID;
   if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride <= 0)
     return KVB_ERR_INVALID;
-  int sb = 0, ns = 0;
-  kvb::decode_plan(batch, pool->num_kv_heads, num_q_heads, max_context_len, split_blocks, &sb, &ns);
-  const size_t need = (size_t)kvb::decode_ws_bytes(batch, num_q_heads, pool->head_dim, ns);
+  const DecodePlan pl = decode_plan_for(batch, pool->num_kv_heads, num_q_heads, pool->head_dim,
+                                        max_context_len, split_blocks);
+  const size_t need = (size_t)pl.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return KVB_ERR_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return KVB_ERR_INVALID;
+  if (pl.stream) {
+    const kvb_pool p{pool->k, pool->v, pool->block_stride, pool->num_blocks, 16, pool->num_kv_heads,
+                     pool->head_dim, dtype};
+    return launch_status(kvb::launch_decode_stream(
+        p, bits, kvb::DecScales{pool->k_scale, pool->v_scale}, q, out, context_lens, block_tables,
+        block_table_stride, batch, num_q_heads, max_context_len, pl.sp, scale, workspace,
+        (hipStream_t)stream));
+  }
   return launch_status(kvb::launch_decode_q8(*pool, bits, dtype, q, out, context_lens, block_tables,
                                              block_table_stride, batch, num_q_heads,
-                                             max_context_len, sb, ns, scale, workspace,
+                                             max_context_len, pl.sb, pl.ns, scale, workspace,
                                              (hipStream_t)stream));
 }
 

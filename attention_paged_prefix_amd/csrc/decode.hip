@@ -24,87 +24,10 @@
 //    the output rescale is rarely executed.
 //  * A split covering the whole context writes the normalised output directly; other
 //    splits write (output, max, sum) partials that decode_merge combines.
-#include <type_traits>
-
-#include "kvb_device.h"
+#include "decode_common.h"
 #include "kvb_launch.h"
 
 namespace kvb {
-
-// 16 bytes per lane with the non-temporal (streaming) cache policy (operand 2 = nt).
-__device__ inline uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
-}
-
-constexpr int kDecWaves = 4;
-constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kMaxSplitBlocks = 256;
-constexpr int kDecHeads = 16;               // query heads per work-group (MFMA N)
-constexpr float kRescaleThreshold = 8.0f;   // log2 units
-constexpr float kNegBig = -1.0e30f;
-
-template <int D> struct DecStep {
-  static constexpr int VCH = D / 32;        // 16-byte chunks per lane per block, K and V
-  uint4 k[2][VCH];
-  uint4 v[2][VCH];
-  int rows[2];                              // valid key rows of each block (0..16)
-  int pos[2];                               // position of each block's first key
-};
-
-// A quantised pool's step (QB bits per code): a 16-byte chunk holds 128/QB codes of one
-// key row, a block's K (or V) is CH = D*QB/8 chunks, NCH per lane; vsc holds the V scale
-// of the key row each of the lane's V chunks belongs to.
-template <int D, int QB> struct DecStepQ {
-  static constexpr int CH = D * QB / 8;          // chunks per block (K or V)
-  static constexpr int CPRQ = D * QB / 128;      // chunks per key row
-  static constexpr int NCH = (CH + 63) / 64;
-  uint4 k[2][NCH];
-  uint4 v[2][NCH];
-  float vsc[2][NCH];
-  int rows[2];
-  int pos[2];
-};
-
-// Scales of the 8-bit pool (ignored by the 16-bit forms): the per-channel K scales
-// [Hkv][D] and the per-token V scales [block][Hkv][16].
-struct DecQ8 {
-  const float* k_scale;
-  const float* v_scale;
-};
-
-// 16 int8 codes -> 16 values code * s of T in two 16-byte halves (s = 1: exact, since
-// |code| <= 127 fits the 8-bit significand of bf16 and the 11-bit one of fp16; otherwise
-// rounded to nearest even like any 16-bit value).
-template <typename T>
-__device__ inline void codes_to(uint4 c, float s, uint4& lo, uint4& hi) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t x = (int32_t)w[i];
-    o[2 * i] = pack2<T>((float)((x << 24) >> 24) * s, (float)((x << 16) >> 24) * s);
-    o[2 * i + 1] = pack2<T>((float)((x << 8) >> 24) * s, (float)(x >> 24) * s);
-  }
-  lo = make_uint4(o[0], o[1], o[2], o[3]);
-  hi = make_uint4(o[4], o[5], o[6], o[7]);
-}
-
-// 32 4-bit codes (two per byte, the even channel in the low nibble, 4-bit two's
-// complement) -> 32 values code * s of T in four 16-byte quarters (s = 1: exact).
-template <typename T>
-__device__ inline void nibbles_to(uint4 c, float s, uint4 (&o4)[4]) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  uint32_t o[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t x = (int32_t)w[i];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      o[4 * i + k] = pack2<T>((float)((x << (28 - 8 * k)) >> 28) * s, (float)((x << (24 - 8 * k)) >> 28) * s);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o4[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-}
 
 // Shared-prefix part of a grouped cascade decode (ignored by the plain form).  A group
 // work-group fills its 16 query columns with `cols` heads of each of `seqs` sequences,
@@ -542,8 +465,6 @@ decode_split_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict_
 // Every slot of the row is loaded without waiting for the context length (eight at a
 // time, all in flight together); slots past the row's count only enter through selects,
 // so whatever they hold never reaches the result.  The merge is one memory round trip.
-constexpr int kMergeRows = 4;
-constexpr int kMergeBatch = 8;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kMergeRows)
@@ -560,6 +481,8 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
   const float* ml = ws_ml + (int64_t)row * ws_slots * 2;
   const float* po = ws_o + (int64_t)row * ws_slots * D;
   float2 mine;                         // (max, sum) of slot s0 + lane % 8
+  // lanes past the head dimension re-read its last element (never written out), so the
+  // loads need no branch
   float v[kMergeBatch][NV];
   auto load = [&](int s0) {
     mine = *reinterpret_cast<const float2*>(ml + 2 * min(s0 + (lane & (kMergeBatch - 1)), ws_slots - 1));
@@ -567,10 +490,7 @@ decode_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws
     for (int j = 0; j < kMergeBatch; ++j) {
       const int s = min(s0 + j, ws_slots - 1);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int d = lane + 64 * i;
-        v[j][i] = d < D ? po[(int64_t)s * D + d] : 0.f;
-      }
+      for (int i = 0; i < NV; ++i) v[j][i] = po[(int64_t)s * D + min(lane + 64 * i, D - 1)];
     }
   };
   load(0);

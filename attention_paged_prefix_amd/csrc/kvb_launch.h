@@ -43,6 +43,29 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
                          const int32_t* bt, int bt_stride, int batch, int hq, int max_ctx, int sb,
                          int ns, float scale, void* ws, hipStream_t s);
 
+// Balanced stream decode (batches of up to 1024 sequences): the batch's blocks in equal
+// ranges, one per wave of a grid sized to be resident, then a merge of the partial
+// records.  Workspace: a header (range length, per-sequence block-count prefix sums),
+// then (max, sum) pairs and partial outputs of `records` records of min(G, 16) heads.
+struct StreamPlan {
+  int span;          // blocks per wave range requested (0: balanced in the kernel)
+  int64_t waves;     // waves in the grid (a multiple of 32)
+  int64_t records;   // partial records: waves + units
+  int64_t bytes;     // workspace bytes
+};
+struct DecScales {   // per-channel K and per-token V scales of a quantised pool (else null)
+  const float* k_scale;
+  const float* v_scale;
+};
+bool decode_use_stream(int batch);
+int64_t stream_hdr_bytes(int batch);
+StreamPlan decode_stream_plan(int batch, int hkv, int hq, int d, int max_ctx, int split_blocks);
+// bits: 0 for the 16-bit pool, else 8 or 4 (p describes the code planes, block_stride in bytes)
+hipError_t launch_decode_stream(const kvb_pool& p, int bits, const DecScales& sc, const void* q,
+                                void* out, const int32_t* ctx, const int32_t* bt, int bt_stride,
+                                int batch, int hq, int max_ctx, const StreamPlan& sp, float scale,
+                                void* ws, hipStream_t s);
+
 // Quantised pools (bits = 8 or 4 per code; the 4-bit pool uses the same descriptor):
 // quantising slot scatter and decode (workspace as launch_decode's).
 hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int bits, int dtype, const void* kn,

@@ -3,6 +3,8 @@
 //    HBM read stream the decode kernel is bounded by (also used to evict L2 and the
 //    Infinity Cache between timed launches; reading, unlike writing, leaves no dirty
 //    lines whose write-back would be charged to the next kernel);
+//  * kvb_probe_gather: 4 KiB chunks at listed positions of a buffer, the read pattern of a
+//    paged decode (one block's K or V rows of one KV head per chunk);
 //  * kvb_probe_mfma: independent v_mfma_f32_32x32x16_bf16 chains on every SIMD over random
 //    operand data, the dense 16-bit matrix rate the chip sustains at the clocks it holds
 //    under that load.
@@ -21,10 +23,14 @@ read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* __restrict__ si
   uint32_t acc = 0;
   const uint64_t stride = (uint64_t)gridDim.x * kReadThreads;
   uint64_t i = (uint64_t)blockIdx.x * kReadThreads + threadIdx.x;
-  // four loads in flight per lane
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  // eight loads in flight per lane
+  constexpr int U = 8;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
   }
   for (; i < n16; i += stride) {
     const uint4 a = p[i];
@@ -32,6 +38,47 @@ read_kernel(const uint4* __restrict__ p, uint64_t n16, uint32_t* __restrict__ si
   }
   // the sum is kept alive by a store that never happens for real data (sink[0] is the
   // caller's; a single lane writes only if the xor equals a value it cannot predict)
+  if (acc == 0x9e3779b9u && threadIdx.x == 0) sink[0] = acc;
+}
+
+// Gather: 4 KiB chunks at the chunk indices idx[0..n) of buf, every byte read once.  Each
+// wave takes chunks w, w + W, ... (W waves in the grid), two at a time (eight 16-byte
+// loads in flight per lane), with the next pair's indices loaded one pair ahead.
+constexpr int kGatherChunk16 = 256;     // 16-byte units per chunk (4 KiB)
+
+// Chunk e & 0x7fffffff through a buffer resource over its 4 KiB; the top bit selects the
+// streaming (non-temporal) load policy (cache-policy operand 2).
+__device__ inline void load_chunk(const uint4* __restrict__ p, uint32_t e, int lane, uint4* a) {
+  const uint4* base = p + (uint64_t)(e & 0x7fffffffu) * kGatherChunk16;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, (short)0, kGatherChunk16 * 16, 0x00020000);
+  if (e >> 31) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      a[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (u * 64 + lane) * 16, 0, 2));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      a[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (u * 64 + lane) * 16, 0, 0));
+  }
+}
+
+__global__ void __launch_bounds__(kReadThreads)
+gather_kernel(const uint4* __restrict__ p, const uint32_t* __restrict__ idx, int n,
+              uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * (kReadThreads / 64);
+  int c = blockIdx.x * (kReadThreads / 64) + (threadIdx.x >> 6);
+  uint32_t acc = 0;
+  for (; c < n; c += 2 * nw) {
+    const uint32_t e0 = idx[c];
+    const uint32_t e1 = c + nw < n ? idx[c + nw] : e0;
+    uint4 a[8];
+    load_chunk(p, e0, lane, a);
+    load_chunk(p, e1, lane, a + 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+  }
   if (acc == 0x9e3779b9u && threadIdx.x == 0) sink[0] = acc;
 }
 
@@ -81,6 +128,18 @@ int kvb_probe_read(const void* buf, uint64_t bytes, uint32_t* sink, int blocks, 
   if (!buf || !sink || (bytes & 15) || ((uintptr_t)buf & 15) || blocks <= 0) return 2;
   hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, (hipStream_t)stream,
                      (const uint4*)buf, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// Reads the n 4-KiB chunks of buf whose indices are idx[0..n) (device uint32; chunk i
+// covers bytes [4096 i, 4096 i + 4096) of buf, which must hold them all; an index with the
+// top bit set is read with the streaming policy).  A chunk listed
+// twice is read twice (the second time mostly from cache).
+int kvb_probe_gather(const void* buf, const uint32_t* idx, int n, uint32_t* sink, int blocks,
+                     void* stream) {
+  if (!buf || !idx || !sink || n < 0 || blocks <= 0 || ((uintptr_t)buf & 15)) return 2;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, (hipStream_t)stream,
+                     (const uint4*)buf, idx, n, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

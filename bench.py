@@ -306,15 +306,20 @@ class Probe:
         settle(torch, lambda: self.mfma(iters, blocks), settle_ms)
         ms = time_each(torch, lambda: self.mfma(iters, blocks), 10)
         fl = self.lib.kvb_probe_mfma_flops(iters, blocks)
-        settle(torch, self.flush, min(settle_ms, 100))
-        rms = time_each(torch, self.flush, 10)
+        # HBM read stream: 4 GiB per launch, 32 work-groups per CU (launch ramp amortised)
+        big = torch.ones(2 * FLUSH_BYTES, dtype=torch.int16, device="cuda:0")
+        rd = lambda: self.lib.kvb_probe_read(big.data_ptr(), 4 * FLUSH_BYTES, self.sink.data_ptr(),  # noqa: E731
+                                             32 * self.cus, self._stream())
+        settle(torch, rd, min(settle_ms, 100))
+        rms = time_each(torch, rd, 10)
+        del big
         return {"mfma_bf16_tflops": fl / (np.median(ms) * 1e-3) / 1e12,
                 "mfma_probe": f"{blocks} work-groups x 4 waves x {iters} x 4 independent "
                               f"v_mfma_f32_32x32x16_bf16 on random N(0,1) bf16 operands, median "
                               f"of 10 launches of {np.median(ms):.3f} ms",
-                "hbm_read_gbps": FLUSH_BYTES / (np.median(rms) * 1e-3) / 1e9,
-                "hbm_probe": f"1 GiB read with 16-byte loads, median of 10 launches of "
-                             f"{np.median(rms):.3f} ms",
+                "hbm_read_gbps": 4 * FLUSH_BYTES / (np.median(rms) * 1e-3) / 1e9,
+                "hbm_probe": f"4 GiB read with 16-byte loads (32 work-groups per CU), median of "
+                             f"10 launches of {np.median(rms):.3f} ms",
                 "compute_units": self.cus}
 
 

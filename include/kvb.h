@@ -149,10 +149,14 @@ kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* o
 /* Paged decode: one query per sequence over its whole context, which is already in the
  * pool (kvstream 0.1.0, "Request lifecycle" step 2; kvboost 0.6.0, "CPU paged attention":
  * only the decode loop changes).  The query of sequence b sits at position
- * context_lens[b]-1 and sees keys 0..context_lens[b]-1 through its block table.  The work
- * is split over groups of split_blocks blocks whose partial results (unnormalised output,
- * running max, sum) are merged by log-sum-exp; split_blocks == 0 picks a size from the
- * host bounds.  A context length <= 0 gives a zero output row.
+ * context_lens[b]-1 and sees keys 0..context_lens[b]-1 through its block table.  For
+ * batches of up to 1024 sequences the (KV head, sequence, block) list of the whole batch
+ * is cut into equal ranges, one per wave of a grid that is resident at once; a sequence
+ * whose blocks fall into several ranges has partial results (unnormalised output, running
+ * max, sum) merged by log-sum-exp.  split_blocks > 0 fixes the range length in blocks
+ * (values above 64 count as 64); 0 balances the ranges over the device.  Larger batches
+ * split each sequence into groups of split_blocks blocks (0: a size from the host bounds).
+ * A context length <= 0 gives a zero output row.
  * q, out: (device) [batch][num_q_heads][head_dim]; context_lens: (device) int32 [batch]
  * <= max_context_len; block_tables: (device) int32 [batch][block_table_stride] with
  * block_table_stride >= ceil(max_context_len/16).
@@ -166,18 +170,17 @@ kvb_status kvb_paged_decode(const kvb_pool* pool, const void* q, void* out,
 
 /* Allocation-free paged decode, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * kernels, split plan and result bits as kvb_paged_decode, with the split partials kept in
- * a static device array of KVB_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a
- * caller workspace.  Each GPU the library runs on holds its own copy of that array from
+ * kernels, split plan and result bits as kvb_paged_decode, with the workspace (split
+ * partials and the plan's header) kept in a static device array of
+ * KVB_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller workspace.  Each GPU the library runs on holds its own copy of that array from
  * the first call on it until the process ends; that first call on a device also looks up
  * the array's address (no allocation call is made by this entry point at any time).
  * Every call on one GPU shares the array and it keeps the last call's contents (nothing in
  * it needs clearing: every partial the merge reads is written by the same call), so calls
  * that overlap on one GPU (different streams, or threads) race and must be serialised by
- * the caller.  A call whose split plan needs more than KVB_NOALLOC_SCRATCH_BYTES
+ * the caller.  A call whose plan needs more than KVB_NOALLOC_SCRATCH_BYTES
  * (kvb_paged_decode_workspace_size for the same arguments) returns KVB_ERR_TOO_LARGE and
- * launches nothing; a plan without splits needs no scratch.  Arguments, layouts and the
- * other errors as kvb_paged_decode. */
+ * launches nothing.  Arguments, layouts and the other errors as kvb_paged_decode. */
 #define KVB_NOALLOC_SCRATCH_BYTES (16u << 20)
 kvb_status kvb_paged_decode_noalloc(const kvb_pool* pool, const void* q, void* out,
                                     const int32_t* context_lens, const int32_t* block_tables,
@@ -206,9 +209,9 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace sizes in bytes (0 = none needed).  Host arithmetic on the arguments and the
- * current device's compute-unit count (the decode split plan aims at a number of
- * work-groups per compute unit), so a size holds for the device that is current when it
- * is queried; call the size query and the decode with the same device current.  The
+ * current device's compute-unit count (the decode plan sizes its grid to the device), so a
+ * size holds for the device that is current when it is queried; call the size query and
+ * the decode with the same device current.  The
  * decode sizes take num_kv_heads too: the split plan counts (sequence, KV head) units. */
 size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                         int32_t total_q, int32_t max_prefix_len);

@@ -143,10 +143,16 @@ def test_decode_validation_and_workspace(lib):
     assert decode(lib, p, q=None) == NULL
     assert decode(lib, p, ctx=FAKE + 1) == INVALID
     assert decode(lib, p, batch=0) == OK
-    # a split size covering the whole context needs no workspace
-    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256) == 0
-    # forced split sizes: (ceil(250/16) splits) x rows x (d + 2) floats
-    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 16 * 4 * 8 * (128 + 2) * 4
+    # the balanced form always needs its header and records, whatever the split size
+    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256) > 0
+    # forced range of 16 blocks: 2 KV heads x 4 sequences x 250 blocks = 2000 blocks in
+    # ranges of 16 -> 125 waves, rounded up to 128 (whole work-groups on all 8 XCDs);
+    # records = waves + units (8) of 4 heads: a 256-byte header, then (max, sum) pairs
+    # (rounded up to 256 bytes), then d floats per head
+    assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 256 + 4352 + 136 * 4 * 128 * 4
+    # ranges longer than 64 blocks are taken as 64
+    assert (lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256)
+            == lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 64))
 
 
 def decode_noalloc(lib, p, **kw):
@@ -170,7 +176,8 @@ def test_decode_noalloc_validation(lib):
     assert decode_noalloc(lib, p, scale=float("inf")) == INVALID
     assert decode_noalloc(lib, pool(head_dim=80)) == UNSUP
     assert decode_noalloc(lib, p, batch=0) == OK
-    # 64 sequences x 32 heads x 250 one-block splits x (128 + 2) floats > 16 MiB
+    # one-block ranges: 64 sequences x 8 KV heads x 250 blocks records of 4 heads x
+    # (128 + 2) floats > 16 MiB
     need = lib.kvb_paged_decode_workspace_size(64, 8, 32, 128, 4000, 1)
     assert need > 16 << 20
     assert decode_noalloc(lib, p, batch=64, hq=32, sb=1) == 6
@@ -190,8 +197,6 @@ def test_cascade_decode_validation_and_workspace(lib):
     p = pool()
     need = lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 4000, 1024, 0)
     assert need > 0
-    # the shared part adds workspace slots to the split decode's
-    assert need > lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000 - 1024, 0)
     assert cascade(lib, p) == WS                      # always needs a workspace
     assert cascade(lib, p, ws=FAKE, wsb=need - 1) == WS
     assert cascade(lib, p, ws=FAKE + 8, wsb=need) == INVALID

@@ -264,6 +264,7 @@ DECODE_CASES = [
     (302, "fp16", 8, 8, 64, [3, 64, 100]),
     (303, "fp16", 40, 8, 96, [1000, 33]),
     (304, "bf16", 16, 2, 128, [300, 2000, 15]),
+    (307, "bf16", 40, 2, 64, [700, 1600, 33, 0, 16]),     # G=20: two head chunks per KV head
 ]
 
 
@@ -289,6 +290,25 @@ def test_decode_zero_context_gives_zero_row():
     assert (got[1] == 0).all()
     ref = u.oracle_decode(w)
     assert u.max_err(got[:1], ref[:1], "bf16") <= 2e-2
+
+
+@pytest.mark.parametrize("batch", [1024, 1025])
+def test_decode_batch_at_the_balanced_form_bound(batch):
+    """1024 sequences: the largest batch of the balanced form (prefix sums of all block
+    counts in one work-group's LDS); 1025: the per-sequence split form.  Ragged contexts
+    with zeros, every row against the oracle."""
+    u = _util()
+    rng = np.random.default_rng(batch)
+    ctx = rng.integers(0, 120, size=batch)
+    ctx[::97] = 0
+    w = make_custom(310 + batch % 2, "bf16", 8, 2, 64, [int(c) for c in ctx], kind="decode",
+                    poison=True)
+    dev = u.Dev(w)
+    for split in (0, 3):
+        got = u.to_bits(dev.decode(split_blocks=split))
+        ref = u.oracle_decode(w)
+        assert (got[ctx == 0] == 0).all()
+        assert u.max_err(got, ref, "bf16") <= 2e-2, split
 
 
 def test_decode_equals_one_row_prefill_within_tolerance():
