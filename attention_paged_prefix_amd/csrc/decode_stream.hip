@@ -44,7 +44,7 @@ namespace {
 constexpr int kStrWaves = 8;
 constexpr int kStrThreads = 64 * kStrWaves;
 constexpr int kStrMaxBatch = 1024;   // block-count prefix sums held in LDS
-constexpr int kStrMaxSpan = 64;      // blocks per wave range: one table entry per lane
+constexpr int kStrMaxSpan = 64;      // blocks per wave (a pair range of two: two table entries per lane)
 constexpr int kStrMinSpan = 16;      // shorter ranges would add partials for little gain
 constexpr int kStrKeepBlocks = 64;   // blocks of a context read with the normal policy
 
@@ -53,6 +53,7 @@ struct DecStream {
   int max_ctx, bt_stride;
   int span;                           // blocks per wave range; 0: balanced
   int waves;                          // waves in the grid
+  int resident;                       // waves the device holds at once
   int32_t* hdr;                       // [0] = S, [1] = blocks per (KV head, chunk), [2 + b] = prefix sums
   float* ws_o;                        // records x nhc x D
   float* ws_ml;                       // records x nhc x 2
@@ -96,8 +97,8 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) uint16_t sV[kStrWaves * SLOT];
   __shared__ int s_cum[kStrMaxBatch + 1];
   __shared__ int s_wsum[kStrWaves];
+  __shared__ int s_last[kStrWaves];          // unit of each wave's last step (-1: none)
 
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -136,29 +137,48 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   }
   const int Tb = s_cum[batch];                       // blocks per (KV head, head chunk)
   const int64_t total = (int64_t)ds.hkv * ds.nchunks * Tb;
+  // S: blocks per wave (two waves per pair range).  Balanced: the list over the waves the
+  // device holds at once.  Work-groups per XCD that take ranges (the rest return at once):
+  // as few as cover the list, the same number on every XCD; hardware work-group h runs on
+  // XCD h % 8, and logical work-group xcd * use + h / 8 keeps each XCD on a contiguous part
+  // of the list.
   int S = ds.span;
   if (S <= 0) {
-    S = (int)((total + ds.waves - 1) / ds.waves);
+    S = (int)((total + ds.resident - 1) / ds.resident);
     S = max(S, kStrMinSpan);
     S = min((S + 1) & ~1, kStrMaxSpan);
   }
-  if (lid == 0) {
+  constexpr int kWavesPerXcdWg = kNumXcd * kStrWaves;
+  const int per = gridDim.x / kNumXcd;
+  const int use = (int)max((int64_t)1, min((int64_t)per, (total + (int64_t)kWavesPerXcdWg * S - 1) /
+                                                           ((int64_t)kWavesPerXcdWg * S)));
+  const int R = 2 * S;                               // blocks per pair range
+  if (blockIdx.x == 0) {
     for (int i = tid; i <= batch; i += kStrThreads) ds.hdr[2 + i] = s_cum[i];
     if (tid == 0) {
-      ds.hdr[0] = S;
+      ds.hdr[0] = R;
       ds.hdr[1] = Tb;
     }
   }
-  const int gw = lid * kStrWaves + w;
-  const int64_t p0 = (int64_t)gw * S;
-  if (p0 >= total) return;                           // no barrier below this point
-  const int len = (int)min((int64_t)S, total - p0);
+  const int xcd = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+  if (j >= use) return;                              // the whole work-group
+  const int lid = xcd * use + j;
+  // Waves w and w + 4 share pair range pp: the first takes the first half of its steps,
+  // the second the rest; the unit the two halves share is combined in LDS at the end, so
+  // the pair writes one output or record per unit.
+  const int side = w / (kStrWaves / 2);
+  const int pp = lid * (kStrWaves / 2) + (w % (kStrWaves / 2));
+  const int64_t p0 = (int64_t)pp * R;
+  const int len = (int)max((int64_t)0, min((int64_t)R, total - p0));
 
-  // This wave's block table: lane i describes block p0 + i of the list (unit, block index
-  // in the context, physical block or -1 outside the pool, valid key rows).
-  int t_u = -1, t_blk = 0, t_pb = -1, t_rows = 0;
-  if (lane < len) {
-    const int64_t p = p0 + lane;
+  // The pair range's block table: lane i describes blocks p0 + i and p0 + 64 + i of the list
+  // (unit, block index in the context, physical block or -1 outside the pool, valid key
+  // rows).
+  int t_u[2] = {-1, -1}, t_blk[2] = {0, 0}, t_pb[2] = {-1, -1}, t_rows[2] = {0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (lane + 64 * h >= len) continue;
+    const int64_t p = p0 + lane + 64 * h;
     const int group = (int)(p / Tb);
     const int r = (int)(p - (int64_t)group * Tb);
     int lo = 0, hi = batch;                          // the b with s_cum[b] <= r < s_cum[b + 1]
@@ -170,16 +190,16 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
     const int blk = r - s_cum[lo];
     const int n = min(ctx_lens[lo], cap);
     const int pb = bt[(int64_t)lo * ds.bt_stride + blk];
-    t_u = group * batch + lo;
-    t_blk = blk;
-    t_pb = (pb >= 0 && pb < num_blocks) ? pb : -1;
-    t_rows = t_pb >= 0 ? min(kBlock, n - blk * kBlock) : 0;
+    t_u[h] = group * batch + lo;
+    t_blk[h] = blk;
+    t_pb[h] = (pb >= 0 && pb < num_blocks) ? pb : -1;
+    t_rows[h] = t_pb[h] >= 0 ? min(kBlock, n - blk * kBlock) : 0;
   }
   auto rl = [](int x, int i) { return __builtin_amdgcn_readlane(x, i); };
-  // first unit after u in the range, or -1
-  auto unit_after = [&](int u) -> int {
-    const uint64_t m = __ballot(lane < len && t_u > u);
-    return m ? rl(t_u, (int)__builtin_ctzll(m)) : -1;
+  // entry i (wave-uniform, 0 <= i < 128) of a table
+  auto tab = [&](const int (&x)[2], int i) -> int {
+    const int a = rl(x[0], i & 63), b = rl(x[1], i & 63);
+    return i < 64 ? a : b;
   };
 
   uint16_t* slot = sV + w * SLOT;           // V rows 0..31 of the current step
@@ -196,10 +216,10 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   auto desc_at = [&](int i) -> Desc {
     Desc d;
     d.i = i;
-    d.u = rl(t_u, i);
-    d.n = (i + 1 < len && rl(t_u, min(i + 1, 63)) == d.u) ? 2 : 1;
-    d.rows0 = rl(t_rows, i);
-    d.rows1 = d.n == 2 ? rl(t_rows, min(i + 1, 63)) : 0;
+    d.u = tab(t_u, i);
+    d.n = (i + 1 < len && tab(t_u, i + 1) == d.u) ? 2 : 1;
+    d.rows0 = tab(t_rows, i);
+    d.rows1 = d.n == 2 ? tab(t_rows, i + 1) : 0;
     return d;
   };
   auto desc_after = [&](const Desc& d) -> Desc {
@@ -211,10 +231,10 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   // the context and blocks outside the pool read as zero and cost no memory traffic.
   auto load = [&](const Desc& d, Step& R) __attribute__((always_inline)) {
     const int kvh = (d.u / batch) / ds.nchunks;
-    const bool nt = !Q8 && rl(t_blk, d.i) >= kStrKeepBlocks;
+    const bool nt = !Q8 && tab(t_blk, d.i) >= kStrKeepBlocks;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int pb = hb < d.n ? rl(t_pb, min(d.i + hb, 63)) : -1;
+      const int pb = hb < d.n ? tab(t_pb, d.i + hb) : -1;
       const int rows = hb == 0 ? d.rows0 : d.rows1;
       if constexpr (Q8) {
         // codes: D*QB/8 bytes per key row; block_stride counts bytes
@@ -418,9 +438,9 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
     __builtin_amdgcn_wave_barrier();
   };
 
-  // End of unit u inside the range: the normalised output when the range holds all of
-  // the unit's blocks, else the partial record gw + u.  Lane (c16, g4) holds
-  // o[db][rr] = O[head c16][d = 16*db + 4*g4 + rr].
+  // End of unit u (all of its blocks in the pair range done): the normalised output when
+  // the pair range holds all of the unit's blocks, else the partial record pp + u.  Lane
+  // (c16, g4) holds o[db][rr] = O[head c16][d = 16*db + 4*g4 + rr].
   auto finish_unit = [&](int u) __attribute__((always_inline)) {
     const float lsum = halves_sum(l_run + xor16(l_run));
     const int group = u / batch, b = u - group * batch;
@@ -440,7 +460,7 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
           *reinterpret_cast<uint2*>(out + row * D + 16 * db + 4 * g4) = v2;
         }
       } else {
-        const int64_t rec = ((int64_t)gw + u) * ds.nhc + c16;
+        const int64_t rec = ((int64_t)pp + u) * ds.nhc + c16;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           *reinterpret_cast<f32x4*>(ds.ws_o + rec * D + 16 * db + 4 * g4) = o[db];
@@ -450,22 +470,54 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
     reset();
   };
 
-  // Steps of the range: each unit piece of m blocks takes ceil(m/2) steps.  Lane i < len
-  // starts a step when it starts a piece or sits an even number of blocks into one.
+  // Steps of the pair range: each unit piece of m blocks takes ceil(m/2) steps.  Position
+  // p < len starts a step when it starts a piece or sits an even number of blocks into
+  // one; step k starts at the k-th such position.
+  uint64_t st0, st1;
   int nsteps;
   {
-    const int prev_u = __shfl_up(t_u, 1, 64);
-    const bool starts = lane < len && (lane == 0 || prev_u != t_u);
-    const uint64_t sm = __ballot(starts);
-    // blocks into the lane's piece: lane minus the last piece start at or before it
-    const uint64_t upto = sm & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
-    const int into = lane - (63 - (int)__builtin_clzll(upto | 1ull));
-    nsteps = __builtin_popcountll(__ballot(lane < len && (into & 1) == 0));
+    // the shuffles run in every lane (a cross-lane read inside a lane-dependent branch
+    // would read inactive lanes), then lane 0 of the second half takes position 63
+    const int prev0 = __shfl_up(t_u[0], 1, 64);
+    const int sh1 = __shfl_up(t_u[1], 1, 64);
+    const int last_first = rl(t_u[0], 63);
+    const int prev1 = lane == 0 ? last_first : sh1;
+    const uint64_t s0 = __ballot(lane < len && (lane == 0 || prev0 != t_u[0]));
+    const uint64_t s1 = __ballot(lane + 64 < len && prev1 != t_u[1]);
+    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+    // the last piece start at or before p (position 0 always starts one)
+    const int last0 = 63 - (int)__builtin_clzll((s0 & upto) | 1ull);
+    const int last1 = (s1 & upto) ? 64 + 63 - (int)__builtin_clzll(s1 & upto)
+                                  : 63 - (int)__builtin_clzll(s0 | 1ull);
+    st0 = __ballot(lane < len && ((lane - last0) & 1) == 0);
+    st1 = __ballot(lane + 64 < len && ((lane + 64 - last1) & 1) == 0);
+    nsteps = __builtin_popcountll(st0) + __builtin_popcountll(st1);
   }
-  Desc cur = desc_at(0);
-  Desc nx = desc_after(cur);
-  fetch_q(cur.u);
-  bool fresh = true;            // qb holds a new unit's raw queries (8-bit: fold pending)
+  const uint64_t below = (1ull << lane) - 1;
+  const int rank0 = __builtin_popcountll(st0 & below);
+  const int rank1 = __builtin_popcountll(st0) + __builtin_popcountll(st1 & below);
+  // The side's next step, or an absent one (n = 0) after its last: steps
+  // [0, ceil(nsteps/2)) in order for the first side, the rest from the last one down for
+  // the second, so that the unit the two share is the last one of each.  (Handing the steps
+  // out one at a time through an LDS counter balances the pair at run time, but the
+  // partials then depend on timing and the rounding of the result changes from run to
+  // run; measured on MI355X it is only about 1% faster.)
+  const int half_steps = (nsteps + 1) / 2;
+  int taken = 0;
+  auto claim = [&]() -> Desc {
+    const int k = side == 0 ? taken : nsteps - 1 - taken;
+    if (side == 0 ? k >= half_steps : k < half_steps) return Desc{0, 0, 0, 0, 0};
+    ++taken;
+    const uint64_t m0 = __ballot(((st0 >> lane) & 1) && rank0 == k);
+    const uint64_t m1 = __ballot(((st1 >> lane) & 1) && rank1 == k);
+    return desc_at(m0 ? (int)__builtin_ctzll(m0) : 64 + (int)__builtin_ctzll(m1));
+  };
+
+  Desc cur = claim();
+  Desc nx = cur.n ? claim() : Desc{0, 0, 0, 0, 0};
+  if (cur.n) fetch_q(cur.u);
+  bool fresh = cur.n != 0;      // qb holds a new unit's raw queries (8-bit: fold pending)
+  int last_u = cur.n ? cur.u : -1;
   reset();
   // X holds the current step, Y the next one (in flight while X is computed); X then takes
   // the loads of the step after Y.  Loads are issued for absent steps too (n = 0:
@@ -490,21 +542,52 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
       fetch_q(nx.u);
       fresh = true;
     }
-    const Desc n2 = desc_after(nx);
-    update(s, cur.rows0, cur.rows1);
+    const Desc n2 = nx.n ? claim() : Desc{0, 0, 0, 0, 0};
     load(n2, X);
+    update(s, cur.rows0, cur.rows1);
     if (change) finish_unit(cur.u);
+    if (nx.n) last_u = nx.u;
     cur = nx;
     nx = n2;
   };
-  // An odd count ends with one absent step (no keys: it changes nothing), so the loop has
-  // no exit between its halves; such an exit would join the loop head with A loaded last
-  // and make the wait before A's staging cover B's loads too.
-  for (int it = 0; it < nsteps; it += 2) {
+  // An absent step changes nothing (no keys), so the loop runs both halves every time
+  // and has no exit between them; such an exit would join the loop head with A loaded
+  // last and make the wait before A's staging cover B's loads too.
+  do {
     half(A);
     half(B);
+  } while (cur.n != 0);
+
+  // The last unit of each side may have steps on the other side too: the first side
+  // leaves its partial (per lane: o, running max, sum) in its LDS slot and the second side
+  // folds it into its own before writing the unit.
+  float* part = reinterpret_cast<float*>(sV + w * SLOT);
+  if (lane == 0) s_last[w] = last_u;
+  if (side == 0 && last_u >= 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part[(db * 4 + rr) * 64 + lane] = o[db][rr];
+    part[NDB * 4 * 64 + lane] = m_run;
+    part[(NDB * 4 + 1) * 64 + lane] = l_run;
   }
-  finish_unit(rl(t_u, len - 1));
+  __syncthreads();
+  const int partner_last = s_last[w ^ (kStrWaves / 2)];
+  if (last_u >= 0) {
+    if (side == 1 && partner_last == last_u) {
+      const float* fp = reinterpret_cast<const float*>(sV + (w ^ (kStrWaves / 2)) * SLOT);
+      const float mf = fp[NDB * 4 * 64 + lane];
+      const float M = fmaxf(m_run, mf);
+      const float ab = fast_exp2(m_run - M), af = fast_exp2(mf - M);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[db][rr] = o[db][rr] * ab + fp[(db * 4 + rr) * 64 + lane] * af;
+      l_run = l_run * ab + fp[(NDB * 4 + 1) * 64 + lane] * af;
+      m_run = M;
+    }
+    if (!(side == 0 && partner_last == last_u)) finish_unit(last_u);
+  }
 }
 
 // One wave per (sequence, query head) row.  The row's unit covers blocks [start, end) of
@@ -602,14 +685,15 @@ StreamPlan decode_stream_plan(int batch, int hkv, int hq, int d, int max_ctx, in
   } else {
     sp.span = 0;
     waves = (tmax + kStrMaxSpan - 1) / kStrMaxSpan;
-    const int64_t resident = (int64_t)kStrWaves * device_cu_count();
-    if (waves < resident) waves = resident;
   }
+  const int64_t resident = (int64_t)kStrWaves * device_cu_count();
+  if (split_blocks <= 0 && waves < resident) waves = resident;
   // whole work-groups on every XCD
   const int64_t unit = (int64_t)kStrWaves * kNumXcd;
   if (waves < 1) waves = 1;
   waves = (waves + unit - 1) / unit * unit;
   sp.waves = waves;
+  sp.resident = resident;
   sp.records = waves + (int64_t)hkv * nchunks * batch;
   sp.bytes = stream_hdr_bytes(batch) + stream_ml_bytes(sp.records, nhc) + sp.records * nhc * d * 4;
   return sp;
@@ -633,6 +717,7 @@ static hipError_t launch_stream_t(const kvb_pool& p, const void* q, void* out, c
   ds.bt_stride = bt_stride;
   ds.span = sp.span;
   ds.waves = (int)sp.waves;
+  ds.resident = (int)sp.resident;
   ds.hdr = (int32_t*)ws;
   ds.ws_ml = (float*)((char*)ws + stream_hdr_bytes(batch));
   ds.ws_o = (float*)((char*)ds.ws_ml + stream_ml_bytes(sp.records, ds.nhc));

@@ -49,7 +49,8 @@ hipError_t launch_decode(const kvb_pool& p, const void* q, void* out, const int3
 // then (max, sum) pairs and partial outputs of `records` records of min(G, 16) heads.
 struct StreamPlan {
   int span;          // blocks per wave range requested (0: balanced in the kernel)
-  int64_t waves;     // waves in the grid (a multiple of 32)
+  int64_t waves;     // waves in the grid (whole work-groups on every XCD)
+  int64_t resident;  // waves the device holds at once (the balanced range length's divisor)
   int64_t records;   // partial records: waves + units
   int64_t bytes;     // workspace bytes
 };

@@ -258,7 +258,8 @@ def progress(msg: str) -> None:
 
 
 class Probe:
-    """libkvb_probe.so: HBM read stream / cache flush and the pure-MFMA rate probe."""
+    """libkvb_probe.so: HBM read stream / cache flush, the 4 KiB gather read and the pure-MFMA
+    rate probe."""
 
     def __init__(self, torch):
         import ctypes
@@ -270,6 +271,8 @@ class Probe:
                                        ctypes.c_void_p]
         lib.kvb_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
+        lib.kvb_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_void_p]
         lib.kvb_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.kvb_probe_mfma_flops.restype = ctypes.c_double
         self.lib = lib
@@ -290,6 +293,13 @@ class Probe:
                                      8 * self.cus, self._stream())
         if rc:
             raise RuntimeError(f"kvb_probe_read failed ({rc})")
+
+    def gather(self, buf, idx, n, blocks):
+        """Read the n 4-KiB chunks of device tensor `buf` listed in device int32 `idx`."""
+        rc = self.lib.kvb_probe_gather(buf.data_ptr(), idx.data_ptr(), n, self.sink.data_ptr(), blocks,
+                                       self._stream())
+        if rc:
+            raise RuntimeError(f"kvb_probe_gather failed ({rc})")
 
     def mfma(self, iters, blocks):
         rc = self.lib.kvb_probe_mfma(iters, blocks, self.ops.data_ptr(), self.sink.data_ptr(),
@@ -678,6 +688,39 @@ def time_launches(torch, fn, n: int) -> float:
     return a.elapsed_time(b) / n
 
 
+def _decode_read_pattern(torch, w, k, v, probe, steps):
+    """The decode's HBM reads alone: every (block, KV head) K and V slice its block tables
+    reach, once each (4 KiB at d = 128 bf16), in the order the decode meets them, read by
+    the gather probe after a cache flush.  No compute, no re-reads: the rate this access
+    pattern reaches, the practical ceiling of the decode's memory stream."""
+    H = w.num_kv_heads
+    assert 16 * w.head_dim * ESZ == 4096, "gather chunks are 4 KiB"
+    kc = []
+    for kvh in range(H):
+        seen = set()
+        for b in range(w.batch):
+            for j in range((int(w.context_lens[b]) + 15) // 16):
+                pb = int(w.block_tables[b][j])
+                if pb not in seen:
+                    seen.add(pb)
+                    kc.append(pb * H + kvh)
+    idx = torch.as_tensor(np.asarray(kc, dtype=np.int32)).to("cuda:0")
+    n = len(kc)
+    blocks = 8 * probe.cus
+
+    def run():
+        probe.gather(k, idx, n, blocks)
+        probe.gather(v, idx, n, blocks)
+
+    for _ in range(3):
+        run()
+    s = stats(time_each(torch, run, steps, before=probe.flush))
+    nbytes = 2.0 * n * 4096
+    return {"what": "gather probe over the decode's unique (block, KV head) K and V slices, "
+                    "4 KiB each, cold cache, no compute",
+            "bytes": nbytes, "ms_cold": s["median"], "gbps_cold": nbytes / (s["median"] * 1e-3) / 1e9}
+
+
 def _time_warm_cold(torch, run, steps, probe):
     """Per-launch ms of `run` launched back to back (warm caches) and after a 1 GiB read
     that evicts L2 and the Infinity Cache (cold); events bracket the launch only."""
@@ -827,6 +870,7 @@ def bench_decode(torch, kvb, args, probe):
     sq4w, sq4c = _time_warm_cold(torch, run_q4, steps, probe)
     tw, tc, cw, cc = sw["mean"], sc["mean"], scw["mean"], scc["mean"]
     qw, qc, q4w, q4c = sqw["mean"], sqc["mean"], sq4w["mean"], sq4c["mean"]
+    pattern = _decode_read_pattern(torch, w, k, v, probe, steps)
     by8 = decode_bytes_q8(w, w.context_lens, w.block_tables)
     by4 = decode_bytes_q8(w, w.context_lens, w.block_tables, 4)
     by = decode_bytes(w, w.context_lens, w.block_tables)
@@ -839,6 +883,7 @@ def bench_decode(torch, kvb, args, probe):
             "frac_hbm_peak_cold": by / (tc * 1e-3) / 1e9 / PEAK_GBPS,
             "logical_kv_gbps_cold": logical / (tc * 1e-3) / 1e9,
             "tflops_cold": decode_flops(w.context_lens, w) / (tc * 1e-3) / 1e12,
+            "read_pattern": dict(pattern, decode_time_vs_pattern_cold=tc / pattern["ms_cold"]),
             "cascade": {"shared_tokens": shared_len, "ms_back_to_back": cw, "ms_cold_cache": cc,
                         "gbps_back_to_back": by / (cw * 1e-3) / 1e9,
                         "gbps_cold_cache": by / (cc * 1e-3) / 1e9,

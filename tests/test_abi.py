@@ -150,9 +150,9 @@ def test_decode_validation_and_workspace(lib):
     # records = waves + units (8) of 4 heads: a 256-byte header, then (max, sum) pairs
     # (rounded up to 256 bytes), then d floats per head
     assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 256 + 4352 + 136 * 4 * 128 * 4
-    # ranges longer than 64 blocks are taken as 64
+    # ranges longer than 128 blocks are taken as 128
     assert (lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256)
-            == lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 64))
+            == lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 128))
 
 
 def decode_noalloc(lib, p, **kw):

@@ -82,6 +82,33 @@ def test_decode_full_size_sampled():
     assert err <= u.TOL[w.dtype], f"max abs err {err}"
 
 
+def test_decode_step_full_size_sampled():
+    """The decode call of the benchmark step on the ragged mix at head dim 96 (32 contexts
+    of up to ~17K tokens, the chunk's and the decode token's K/V scattered into the pool
+    first): the balanced form at about 62 blocks per wave, one range per resident wave."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    u = _util()
+    w = make_config("ragged_d96", poison=True, with_decode=True)
+    dev = u.Dev(w)
+    kvb.write_kv(dev.pool, dev.k_new, dev.v_new, dev.slots)
+    dk, dv = u.to_dev(w.dec_k, w.dtype), u.to_dev(w.dec_v, w.dtype)
+    kvb.write_kv(dev.pool, dk, dv, u.idev(w.dec_slots, torch.int64))
+    dq = u.to_dev(w.dec_q, w.dtype)
+    ctx = w.dec_context_lens
+    got = u.to_bits(kvb.paged_decode(dev.pool, dq, u.idev(ctx), dev.bt, w.scale, int(ctx.max())))
+    torch.cuda.synchronize()
+    ek, ev = oracle.write_kv(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping)
+    ek, ev = oracle.write_kv(ek, ev, w.dec_k, w.dec_v, w.dec_slots)
+    rng = np.random.default_rng(96)
+    seqs = sorted(set([0, w.batch - 1, int(np.argmax(ctx))] + [int(x) for x in rng.integers(0, w.batch, size=6)]))
+    ref = oracle.paged_decode(ek, ev, w.dec_q, ctx, w.block_tables, w.scale, w.dtype, seqs=seqs)
+    vals = oracle.decode_bits(got, w.dtype)
+    assert np.isfinite(vals).all()
+    err = float(np.max(np.abs(vals[seqs] - ref[seqs])))
+    assert err <= u.TOL[w.dtype], f"max abs err {err}"
+
+
 def test_cascade_decode_full_size_sampled():
     """The decode workload's first 1024 tokens (64 blocks) are one shared prefix; the
     cascade form reads them once for all 64 sequences."""

@@ -269,7 +269,7 @@ DECODE_CASES = [
 
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}")
-@pytest.mark.parametrize("split", [0, 1, 4, 7])
+@pytest.mark.parametrize("split", [0, 1, 4, 7, 77, 128])
 def test_decode_matches_oracle(case, split):
     u = _util()
     seed, dt, hq, hkv, d, ctx = case
