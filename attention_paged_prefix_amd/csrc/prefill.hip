@@ -274,7 +274,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 
   // tiles of the chunk itself crossing the causal diagonal, or the end of the keys, need
   // per-row masking (uniform per work-group)
-  auto tile_needs_mask = [&](int t) {
+  // (by-value captures: a select between two captured references otherwise becomes a
+  // load through a selected pointer into a closure held in scratch memory)
+  auto tile_needs_mask = [=](int t) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
@@ -375,16 +377,20 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   };
 
   // keys of tile t this lane's row may not see -> -inf
-  auto mask = [&](int t, f32x16* s) {
+  auto mask = [=](int t, f32x16* s) {
     const bool pre = t < n_pre;
     const int base = pre ? t * kKT : (t - n_pre) * kKT;
     const int count = pre ? min(kKT, P - base) : min(kKT, self_n - base);
     const int lim = pre ? min(count, row_lim - base) : min(count, i_row - base + 1);
+    // key (rr/4)*8 + 4*hf + rr%4 (+32 in the second half): the lane's half moves to the
+    // limit, so each comparison is against an immediate (per-key constants kept in
+    // registers across the loop cost a dozen of them)
+    const int limh = lim - 4 * hf;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int kl = (rr >> 2) * 8 + hf * 4 + (rr & 3);
-      s[0][rr] = kl < lim ? s[0][rr] : -INFINITY;
-      s[1][rr] = kl + 32 < lim ? s[1][rr] : -INFINITY;
+      const int kc = (rr >> 2) * 8 + (rr & 3);
+      s[0][rr] = kc < limh ? s[0][rr] : -INFINITY;
+      s[1][rr] = kc + 32 < limh ? s[1][rr] : -INFINITY;
     }
   };
   // exp2 of the two scores of pair e (kp4 = e/4, element e%4) of a tile, packed
