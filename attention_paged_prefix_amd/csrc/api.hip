@@ -470,8 +470,8 @@ size_t kvb_paged_prefill_q8_workspace_size(int32_t batch, int32_t num_kv_heads,
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || total_q <= 0 || max_prefix_len < 0 ||
       (head_dim != 64 && head_dim != 96 && head_dim != 128))
     return 0;
-  return (size_t)kvb::prefill_q8_ws_bytes(batch, num_kv_heads, num_q_heads, head_dim, total_q,
-                                          max_prefix_len);
+  // the prefill's dispatch plan only: the codes are widened inside the prefill kernel
+  return (size_t)kvb::prefill_plan_bytes(batch, num_q_heads, total_q);
 }
 
 static kvb_status prefill_quant(const kvb_pool_q8* pool, int bits, int32_t dtype, const void* q,
@@ -498,13 +498,13 @@ static kvb_status prefill_quant(const kvb_pool_q8* pool, int bits, int32_t dtype
   if (block_table_stride < (max_prefix_len + 15) / 16 || block_table_stride < 0) return KVB_ERR_INVALID;
   const size_t need = kvb_paged_prefill_q8_workspace_size(batch, pool->num_kv_heads, num_q_heads,
                                                           pool->head_dim, total_q, max_prefix_len);
-  if (!workspace || workspace_bytes < need) return KVB_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return KVB_ERR_INVALID;
+  if (workspace && workspace_bytes < need) return KVB_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return KVB_ERR_INVALID;
   if (max_q_len == 0) return KVB_OK;
-  return launch_status(kvb::launch_prefill_q8(*pool, bits, dtype, q, k_new, v_new, out, cu_q_lens,
-                                              prefix_lens, block_tables, block_table_stride, batch,
-                                              num_q_heads, total_q, max_q_len, max_prefix_len,
-                                              scale, workspace, (hipStream_t)stream));
+  return launch_status(kvb::launch_prefill_quant(*pool, bits, dtype, q, k_new, v_new, out, cu_q_lens,
+                                                 prefix_lens, block_tables, block_table_stride, batch,
+                                                 num_q_heads, total_q, max_q_len, scale,
+                                                 need > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
 kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,

@@ -74,14 +74,14 @@ hipError_t launch_write_kv_q8(const kvb_pool_q8& p, int bits, int dtype, const v
 hipError_t launch_decode_q8(const kvb_pool_q8& p, int bits, int dtype, const void* q, void* out,
                             const int32_t* ctx, const int32_t* bt, int bt_stride, int batch, int hq,
                             int max_ctx, int sb, int ns, float scale, void* ws, hipStream_t s);
-// Prefill over the 8-bit pool: prefix blocks widened into a staging pool in the
-// workspace (prefill_q8_ws_bytes), then the 16-bit prefill.
-int64_t prefill_q8_ws_bytes(int batch, int hkv, int hq, int d, int total_q, int max_prefix_len);
-hipError_t launch_prefill_q8(const kvb_pool_q8& p, int bits, int dtype, const void* q, const void* kn,
-                             const void* vn, void* out, const int32_t* cu, const int32_t* plen,
-                             const int32_t* bt, int bt_stride, int batch, int hq, int total_q,
-                             int max_q_len, int max_prefix_len, float scale, void* ws,
-                             hipStream_t s);
+// Prefill over the 8-bit or 4-bit pool: the prefill kernel stages each prefix block's
+// codes in LDS and widens them there; the workspace holds only the dispatch plan
+// (prefill_plan_bytes).
+hipError_t launch_prefill_quant(const kvb_pool_q8& p, int bits, int dtype, const void* q,
+                                const void* kn, const void* vn, void* out, const int32_t* cu,
+                                const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
+                                int hq, int total_q, int max_q_len, float scale, void* plan_ws,
+                                hipStream_t s);
 
 // Cascade decode: the shared prefix pass (prefill kernel over all sequences' queries,
 // key tiles split over `nks` work-groups of `ks_tiles` tiles, partials to slots 0..nks-1)

@@ -105,6 +105,96 @@ struct PfWrite {
   uint16_t* v;
 };
 
+// 8-bit or 4-bit pool (QB = bits per code; kp/vp then hold codes, block_stride bytes):
+// K code c of channel e stands for c * k_scale[kvh][e], V code c of token row r for
+// c * v_scale[(block * hkv + kvh) * 16 + r].  The codes of each prefix block are staged
+// into LDS by the wave that owns the block, then widened by the same wave into the 16-bit
+// tile (V times its token's scale); the K channel scales are folded into the queries.
+struct PfQuant {
+  const float* v_scale;
+  const float* k_scale;
+};
+
+// Widening of staged codes into 16-bit tile values.  K codes are widened exactly (their
+// channel scales are folded into the queries); V codes become code * s, the token's
+// scale s applied in fp32 and the product rounded to nearest even.  In fp16 both start
+// from the same bit trick: a code biased to unsigned and placed under the exponent of
+// 1024 is the fp16 value 1024 + code + bias, exact; K subtracts the constant in fp16,
+// V takes (1024 + code + bias) * s - (1024 + bias) * s in one mixed-precision FMA.
+// Four int8 codes (one dword, channel order) -> two packed pairs.  ns = -1152 * s.
+template <typename T, bool V>
+__device__ inline void widen_q8(uint32_t x, float s, float ns, uint32_t& a, uint32_t& b) {
+  if constexpr (std::is_same<T, F16>::value) {
+    const uint32_t u = x ^ 0x80808080u;                     // code + 128
+    const f16x2v h0 = __builtin_bit_cast(f16x2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+    const f16x2v h1 = __builtin_bit_cast(f16x2v, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+    if constexpr (!V) {
+      const f16x2v bias = {(_Float16)-1152.f, (_Float16)-1152.f};
+      a = __builtin_bit_cast(uint32_t, h0 + bias);
+      b = __builtin_bit_cast(uint32_t, h1 + bias);
+    } else {
+      f16x2v r0, r1;
+      r0.x = (_Float16)__builtin_fmaf((float)h0.x, s, ns);
+      r0.y = (_Float16)__builtin_fmaf((float)h0.y, s, ns);
+      r1.x = (_Float16)__builtin_fmaf((float)h1.x, s, ns);
+      r1.y = (_Float16)__builtin_fmaf((float)h1.y, s, ns);
+      a = __builtin_bit_cast(uint32_t, r0);
+      b = __builtin_bit_cast(uint32_t, r1);
+    }
+  } else {
+    const int32_t xi = (int32_t)x;
+    float f0 = (float)((xi << 24) >> 24), f1 = (float)((xi << 16) >> 24);
+    float f2 = (float)((xi << 8) >> 24), f3 = (float)(xi >> 24);
+    if constexpr (V) {
+      f0 *= s;
+      f1 *= s;
+      f2 *= s;
+      f3 *= s;
+    }
+    a = pack2<T>(f0, f1);
+    b = pack2<T>(f2, f3);
+  }
+}
+// Eight 4-bit codes (one dword; channel 2i in the low nibble of byte i, two's
+// complement) -> four packed pairs.  In fp16, byte k is copied into both halves with its
+// low nibble (biased, + 8) under the exponent of 1024 in the low half and its high nibble
+// times 16 in the high half; K removes both biases with one packed FMA, V applies s.
+template <typename T, bool V>
+__device__ inline void widen_q4(uint32_t x, float s, uint4& o) {
+  uint32_t w[4];
+  if constexpr (std::is_same<T, F16>::value) {
+    const uint32_t u = x ^ 0x88888888u;
+    const f16x2v mul = {(_Float16)1.f, (_Float16)0.0625f};
+    const f16x2v add = {(_Float16)-1032.f, (_Float16)-72.f};
+    const float s16 = s * 0.0625f, nlo = -1032.f * s, nhi = -72.f * s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t y = __builtin_amdgcn_perm(0u, u, 0x0c000c00u | ((uint32_t)k << 16) | (uint32_t)k);
+      const f16x2v z = __builtin_bit_cast(f16x2v, (y & 0x00F0000Fu) | 0x64006400u);
+      if constexpr (!V) {
+        w[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(z, mul, add));
+      } else {
+        f16x2v r;
+        r.x = (_Float16)__builtin_fmaf((float)z.x, s, nlo);
+        r.y = (_Float16)__builtin_fmaf((float)z.y, s16, nhi);
+        w[k] = __builtin_bit_cast(uint32_t, r);
+      }
+    }
+  } else {
+    const int32_t xi = (int32_t)x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float f0 = (float)((xi << (28 - 8 * k)) >> 28), f1 = (float)((xi << (24 - 8 * k)) >> 28);
+      if constexpr (V) {
+        f0 *= s;
+        f1 *= s;
+      }
+      w[k] = pack2<T>(f0, f1);
+    }
+  }
+  o = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Work-group = 4 * KS waves.  Wave w handles the 32 virtual rows 32*(w & 3) .. +31 of
 // the work-group's 128 and the key tiles t with t % KS == (w >> 2) ("key part").  With
 // KS = 2 (small grids: 8 waves, one work-group per CU) the two waves of a row group split
@@ -122,7 +212,7 @@ struct PfWrite {
 // included, read from the pool through the block table after kvb_write_kv).
 constexpr int kModePrefill = 0, kModeCascade = 1, kModePooled = 2;
 
-template <typename T, int D, int KS, int MODE>
+template <typename T, int D, int KS, int MODE, int QB = 0>
 __global__ void __launch_bounds__(256 * KS, 2 / KS)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
@@ -130,7 +220,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                uint16_t* __restrict__ out, const int32_t* __restrict__ cu,
                const int32_t* __restrict__ plen, const int32_t* __restrict__ bt, int bt_stride,
                int batch, int hq, int hkv, int total_q, int max_tiles, float c_log2, int padded,
-               int real, const int32_t* __restrict__ order, PfCascade cas, PfWrite wr) {
+               int real, const int32_t* __restrict__ order, PfCascade cas, PfWrite wr,
+               PfQuant qz) {
   using L = PfLayout<D>;
   constexpr int CPR = L::CPR;
   constexpr int NKK = D / 16;                // MFMA k-steps over head_dim
@@ -140,9 +231,15 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr uint32_t HTB = HT * 2;           // bytes of one K (or V) tile
   constexpr int NPV = 4 * NDB;               // PV MFMAs per tile (2 V reads each)
   static_assert(2 * NLD == NKK, "one load per S step");
+  static_assert(QB == 0 || (MODE == kModePrefill && (QB == 8 || QB == 4)), "quantised pools: prefill only");
+  // quantised pool: code bytes per token row and per block; a block's codes are staged by
+  // QNL loads of 1 KiB (the tail past the block reads as zero) into QAREA bytes of LDS
+  constexpr int QROW = D * (QB ? QB : 16) / 8;
+  constexpr int QNL = (kBlock * QROW + 1023) / 1024;
+  constexpr uint32_t QAREA = QB ? 1024u * QNL : 0u;
 
-  // [key part][parity][K | V][64 x D]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT];
+  // [key part][parity][K | V][64 x D], then (quantised pool) per wave: K codes, V codes
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT + KS * kRowWaves * QAREA];
 
   int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -226,6 +323,52 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int n_self = (self_n + kKT - 1) / kKT;
   const int total = n_pre + n_self;
   const int nstage = max(1, (total - t_begin + KS - 1) / KS);
+  // prefix tiles of this key part (its steps u < n_pre_part compute prefix scores)
+  const int n_pre_part = max(0, (n_pre - t_begin - kh + KS - 1) / KS);
+
+  // Quantised pool: prefix scores are taken with the queries times kscale[e] / kmx (kmx =
+  // the KV head's largest K channel scale, so no query element grows and fp16 cannot
+  // overflow) against the integer codes, and scaled by c_log2 * kmx; the chunk's own
+  // tiles use the plain queries and c_log2.  c_cur is the factor of the tile whose
+  // scores the current step computes.
+  float c_cur = c_log2;
+  if constexpr (QB != 0) {
+    const float* ksc = qz.k_scale + (int64_t)kvh * D;
+    float kmx = 0.f;
+    for (int e = lane; e < D; e += 64) kmx = fmaxf(kmx, ksc[e]);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, sh, 64));
+    const float kinv = kmx > 0.f ? 1.f / kmx : 0.f;
+    if (n_pre_part > 0) {
+      c_cur = fmaxf(c_log2 * kmx, 1e-30f);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 w4 = __builtin_bit_cast(u32x4, qreg[kk]);
+        u32x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 16 * kk + 8 * hf + 2 * i;
+          o4[i] = pack2<T>(lo_f32<T>(w4[i]) * (ksc[e] * kinv), hi_f32<T>(w4[i]) * (ksc[e + 1] * kinv));
+        }
+        qreg[kk] = __builtin_bit_cast(s16x8, o4);
+      }
+    }
+  }
+  // the plain queries again (quantised pool, at the first tile of the chunk itself);
+  // the row is recomputed from an opaque copy of the thread id so that nothing of it
+  // stays live across the loop
+  auto reload_q = [&]() {
+    int tq = threadIdx.x;
+    asm volatile("" : "+v"(tq));
+    const int vr = v0 + 32 * rw + (tq & 31);
+    const int ir = vr / G;
+    const uint16_t* qr = q + ((int64_t)(cu_b + ir) * hq + kvh * G + (vr - ir * G)) * D + 8 * ((tq >> 5) & 1);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (vr < nrows) qreg[kk] = *reinterpret_cast<const s16x8*>(qr + 16 * kk);
+      else qreg[kk] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
 
   f32x16 o[NDB];
 #pragma unroll
@@ -271,6 +414,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const uint16_t* vnb = vn + ((int64_t)cu_b * hkv + kvh) * D;
   const uint32_t self_row_bytes = (uint32_t)(hkv * D * 2);
   const uint32_t bs32 = (uint32_t)block_stride;
+  // quantised pool: the KV head's codes in a block
+  const uint8_t* kq_base = reinterpret_cast<const uint8_t*>(kp) + (int64_t)kvh * kBlock * QROW;
+  const uint8_t* vq_base = reinterpret_cast<const uint8_t*>(vp) + (int64_t)kvh * kBlock * QROW;
 
   // tiles of the chunk itself crossing the causal diagonal, or the end of the keys, need
   // per-row masking (uniform per work-group)
@@ -288,7 +434,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // past the end read as zero; past the last tile the size is zero), plus wave-wide bit
   // masks of "prefix tile" and "needs masking".  Filled 64 tiles at a time with one
   // gathered block-table read; a step then only reads lanes out of it.
-  uint32_t tk_lo, tk_hi, tv_lo, tv_hi, t_nb;
+  uint32_t tk_lo, tk_hi, tv_lo, tv_hi, t_nb, t_pb = 0;
   uint64_t pre_bits, mask_bits;
   int u0 = 0;
   auto refill = [&](int u_first) {
@@ -301,15 +447,25 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const int rows_pre = max(0, min(kBlock, P - jb * kBlock));
     const int row0 = (t - n_pre) * kKT + kBlock * ld_blk;
     const int rows_self = (!pre && t < total) ? max(0, min(kBlock, self_n - row0)) : 0;
-    const uint64_t off = pre ? (uint64_t)(pvalid ? (uint32_t)pb : 0u) * bs32
-                             : (uint64_t)(uint32_t)min(max(row0, 0), C) * (uint32_t)(hkv * D);
-    const uint64_t ak = (uint64_t)(pre ? kbase : knb) + 2 * off;
-    const uint64_t av = (uint64_t)(pre ? vbase : vnb) + 2 * off;
+    uint64_t ak, av;
+    if constexpr (QB == 0) {
+      const uint64_t off = pre ? (uint64_t)(pvalid ? (uint32_t)pb : 0u) * bs32
+                               : (uint64_t)(uint32_t)min(max(row0, 0), C) * (uint32_t)(hkv * D);
+      ak = (uint64_t)(pre ? kbase : knb) + 2 * off;
+      av = (uint64_t)(pre ? vbase : vnb) + 2 * off;
+    } else {
+      // codes: byte offsets, block_stride in bytes
+      const uint64_t offp = (uint64_t)(pvalid ? (uint32_t)pb : 0u) * (uint64_t)bs32;
+      const uint64_t offs = 2 * (uint64_t)(uint32_t)min(max(row0, 0), C) * (uint32_t)(hkv * D);
+      ak = pre ? (uint64_t)kq_base + offp : (uint64_t)knb + offs;
+      av = pre ? (uint64_t)vq_base + offp : (uint64_t)vnb + offs;
+      t_pb = pvalid ? (uint32_t)pb : 0xffffffffu;
+    }
     tk_lo = (uint32_t)ak;
     tk_hi = (uint32_t)(ak >> 32);
     tv_lo = (uint32_t)av;
     tv_hi = (uint32_t)(av >> 32);
-    t_nb = pre ? (pvalid ? (uint32_t)(rows_pre * D * 2) : 0u)
+    t_nb = pre ? (pvalid ? (uint32_t)(rows_pre * QROW) : 0u)
                : (rows_self > 0 ? (uint32_t)(rows_self - 1) * self_row_bytes + D * 2 : 0u);
     pre_bits = __ballot(pre);
     mask_bits = __ballot(tile_needs_mask(t));
@@ -331,9 +487,22 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   };
   // load instruction m (1 KiB) of a part; `pre` (compile-time): the tile is known to be
   // a prefix tile, whose offsets are precomputed
+  // (quantised pool: only the chunk's own tiles are loaded this way, so the offsets are
+  // recomputed from an opaque lane id at each use instead of held in registers)
   auto issue = [&](const LdDesc& d, bool is_v, int m, auto pre_c) {
-    const uint32_t base = is_v ? ld_offV[m] : ld_offK[m];
-    const uint32_t off = decltype(pre_c)::value ? base : base + ld_row(m) * d.dpitch;
+    uint32_t base, row;
+    if constexpr (QB != 0) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int pos = 64 * m + ln;
+      const int rb = pos / CPR, cp = pos - (pos / CPR) * CPR;
+      base = (uint32_t)rb * (uint32_t)(D * 2) + (uint32_t)(is_v ? L::invV(rb, cp) : L::invK(rb, cp)) * 16;
+      row = (uint32_t)rb;
+    } else {
+      base = is_v ? ld_offV[m] : ld_offK[m];
+      row = ld_row(m);
+    }
+    const uint32_t off = decltype(pre_c)::value ? base : base + row * d.dpitch;
     buf_load16_lds(d.rs, off, lds + d.dst + 64 * 16 * m);
   };
   auto issue_all = [&](const LdDesc& d, bool is_v, auto pre_c) {
@@ -342,6 +511,95 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   };
   using Gen = std::false_type;
   using Pre = std::true_type;
+
+  // ---- quantised pool: each wave stages the codes of its own block of a prefix tile
+  // into its code area (K codes, then V codes; no other wave reads them) and later widens
+  // them into the 16-bit tile.  Lane L widens row L/4 of the block, 8-code chunks
+  // (L%4)*NCQ .. +NCQ-1.
+  const uint32_t q_area = (uint32_t)(KS * 4 * HTB) + (uint32_t)w * 2u * QAREA;
+  constexpr int NCQ = D / 32;
+  auto qload = [&](int li, bool is_v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(is_v ? tv_lo : tk_lo), li);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(is_v ? tv_hi : tk_hi), li);
+    const int nb = __builtin_amdgcn_readlane((int)t_nb, li);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, nb, kBufDword3);
+#pragma unroll
+    for (int i = 0; i < QNL; ++i)
+      buf_load16_lds(rs, 1024u * i + 16u * lane, lds + q_area + (is_v ? QAREA : 0u) + 1024u * i);
+  };
+  // the V scale of this lane's row of the block (0 past its valid rows or for a missing
+  // block: the buffer holds only the valid rows' scales)
+  auto qscale = [&](int li) -> float {
+    const int pb = __builtin_amdgcn_readlane((int)t_pb, li);
+    const int nb = __builtin_amdgcn_readlane((int)t_nb, li);
+    const float* sp = qz.v_scale + ((int64_t)max(pb, 0) * hkv + kvh) * kBlock;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sp, (uint32_t)(nb / QROW) * 4u);
+    return __builtin_bit_cast(float, buf_load4(rs, (uint32_t)(lane >> 2) * 4u));
+  };
+  // Widening: lane L holds code dwords NCW of row L/4 of each staged block (contiguous);
+  // both blocks are read before either is widened.
+  constexpr int NCW = NCQ * (QB ? QB : 8) / 4;
+  struct QCodes { uint32_t k[NCW], v[NCW]; };
+  auto qread = [&]() -> QCodes {
+    QCodes c;
+    const char* src = lds + q_area + (uint32_t)((lane >> 2) * QROW + (lane & 3) * NCW * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t* d = h ? c.v : c.k;
+      const char* p = src + (h ? QAREA : 0u);
+      if constexpr (NCW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NCW / 4; ++i) {
+          const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * i);
+          d[4 * i] = x.x; d[4 * i + 1] = x.y; d[4 * i + 2] = x.z; d[4 * i + 3] = x.w;
+        }
+      } else if constexpr (NCW % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < NCW / 2; ++i) {
+          const uint2 x = *reinterpret_cast<const uint2*>(p + 8 * i);
+          d[2 * i] = x.x; d[2 * i + 1] = x.y;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) d[i] = *reinterpret_cast<const uint32_t*>(p + 4 * i);
+      }
+    }
+    return c;
+  };
+  auto qwiden = [&](auto is_v_c, const uint32_t (&cw)[NCW], uint32_t buf_off, float vs) {
+    constexpr bool is_v = decltype(is_v_c)::value;
+    const int r = lane >> 2, c0 = (lane & 3) * NCQ;
+    const int trow = kBlock * ld_blk + r;
+    // LDS byte address of chunk c0 + i of the row.  At head dims 64 and 128 the lane's
+    // chunks differ only in their low bits: K positions are the first one's with those
+    // bits XORed, V positions consecutive; head dim 96 computes each.
+    const uint32_t row_base = part_base + buf_off + (uint32_t)(trow * CPR) * 16;
+    const uint32_t a0 = row_base + (uint32_t)(is_v ? L::posV(trow, c0) : L::posK(trow, c0)) * 16;
+    auto chunk_addr = [&](int i) -> uint32_t {
+      if constexpr (D == 96)
+        return row_base + (uint32_t)(is_v ? L::posV(trow, c0 + i) : L::posK(trow, c0 + i)) * 16;
+      else if constexpr (is_v)
+        return a0 + (uint32_t)(16 * i);
+      else
+        return a0 ^ (uint32_t)(16 * i);
+    };
+    const float ns = -1152.f * vs;
+#pragma unroll
+    for (int i = 0; i < NCQ; ++i) {
+      uint4 o;
+      if constexpr (QB == 8) {
+        widen_q8<T, is_v>(cw[2 * i], vs, ns, o.x, o.y);
+        widen_q8<T, is_v>(cw[2 * i + 1], vs, ns, o.z, o.w);
+      } else {
+        widen_q4<T, is_v>(cw[i], vs, o);
+      }
+      *reinterpret_cast<uint4*>(lds + chunk_addr(i)) = o;
+    }
+  };
+  using IsK = std::false_type;
+  using IsV = std::true_type;
+  float vs_cur = 0.f;                               // V scale of the staged V codes
 
   // ---- per-lane LDS read addresses (bytes, including this key part's base)
   // K operand: row 32*half + lr, logical chunk 2*kk + hf
@@ -437,9 +695,42 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // ---- prologue: K and V of step 0, K of step 1; scores of step 0, whose row maximum is
   // the first reference
   refill(0);
-  issue_all(desc(0, false, kOffK0), false, Gen{});
-  issue_all(desc(0, true, kOffV0), true, Gen{});
-  issue_all(desc(1, false, kOffK1), false, Gen{});
+  if constexpr (QB == 0) {
+    issue_all(desc(0, false, kOffK0), false, Gen{});
+    issue_all(desc(0, true, kOffV0), true, Gen{});
+    issue_all(desc(1, false, kOffK1), false, Gen{});
+  } else {
+    // tiles 0 and 1 widened here, in two rounds through the one code area; the V codes
+    // of tile 1 and the K codes of tile 2 stay staged for step 0
+    const bool p0 = pre_bits & 1, p1 = (pre_bits >> 1) & 1, p2 = (pre_bits >> 2) & 1;
+    if (p0) {
+      qload(0, false);
+      qload(0, true);
+      vs_cur = qscale(0);
+    } else {
+      issue_all(desc(0, false, kOffK0), false, Gen{});
+      issue_all(desc(0, true, kOffV0), true, Gen{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);                  // this wave's own block
+    if (p0) {
+      const QCodes c = qread();
+      qwiden(IsK{}, c.k, kOffK0, 0.f);
+      qwiden(IsV{}, c.v, kOffV0, vs_cur);
+    }
+    if (p1) {
+      qload(1, false);
+      qload(1, true);
+      vs_cur = qscale(1);
+    } else {
+      issue_all(desc(1, false, kOffK1), false, Gen{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (p1) {
+      const QCodes c = qread();
+      qwiden(IsK{}, c.k, kOffK1, 0.f);
+    }
+    if (p2) qload(2, false);
+  }
   f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -455,14 +746,14 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     float m = fmaxf(s_cur[0][0], s_cur[1][0]);
 #pragma unroll
     for (int rr = 1; rr < 16; ++rr) m = fmaxf(m, fmaxf(s_cur[0][rr], s_cur[1][rr]));
-    m = halves_max(m) * c_log2;
+    m = halves_max(m) * c_cur;
     // a row with no visible key in its first tile has none in the later ones either
     // (visibility only shrinks with the key index); its reference stays 0
     m_run = m == -INFINITY ? 0.f : m;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      s_cur[0][rr] = fmaf(s_cur[0][rr], c_log2, -m_run);
-      s_cur[1][rr] = fmaf(s_cur[1][rr], c_log2, -m_run);
+      s_cur[0][rr] = fmaf(s_cur[0][rr], c_cur, -m_run);
+      s_cur[1][rr] = fmaf(s_cur[1][rr], c_cur, -m_run);
     }
   }
   __syncthreads();                                  // K buffer 0 is reloaded in step 0
@@ -475,7 +766,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     constexpr int PAR = decltype(par_c)::value;
     constexpr uint32_t offK_ld = PAR ? kOffK1 : kOffK0, offV_ld = PAR ? kOffV0 : kOffV1;
     constexpr uint32_t offK_rd = PAR ? kOffK0 : kOffK1, offV_rd = PAR ? kOffV1 : kOffV0;
-    if (j + 2 - u0 >= 64) {                         // next 64 tiles of the sequence
+    // next 64 tiles of the sequence (a quantised pool stages codes one tile further)
+    if (j + 2 + (QB ? 1 : 0) - u0 >= 64) {
       keep_branch();
       u0 = j + 1;
       refill(u0);
@@ -484,9 +776,32 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const LdDesc dk = desc(lk, false, offK_ld);
     const LdDesc dv = desc(lv, true, offV_ld);
     const bool need_mask = (mask_bits >> lv) & 1;
+    // K of tile j+2 and V of tile j+1: loaded straight into LDS, or (prefix tiles of a
+    // quantised pool) widened from the codes staged in the previous step, whose place
+    // then takes the codes of K j+3 and V j+2
+    bool k_direct = true, v_direct = true;
+    if constexpr (QB != 0) {
+      if (!decltype(pre_c)::value && j + 1 == n_pre_part) {   // tile j+1: the chunk's first own tile
+        keep_branch();
+        reload_q();
+        c_cur = c_log2;
+      }
+      const bool kq = decltype(pre_c)::value || ((pre_bits >> lk) & 1);
+      const bool vq = decltype(pre_c)::value || ((pre_bits >> lv) & 1);
+      const QCodes c = qread();
+      if (kq) qwiden(IsK{}, c.k, offK_ld, 0.f);
+      if (vq) qwiden(IsV{}, c.v, offV_ld, vs_cur);
+      if ((pre_bits >> (lk + 1)) & 1) qload(lk + 1, false);
+      if ((pre_bits >> (lv + 1)) & 1) {
+        qload(lv + 1, true);
+        vs_cur = qscale(lv + 1);
+      }
+      k_direct = !kq;
+      v_direct = !vq;
+    }
     if (!wave_active) {
-      issue_all(dk, false, pre_c);
-      issue_all(dv, true, pre_c);
+      if (k_direct) issue_all(dk, false, pre_c);
+      if (v_direct) issue_all(dv, true, pre_c);
       return;
     }
     // Hand-interleaved: each step of a phase is a scheduling region of its own, so
@@ -509,8 +824,11 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       __builtin_amdgcn_sched_barrier(0);
       // one load per step: bunched at the step start, the loads of all waves queue at
       // the memory pipeline and stall the issuing waves
-      if (kk < NLD) issue(dk, false, kk, pre_c);
-      else issue(dv, true, kk - NLD, pre_c);
+      if (kk < NLD) {
+        if (k_direct) issue(dk, false, kk, pre_c);
+      } else {
+        if (v_direct) issue(dv, true, kk - NLD, pre_c);
+      }
       if (kk + 2 < NKK) {
         ka[kk + 2][0] = k_operand(offK_rd, kk + 2, 0);
         ka[kk + 2][1] = k_operand(offK_rd, kk + 2, 1);
@@ -566,7 +884,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
         if (u * NPV / 8 != i) continue;
         const int h = u >> 2, r0 = (u & 3) * 4;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_log2, -m_run);
+        for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_cur, -m_run);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -584,7 +902,6 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // part take the precomputed offsets; the chunk's own tiles and the tail the general
   // form.  Every step ends in one barrier in both loops, so the key parts may switch
   // loops at different steps.
-  const int n_pre_part = max(0, (n_pre - t_begin - kh + KS - 1) / KS);
   int j = 0;
   for (; j + 3 < n_pre_part && j + 2 < nstage; j += 2) {
     step(j, Par0{}, Pre{});
@@ -798,12 +1115,13 @@ int64_t prefill_plan_bytes(int batch, int hq, int total_q) {
   return (items * 4 + 255) / 256 * 256;
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int QB = 0>
 static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void* kn, const void* vn,
                                    void* out, const int32_t* cu, const int32_t* plen,
                                    const int32_t* bt, int bt_stride, int batch, int hq,
                                    int total_q, int max_q_len, float scale, const PfCascade& cas,
-                                   int32_t* plan_ws, hipStream_t s, const int64_t* slots = nullptr) {
+                                   int32_t* plan_ws, hipStream_t s, const int64_t* slots = nullptr,
+                                   PfQuant qz = PfQuant{nullptr, nullptr}) {
   const PfWrite wr{slots, (uint16_t*)p.k, (uint16_t*)p.v};
   const int G = hq / p.num_kv_heads;
   const long long rows = (long long)max_q_len * G;
@@ -826,17 +1144,17 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
     order = plan_ws;
   }
   if (split)
-    hipLaunchKernelGGL((prefill_kernel<T, D, 2, MODE>), dim3((unsigned)padded), dim3(512), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 2, MODE, QB>), dim3((unsigned)padded), dim3(512), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, order, cas, wr);
+                       (int)padded, (int)real, order, cas, wr, qz);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE>), dim3((unsigned)padded), dim3(256), 0, s,
+    hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE, QB>), dim3((unsigned)padded), dim3(256), 0, s,
                        (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
                        (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
                        cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
-                       (int)padded, (int)real, order, cas, wr);
+                       (int)padded, (int)real, order, cas, wr, qz);
   return hipGetLastError();
 }
 
@@ -860,6 +1178,26 @@ hipError_t launch_prefill(const kvb_pool& p, const void* q, const void* kn, cons
     return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill>(p, q, kn, vn, out, cu, plen, bt, bt_stride,
                                                              batch, hq, total_q, max_q_len, scale, none,
                                                              (int32_t*)plan_ws, s, slots);
+  });
+}
+
+hipError_t launch_prefill_quant(const kvb_pool_q8& p, int bits, int dtype, const void* q,
+                                const void* kn, const void* vn, void* out, const int32_t* cu,
+                                const int32_t* plen, const int32_t* bt, int bt_stride, int batch,
+                                int hq, int total_q, int max_q_len, float scale, void* plan_ws,
+                                hipStream_t s) {
+  // the kernel takes the code pools where it takes the 16-bit ones (block_stride in bytes)
+  const kvb_pool view{p.k, p.v, p.block_stride, p.num_blocks, kBlock, p.num_kv_heads, p.head_dim, dtype};
+  const PfCascade none{nullptr, 0, 0, 0, 1, nullptr, nullptr, 0};
+  const PfQuant qz{p.v_scale, p.k_scale};
+  return dispatch_prefill(view, [&](auto t, auto d) {
+    if (bits == 4)
+      return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill, 4>(
+          view, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, none,
+          (int32_t*)plan_ws, s, nullptr, qz);
+    return launch_prefill_t<decltype(t), decltype(d)::value, kModePrefill, 8>(
+        view, q, kn, vn, out, cu, plen, bt, bt_stride, batch, hq, total_q, max_q_len, scale, none,
+        (int32_t*)plan_ws, s, nullptr, qz);
   });
 }
 

@@ -457,8 +457,8 @@ def main(argv=None):
     ap.add_argument("--separate-write", action="store_true",
                     help="step with kvb_write_kv of the chunk before kvb_paged_prefill instead of "
                          "kvb_paged_prefill_write (prefill and slot scatter in one launch)")
-    ap.add_argument("--only", choices=["step", "prefill", "prefill_write", "decode_workload",
-                                       "copy", "copy_blocks", "peaks"],
+    ap.add_argument("--only", choices=["step", "prefill", "prefill_write", "prefill_q8", "prefill_q4",
+                                       "decode_workload", "copy", "copy_blocks", "peaks"],
                     default="step", help="profiling aid: run only one part")
     args = ap.parse_args(argv)
 
@@ -497,6 +497,12 @@ def main(argv=None):
 
     w = make_config(args.config, with_decode=True)
     up = Uploaded(torch, kvb, w)
+    if args.only in ("prefill_q8", "prefill_q4"):
+        # profiling aid: the quantised-pool prefill against the 16-bit one, both cold
+        cold, _ = time_prefill(torch, up, probe, "prefill", args.steps, args.settle_ms)
+        r = bench_prefill_q8(torch, kvb, up, probe, cold["mean"], args, 8 if args.only == "prefill_q8" else 4)
+        print(json.dumps({"config": args.config, "part": args.only, **r}))
+        return 0
     if args.only in ("prefill", "prefill_write"):
         # profiling aid: the prefill call alone, settled, then launched after flushes
         cold, warm = time_prefill(torch, up, probe, args.only, args.steps, args.settle_ms)
@@ -649,7 +655,8 @@ def main(argv=None):
     if not args.no_q8:
         up = Uploaded(torch, kvb, w)
         res["prefill_q8"] = bench_prefill_q8(torch, kvb, up, probe, pe["ms_cold"]["mean"], args)
-        progress("8-bit pool prefill timed")
+        res["prefill_q4"] = bench_prefill_q8(torch, kvb, up, probe, pe["ms_cold"]["mean"], args, 4)
+        progress("8-bit and 4-bit pool prefill timed")
         del up
 
     if not args.no_cpu_baseline:
@@ -767,9 +774,9 @@ def bench_copy_blocks(torch, kvb, args):
     return res
 
 
-def bench_prefill_q8(torch, kvb, up, probe, ms16_cold, args):
-    """The step's prefill with the cached prefix in the 8-bit pool: the prefix tokens
-    written by kvb_write_kv_q8 (K scales from their per-channel maxima), then
+def bench_prefill_q8(torch, kvb, up, probe, ms16_cold, args, bits=8):
+    """The step's prefill with the cached prefix in the 8-bit (or 4-bit) pool: the prefix
+    tokens written by kvb_write_kv_q8 (K scales from their per-channel maxima), then
     kvb_paged_prefill_q8, timed cold like the 16-bit prefill."""
     w = up.w
     slot_list = []
@@ -779,8 +786,8 @@ def bench_prefill_q8(torch, kvb, up, probe, ms16_cold, args):
     slots = torch.from_numpy(np.unique(np.concatenate(slot_list))).to("cuda:0")
     kt = up.k[slots // 16, :, slots % 16, :].contiguous()
     vt = up.v[slots // 16, :, slots % 16, :].contiguous()
-    k_scale = (kt.float().abs().amax(dim=0) / 127.0).contiguous()
-    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, k_scale)
+    k_scale = (kt.float().abs().amax(dim=0) / (127.0 if bits == 8 else 7.0)).contiguous()
+    p8 = kvb.PoolQ8.empty(w.k_pool.shape[0], w.num_kv_heads, w.head_dim, k_scale, bits=bits)
     kvb.write_kv_q8(p8, kt, vt, slots)
     del kt, vt
     out = torch.empty_like(up.q)
@@ -795,7 +802,7 @@ def bench_prefill_q8(torch, kvb, up, probe, ms16_cold, args):
     settle(torch, run, min(args.settle_ms, 200))
     cold = stats(time_each(torch, run, max(args.steps, 10), before=probe.flush))
     pf = prefill_flops(w)
-    return {"pool": "8-bit codes, per-channel K scales, per-token V scales",
+    return {"pool": f"{bits}-bit codes, per-channel K scales, per-token V scales",
             "ms_cold": cold, "tflops_cold": pf / (cold["mean"] * 1e-3) / 1e12,
             "ms_cold_16bit_pool": ms16_cold, "time_vs_16bit": cold["mean"] / ms16_cold}
 

@@ -284,12 +284,13 @@ kvb_status kvb_paged_decode_q8(const kvb_pool_q8* pool, int32_t dtype, const voi
 
 /* Paged prefill over the 8-bit pool: kvb_paged_prefill with the cached prefix read as the
  * values its codes stand for (the chunk's own K/V are the call's 16-bit rows).  The
- * prefix blocks of each sequence are first widened into a 16-bit staging pool inside
- * the workspace (one staged block per sequence and logical block, shared blocks widened
- * once per sequence that reads them), then the 16-bit prefill runs on it.  q, k_new,
- * v_new, out in `dtype`.  workspace: (device, required) at least
- * kvb_paged_prefill_q8_workspace_size(...) bytes; contents on entry do not matter.
- * Other arguments as kvb_paged_prefill. */
+ * codes of each prefix block are staged in LDS and widened there to 16 bits (V times its
+ * token's scale, rounded to nearest even; the K channel scales are folded into the
+ * queries), so no widened copy of the prefix is written anywhere.  q, k_new, v_new, out
+ * in `dtype`.  workspace: (device, optional) NULL (no dispatch plan), or at least
+ * kvb_paged_prefill_q8_workspace_size(...) bytes (the dispatch plan, as for
+ * kvb_paged_prefill; independent of the prefix lengths); contents on entry do not
+ * matter.  Other arguments as kvb_paged_prefill. */
 kvb_status kvb_paged_prefill_q8(const kvb_pool_q8* pool, int32_t dtype, const void* q,
                                 const void* k_new, const void* v_new, void* out,
                                 const int32_t* cu_q_lens, const int32_t* prefix_lens,

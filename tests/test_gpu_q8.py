@@ -186,7 +186,8 @@ Q8_PREFILL_CASES = [
     (821, "bf16", 16, 2, 128, [0, 100, 513, 2048], [37, 200, 1, 64], "pairs"),
     (822, "fp16", 40, 8, 96, [700, 33], [129, 300], "none"),
     (823, "bf16", 8, 8, 64, [17, 1000, 256], [16, 50, 99], "all"),
-    # several rounds of work-groups: the dispatch plan runs on the staged pool
+    # several rounds of work-groups (dispatch plan; a prefix past 64 tiles refills the
+    # per-wave tile table, whose codes are staged one tile ahead)
     (824, "fp16", 32, 8, 128, [4500, 100, 0, 2047], [512, 480, 300, 511], "pairs"),
 ]
 
