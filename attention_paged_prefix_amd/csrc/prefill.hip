@@ -652,6 +652,19 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     }
   };
   // exp2 of the two scores of pair e (kp4 = e/4, element e%4) of a tile, packed
+  // At head dims 64 and 96 phase 2 of a step (PV MFMAs) also takes the exponentials of
+  // the first half of the next tile's scores (pe), so that both phases carry about the
+  // same VALU work under their MFMAs; at 128 the registers are not there.
+  constexpr bool kEarlyExp = D <= 96;
+  float pe[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) pe[rr] = 0.f;
+  // packed probabilities of pair e, the first half from pe
+  auto pack_pair_pe = [&](const f32x16 (&x)[2], int e) -> uint32_t {
+    const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
+    if (kEarlyExp && mb == 0) return pack2<T>(pe[r0 + 2 * ee], pe[r0 + 2 * ee + 1]);
+    return pack2<T>(fast_exp2(x[mb][r0 + 2 * ee]), fast_exp2(x[mb][r0 + 2 * ee + 1]));
+  };
   auto pack_pair = [&](const f32x16 (&x)[2], int e) -> uint32_t {
     const int kp4 = e >> 2, ee = e & 3, mb = kp4 >> 1, r0 = (kp4 & 1) * 8;
     return pack2<T>(fast_exp2(x[mb][r0 + 2 * ee]), fast_exp2(x[mb][r0 + 2 * ee + 1]));
@@ -755,6 +768,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       s_cur[0][rr] = fmaf(s_cur[0][rr], c_cur, -m_run);
       s_cur[1][rr] = fmaf(s_cur[1][rr], c_cur, -m_run);
     }
+    if constexpr (kEarlyExp) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) pe[rr] = fast_exp2(s_cur[0][rr]);
+    }
   }
   __syncthreads();                                  // K buffer 0 is reloaded in step 0
 
@@ -840,7 +857,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
         if (e * NKK / 16 == kk) {
           // each packed word is pinned here, in phase 1: pinning the assembled operand
           // instead made the compiler rebuild it with copies before the PV product
-          uint32_t w2 = pack_pair(s_cur, e);
+          uint32_t w2 = pack_pair_pe(s_cur, e);
           asm volatile("" : "+v"(w2));
           pw[e >> 2][e & 3] = w2;
         }
@@ -885,10 +902,19 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
         const int h = u >> 2, r0 = (u & 3) * 4;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) s_nxt[h][r0 + rr] = fmaf(s_nxt[h][r0 + rr], c_cur, -m_run);
+        // exponentials of the first half one unit group later, beside the second half's FMAs
+        if (kEarlyExp && h == 1) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) pe[r0 + rr] = fast_exp2(s_nxt[0][r0 + rr]);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]));   // scaled scores stay in phase 2
+    if constexpr (kEarlyExp) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) asm volatile("" ::"v"(pe[rr]));
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
   };

@@ -134,6 +134,34 @@ def read_traffic(kernel_key: str):
         return None
 
 
+def read_counters(kernel_key: str):
+    """Shader-sequencer counters per launch from a committed rocprofv3 summary
+    (profiles/<key>.sq.txt: MFMA utilisation, instruction mix, LDS bank conflicts), if it was
+    taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_key}.sq.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in fields.get("source_files", "").split(","):
+        h.update(open(os.path.join(ROOT, src.strip()), "rb").read())
+    if h.hexdigest()[:16] != fields.get("source_sha256_16"):
+        return None
+    out = {}
+    for k in ("mfma_util_percent", "valu_per_mfma", "lds_per_mfma", "salu_per_mfma",
+              "lds_bank_conflicts_per_lds_inst", "l2_hit_rate", "wave_cycles_waiting_frac"):
+        try:
+            out[k] = float(fields[k])
+        except (KeyError, ValueError):
+            pass
+    return out or None
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same prefill workload:
     whole (sequence, query head) problems in order, repeating the workload until about
@@ -615,6 +643,7 @@ def main(argv=None):
     res["roofline"] = {"bound": "mfma", "kernel": "paged_" + pname, "achieved": pe["tflops_cold_mean"],
                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": pe["frac_mfma_peak"],
                        "traffic": read_traffic(f"paged_{pname}_{args.config}"),
+                       "counters": read_counters(f"paged_{pname}_{args.config}"),
                        "timing": "per-launch HIP events after a 1 GiB read flush; mean of "
                                  f"{cold['n']} launches (dispatch-plan kernel included)",
                        "achieved_median": pe["tflops_cold_median"], "achieved_best": pe["tflops_cold_best"],
@@ -631,6 +660,8 @@ def main(argv=None):
         uo = Uploaded(torch, kvb, wo)
         c_, w_ = time_prefill(torch, uo, probe, pname, max(args.steps, 20), min(args.settle_ms, 200.0))
         e = prefill_entry(wo, c_, w_, peaks)
+        e["traffic"] = read_traffic(f"paged_{pname}_{name}")
+        e["counters"] = read_counters(f"paged_{pname}_{name}")
         ms = time_launches(torch, lambda: uo.part("write_kv"), max(args.steps, 10))
         e["write_kv"] = {"tokens": wo.total_q, "ms": ms,
                          "gbps": write_kv_bytes(wo.total_q, wo) / (ms * 1e-3) / 1e9}
