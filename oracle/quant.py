@@ -131,20 +131,28 @@ def paged_decode_q8(k_codes, v_codes, v_scales, k_scale, q, context_lens, block_
 
 
 def paged_prefill_q8(k_codes, v_codes, v_scales, k_scale, q, k_new, v_new, cu_q_lens, prefix_lens,
-                     block_tables, num_q_heads: int, scale: float, dtype: str):
+                     block_tables, num_q_heads: int, scale: float, dtype: str, select=None):
     """Chunk prefill (as ``attention.paged_prefill``: row i of sequence b at position
     ``P_b + i`` sees the whole cached prefix and chunk tokens ``0..i``) with the cached
     prefix read from the 8-bit pool as the values its codes stand for; the chunk's own
-    K/V are the call's 16-bit rows.  Returns float64 ``[T][Hq][d]``."""
+    K/V are the call's 16-bit rows.  Returns float64 ``[T][Hq][d]``; with ``select``, a
+    list of (b, h, rows), only those rows, as a dict {(b, h): out[rows][d]} (the same
+    arithmetic, for sampled rows of large workloads)."""
     cu = np.asarray(cu_q_lens, dtype=np.int64)
     P = np.asarray(prefix_lens, dtype=np.int64)
     Hkv = k_codes.shape[1]
     G = num_q_heads // Hkv
     T, _, d = q.shape
-    out = np.zeros((T, num_q_heads, d), dtype=np.float64)
+    want = None
+    if select is not None:
+        want = {}
+        for b, h, rows in select:
+            want.setdefault(int(b), []).append((int(h), np.asarray(rows, dtype=np.int64)))
+    res = {}
+    out = np.zeros((T, num_q_heads, d), dtype=np.float64) if want is None else None
     for b in range(len(P)):
         C = int(cu[b + 1] - cu[b])
-        if C == 0:
+        if C == 0 or (want is not None and b not in want):
             continue
         n = int(P[b])
         j = np.arange(n)
@@ -153,8 +161,15 @@ def paged_prefill_q8(k_codes, v_codes, v_scales, k_scale, q, k_new, v_new, cu_q_
         Vp = dequant_v(gather_kv(v_codes, block_tables[b], n), v_scales[blocks, :, j % BLOCK_SIZE])
         K = np.concatenate([Kp, decode_bits(k_new[cu[b]:cu[b + 1]], dtype)], axis=0)
         V = np.concatenate([Vp, decode_bits(v_new[cu[b]:cu[b + 1]], dtype)], axis=0)
+        if want is not None:
+            for h, rows in want[b]:
+                assert np.all(rows < C)
+                o, _ = attend(decode_bits(q[cu[b] + rows, h], dtype), K[:, h // G], V[:, h // G],
+                              n + rows, scale)
+                res[(b, h)] = o
+            continue
         pos = n + np.arange(C)
         for h in range(num_q_heads):
             o, _ = attend(decode_bits(q[cu[b]:cu[b + 1], h], dtype), K[:, h // G], V[:, h // G], pos, scale)
             out[cu[b]:cu[b + 1], h] = o
-    return out
+    return res if want is not None else out

@@ -228,6 +228,71 @@ def test_prefill_q8_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+@pytest.mark.parametrize("name,bits", [("ragged_d96", 8), ("ragged_d96", 4), ("long_prefix", 8)])
+def test_prefill_quant_full_size_sampled(name, bits):
+    """The benchmark's quantised-pool prefill at full size, in its launch configuration:
+    the prefix tokens written by kvb_write_kv_q8/_q4 into a poisoned pool (K scales from
+    their per-channel maxima), then sampled rows (first/last, tile and block edges, random;
+    heads at GQA group edges) of a few sequences against the oracle, which quantises those
+    sequences' tokens itself."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    from oracle import quant
+    u = _util()
+    w = make_config(name)
+    dt, hq, hkv, d = w.dtype, w.num_q_heads, w.num_kv_heads, w.head_dim
+    cmax = 127 if bits == 8 else 7
+    slots = _prefix_slots(w)
+    kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+    ks = channel_scales(oracle_f32(kt, dt), cmax)
+    nb = w.k_pool.shape[0]
+    pool = kvb.PoolQ8.empty(nb, hkv, d, torch.from_numpy(ks), device="cuda:0", bits=bits)
+    pool.k.fill_(127 if bits == 8 else 0x77)          # unwritten codes at the extremes
+    pool.v.fill_(-127 if bits == 8 else 0x99)
+    pool.v_scale.fill_(float("nan"))                  # and NaN V scales
+    kvb.write_kv_q8(pool, u.to_dev(kt, dt), u.to_dev(vt, dt), u.idev(slots, torch.int64))
+    del kt, vt
+    got = u.to_bits(kvb.paged_prefill_q8(pool, u.to_dev(w.q, dt), u.to_dev(w.k_new, dt),
+                                         u.to_dev(w.v_new, dt), u.idev(w.cu_q_lens),
+                                         u.idev(w.prefix_lens), u.idev(w.block_tables), w.scale,
+                                         int(w.q_lens.max()), int(w.prefix_lens.max())))
+    torch.cuda.synchronize()
+    vals = oracle.decode_bits(got, dt)
+    assert np.isfinite(vals).all()
+    rng = np.random.default_rng(97)
+    B = w.batch
+    seqs = sorted(set([0, B - 1] + [int(x) for x in rng.integers(0, B, size=min(B, 4))]))
+    select = []
+    for b in seqs:
+        C = int(w.q_lens[b])
+        if C == 0:
+            continue
+        cand = {0, 1, 15, 16, 31, 32, 63, 64, 127, 128, C // 2, C - 2, C - 1}
+        cand |= set(int(x) for x in rng.integers(0, C, size=4))
+        rows = sorted(r for r in cand if 0 <= r < C)
+        G = hq // hkv
+        heads = sorted(h for h in {0, G - 1, G, hq - 1, int(rng.integers(0, hq))} if 0 <= h < hq)
+        for h in heads:
+            select.append((b, h, rows))
+    sl = []
+    for b in seqs:
+        j = np.arange(int(w.prefix_lens[b]))
+        sl.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    sl = np.unique(np.concatenate(sl))
+    kc = np.full((nb, hkv, 16, d), 127, np.int8)
+    vc = np.full((nb, hkv, 16, d), -127, np.int8)
+    vs = np.full((nb, hkv, 16), np.nan, np.float32)
+    kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, _tokens_at(w.k_pool, sl), _tokens_at(w.v_pool, sl),
+                                   sl, dt, cmax)
+    ref = quant.paged_prefill_q8(kc, vc, vs, ks, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens,
+                                 w.block_tables, hq, w.scale, dt, select=select)
+    worst = 0.0
+    for (b, h, rows) in select:
+        g = vals[w.cu_q_lens[b] + np.asarray(rows), h]
+        worst = max(worst, float(np.max(np.abs(g - ref[(b, h)]))))
+    assert worst <= u.TOL[dt], f"max abs err {worst}"
+
+
 # ------------------------------------------------------------------ 4-bit pool
 
 def _pool_q4(kc, vc, vs, ks):

@@ -227,3 +227,27 @@ def test_4bit_error_bound_and_exact_reduction():
     ref = oracle.paged_decode(K16, V16, q, ctx, bt, 0.125, dtype)
     got = quant.paged_decode_q8(Kc, Vc, Vs, k_scale, q, ctx, bt, 0.125, dtype)
     assert np.array_equal(got, ref)
+
+
+def test_prefill_q8_select_matches_full():
+    """The oracle's row selection computes the same values as its full prefill (up to the
+    summation order of the matrix products, which depends on the number of rows)."""
+    from workloads import make_custom, channel_scales
+    w = make_custom(851, "bf16", 8, 2, 64, [40, 0, 90], [17, 5, 33], share="pairs", poison=False)
+    slots = []
+    for b in range(w.batch):
+        j = np.arange(int(w.prefix_lens[b]))
+        slots.append(w.block_tables[b][j // 16].astype(np.int64) * 16 + j % 16)
+    slots = np.unique(np.concatenate(slots))
+    kt = np.ascontiguousarray(w.k_pool[slots // 16, :, slots % 16, :])
+    vt = np.ascontiguousarray(w.v_pool[slots // 16, :, slots % 16, :])
+    ks = channel_scales(oracle.decode_bits(kt, "bf16").astype(np.float32))
+    nb = w.k_pool.shape[0]
+    kc, vc, vs = quant.write_kv_q8(np.zeros((nb, 2, 16, 64), np.int8), np.zeros((nb, 2, 16, 64), np.int8),
+                                   np.zeros((nb, 2, 16), np.float32), ks, kt, vt, slots, "bf16")
+    args = (kc, vc, vs, ks, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens, w.block_tables, 8, w.scale, "bf16")
+    full = quant.paged_prefill_q8(*args)
+    sel = [(0, 3, [0, 16]), (2, 7, [1, 32]), (1, 0, [4])]
+    part = quant.paged_prefill_q8(*args, select=sel)
+    for (b, h, rows) in sel:
+        assert np.allclose(part[(b, h)], full[w.cu_q_lens[b] + np.asarray(rows), h], rtol=0, atol=1e-12)
