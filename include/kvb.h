@@ -153,8 +153,8 @@ kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* o
  * batches of up to 1024 sequences the (KV head, sequence, block) list of the whole batch
  * is cut into equal ranges, one per wave of a grid that is resident at once; a sequence
  * whose blocks fall into several ranges has partial results (unnormalised output, running
- * max, sum) merged by log-sum-exp.  split_blocks > 0 fixes the range length in blocks
- * (values above 128 count as 128); 0 balances the ranges over the device.  Larger batches
+ * max, sum) merged by log-sum-exp.  split_blocks > 0 fixes the blocks each wave takes
+ * (values above 64 count as 64); 0 balances the ranges over the device.  Larger batches
  * split each sequence into groups of split_blocks blocks (0: a size from the host bounds).
  * A context length <= 0 gives a zero output row.
  * q, out: (device) [batch][num_q_heads][head_dim]; context_lens: (device) int32 [batch]
