@@ -1120,15 +1120,23 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
     key[i] = k;
   }
   __syncthreads();
+  // Bitonic sort.  A wave's pairs i cover the same 128 consecutive elements (per 256
+  // pairs) in every pass with stride <= 64, so such a pass depends only on the same wave's
+  // previous pass (LDS operations of one wave complete in order) unless that pass had a
+  // larger stride: a wave fence suffices there, and only passes with a larger stride, or
+  // right after one, wait for the whole work-group.
   for (int size = 2; size <= N; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride > 64 || (stride == 64 && size >= 256)) __syncthreads();
       for (int i = threadIdx.x; i < N / 2; i += kPlanThreads) {
         const int a = 2 * i - (i & (stride - 1));      // pair (a, a + stride), bit `stride` of a clear
         const uint64_t x = key[a], y = key[a + stride];
         if ((x > y) == ((a & size) == 0)) { key[a] = y; key[a + stride] = x; }
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
+  __syncthreads();
   for (int i = threadIdx.x; i < n; i += kPlanThreads) order[lo + i] = (int32_t)(uint32_t)key[i];
 }
 

@@ -191,6 +191,55 @@ def test_prefill_dispatch_plan_gives_same_bits():
     assert err <= u.TOL["bf16"], f"max abs err {err}"
 
 
+@pytest.mark.parametrize("batch,G,cmax", [(32, 4, 512), (64, 8, 1024)])
+def test_prefill_dispatch_plan_is_a_stable_longest_first_permutation(batch, G, cmax):
+    """The plan the prefill writes into its workspace: within each XCD's range of logical
+    work items a permutation of that range, ordered by 32 cost buckets (key count of the
+    item's last row relative to the range's largest, empty items last) and, inside a
+    bucket, by table order.  Ranges of 512 and 4096 items (several sort passes across the
+    waves of the plan's work-group, several pairs per thread)."""
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    rng = np.random.default_rng(batch)
+    hkv, d = 8, 64
+    P = [int(x) for x in rng.integers(0, 16384 if batch <= 32 else 4096, size=batch)]
+    C = [int(x) for x in rng.integers(1, cmax + 1, size=batch)]
+    C[0] = cmax
+    hq = hkv * G
+    w = make_custom(917 + batch, "bf16", hq, hkv, d, P, C, poison=False)
+    dev = u.Dev(w)
+    mq, mp = int(w.q_lens.max()), int(w.prefix_lens.max())
+    need = kvb.paged_prefill_workspace_size(w.batch, hq, d, w.total_q, mp)
+    ws = torch.full((need // 4,), -7, dtype=torch.int32, device="cuda:0")
+    kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale, mq, mp,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    max_tiles = (mq * G + 127) // 128
+    real = batch * hkv * max_tiles
+    padded = (real + 7) // 8 * 8
+    per = padded // 8
+    assert per <= 4096 and real >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    order = ws[:real].cpu().numpy()
+    cu = np.asarray(w.cu_q_lens, dtype=np.int64)
+
+    def cost(lid):
+        tile, b = lid % max_tiles, (lid // max_tiles) % batch
+        nrows, v0 = int(cu[b + 1] - cu[b]) * G, tile * 128
+        return int(w.prefix_lens[b]) + (min(nrows, v0 + 128) - 1) // G + 1 if v0 < nrows else 0
+
+    for lo in range(0, real, per):
+        n = min(per, real - lo)
+        got = order[lo:lo + n]
+        assert sorted(got.tolist()) == list(range(lo, lo + n))
+        costs = [cost(lid) for lid in range(lo, lo + n)]
+        cmx, cmn = max(costs), min([c for c in costs if c > 0] or [0])
+        if 2 * cmn > cmx:
+            assert got.tolist() == list(range(lo, lo + n))
+            continue
+        keys = [((31 - min(31, cost(l) * 32 // (cmx + 1))) if cost(l) > 0 else 32, l) for l in got.tolist()]
+        assert keys == sorted(keys)
+
+
 @pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:1],
                          ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
 def test_prefill_pooled_matches_oracle(case):
