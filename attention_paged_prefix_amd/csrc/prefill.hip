@@ -212,8 +212,8 @@ __device__ inline void widen_q4(uint32_t x, float s, uint4& o) {
 // included, read from the pool through the block table after kvb_write_kv).
 constexpr int kModePrefill = 0, kModeCascade = 1, kModePooled = 2;
 
-template <typename T, int D, int KS, int MODE, int QB = 0>
-__global__ void __launch_bounds__(256 * KS, 2 / KS)
+template <typename T, int D, int KS, int MODE, int QB = 0, int RW = kRowWaves>
+__global__ void __launch_bounds__(64 * RW * KS, RW * KS == 4 ? 2 : 1)
 prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
                int64_t block_stride, int num_blocks, const uint16_t* __restrict__ q,
                const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
@@ -231,6 +231,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr uint32_t HTB = HT * 2;           // bytes of one K (or V) tile
   constexpr int NPV = 4 * NDB;               // PV MFMAs per tile (2 V reads each)
   static_assert(2 * NLD == NKK, "one load per S step");
+  // RW row waves of 32 rows: 4 (each wave stages K and V of its block of every tile), or 8
+  // (ordinary prefill, one key part: waves 0-3 stage the K blocks, waves 4-7 the V blocks)
+  static_assert(RW == 4 || (RW == 8 && KS == 1 && MODE == kModePrefill), "row-wave forms");
+  constexpr int BM = 32 * RW;                // virtual rows per work-group
   static_assert(QB == 0 || (MODE == kModePrefill && (QB == 8 || QB == 4)), "quantised pools: prefill only");
   // quantised pool: code bytes per token row and per block; a block's codes are staged by
   // QNL loads of 1 KiB (the tail past the block reads as zero) into QAREA bytes of LDS
@@ -239,7 +243,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr uint32_t QAREA = QB ? 1024u * QNL : 0u;
 
   // [key part][parity][K | V][64 x D], then (quantised pool) per wave: K codes, V codes
-  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT + KS * kRowWaves * QAREA];
+  // (8 row waves: the codes of its one tensor)
+  constexpr uint32_t QW = (RW == 8 ? 1u : 2u) * QAREA;       // code bytes per wave
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT + KS * RW * QW / 2];
 
   int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -258,15 +264,17 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const int cu_b = cascade ? 0 : min(max(cu[b], 0), total_q);
   const int C = cascade ? total_q : max(0, min(cu[b + 1], total_q) - cu_b);
   const int nrows = C * G;
-  const int v0 = tile * kBM;
+  const int v0 = tile * BM;
   if (v0 >= nrows) return;
   const int P0 = max(0, min(cascade ? cas.shared_len : plen[b], bt_stride * kBlock));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = uniform(tid >> 6);
   const int lr = lane & 31, hf = lane >> 5;
-  const int rw = w & (kRowWaves - 1);                       // row group
-  const int kh = KS == 1 ? 0 : w / kRowWaves;                // key part
+  const int rw = w & (RW - 1);                              // row group
+  const int kh = KS == 1 ? 0 : w / RW;                       // key part
+  // which tensors this wave stages: both (4 row waves), K or V (8 row waves)
+  const bool st_k = RW == 4 || w < 4, st_v = RW == 4 || w >= 4;
 
   // this lane's query row (virtual row v = i*G + g)
   const int vrow = v0 + 32 * rw + lr;
@@ -284,7 +292,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   }
   const bool wave_active = v0 + 32 * rw < nrows;
 
-  const int last_row = min(nrows, v0 + kBM) - 1;
+  const int last_row = min(nrows, v0 + BM) - 1;
   const int i_first = v0 / G;
   // cascade: each row (sequence) sees only the shared keys below its context length.
   // wg_lim is the smallest such limit over the work-group's rows; keys at or past the
@@ -390,7 +398,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // ld_offK/V[m]: the byte offset for a pool block (row pitch D*2); a source with another
   // pitch adds row * (pitch - D*2).  The row of instruction m is ld_row0 + m * 64/CPR
   // where CPR divides 64 (head dims 64, 128), else kept per instruction.
-  const int ld_blk = w & (kRowWaves - 1);
+  const int ld_blk = w & 3;
   constexpr bool kRowAffine = 64 % CPR == 0;
   uint32_t ld_offK[NLD], ld_offV[NLD], ld_rows[kRowAffine ? 1 : NLD];
 #pragma unroll
@@ -516,7 +524,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // into its code area (K codes, then V codes; no other wave reads them) and later widens
   // them into the 16-bit tile.  Lane L widens row L/4 of the block, 8-code chunks
   // (L%4)*NCQ .. +NCQ-1.
-  const uint32_t q_area = (uint32_t)(KS * 4 * HTB) + (uint32_t)w * 2u * QAREA;
+  const uint32_t q_area = (uint32_t)(KS * 4 * HTB) + (uint32_t)w * QW;
+  // LDS offset of the staged V codes within the wave's area
+  constexpr uint32_t QV = RW == 8 ? 0u : QAREA;
   constexpr int NCQ = D / 32;
   auto qload = [&](int li, bool is_v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(is_v ? tv_lo : tk_lo), li);
@@ -526,7 +536,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
         __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, nb, kBufDword3);
 #pragma unroll
     for (int i = 0; i < QNL; ++i)
-      buf_load16_lds(rs, 1024u * i + 16u * lane, lds + q_area + (is_v ? QAREA : 0u) + 1024u * i);
+      buf_load16_lds(rs, 1024u * i + 16u * lane, lds + q_area + (is_v ? QV : 0u) + 1024u * i);
   };
   // the V scale of this lane's row of the block (0 past its valid rows or for a missing
   // block: the buffer holds only the valid rows' scales)
@@ -545,7 +555,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     QCodes c;
     const char* src = lds + q_area + (uint32_t)((lane >> 2) * QROW + (lane & 3) * NCW * 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < (RW == 8 ? 1 : 2); ++h) {
+      // 8 row waves: the one staged tensor, in c.k
       uint32_t* d = h ? c.v : c.k;
       const char* p = src + (h ? QAREA : 0u);
       if constexpr (NCW % 4 == 0) {
@@ -709,40 +720,44 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // the first reference
   refill(0);
   if constexpr (QB == 0) {
-    issue_all(desc(0, false, kOffK0), false, Gen{});
-    issue_all(desc(0, true, kOffV0), true, Gen{});
-    issue_all(desc(1, false, kOffK1), false, Gen{});
+    if (st_k) issue_all(desc(0, false, kOffK0), false, Gen{});
+    if (st_v) issue_all(desc(0, true, kOffV0), true, Gen{});
+    if (st_k) issue_all(desc(1, false, kOffK1), false, Gen{});
   } else {
     // tiles 0 and 1 widened here, in two rounds through the one code area; the V codes
     // of tile 1 and the K codes of tile 2 stay staged for step 0
     const bool p0 = pre_bits & 1, p1 = (pre_bits >> 1) & 1, p2 = (pre_bits >> 2) & 1;
     if (p0) {
-      qload(0, false);
-      qload(0, true);
-      vs_cur = qscale(0);
+      if (st_k) qload(0, false);
+      if (st_v) {
+        qload(0, true);
+        vs_cur = qscale(0);
+      }
     } else {
-      issue_all(desc(0, false, kOffK0), false, Gen{});
-      issue_all(desc(0, true, kOffV0), true, Gen{});
+      if (st_k) issue_all(desc(0, false, kOffK0), false, Gen{});
+      if (st_v) issue_all(desc(0, true, kOffV0), true, Gen{});
     }
     __builtin_amdgcn_s_waitcnt(0);                  // this wave's own block
     if (p0) {
       const QCodes c = qread();
-      qwiden(IsK{}, c.k, kOffK0, 0.f);
-      qwiden(IsV{}, c.v, kOffV0, vs_cur);
+      if (st_k) qwiden(IsK{}, c.k, kOffK0, 0.f);
+      if (st_v) qwiden(IsV{}, RW == 8 ? c.k : c.v, kOffV0, vs_cur);
     }
     if (p1) {
-      qload(1, false);
-      qload(1, true);
-      vs_cur = qscale(1);
+      if (st_k) qload(1, false);
+      if (st_v) {
+        qload(1, true);
+        vs_cur = qscale(1);
+      }
     } else {
-      issue_all(desc(1, false, kOffK1), false, Gen{});
+      if (st_k) issue_all(desc(1, false, kOffK1), false, Gen{});
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (p1) {
+    if (p1 && st_k) {
       const QCodes c = qread();
       qwiden(IsK{}, c.k, kOffK1, 0.f);
     }
-    if (p2) qload(2, false);
+    if (p2 && st_k) qload(2, false);
   }
   f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
@@ -806,10 +821,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       const bool kq = decltype(pre_c)::value || ((pre_bits >> lk) & 1);
       const bool vq = decltype(pre_c)::value || ((pre_bits >> lv) & 1);
       const QCodes c = qread();
-      if (kq) qwiden(IsK{}, c.k, offK_ld, 0.f);
-      if (vq) qwiden(IsV{}, c.v, offV_ld, vs_cur);
-      if ((pre_bits >> (lk + 1)) & 1) qload(lk + 1, false);
-      if ((pre_bits >> (lv + 1)) & 1) {
+      if (kq && st_k) qwiden(IsK{}, c.k, offK_ld, 0.f);
+      if (vq && st_v) qwiden(IsV{}, RW == 8 ? c.k : c.v, offV_ld, vs_cur);
+      if (st_k && ((pre_bits >> (lk + 1)) & 1)) qload(lk + 1, false);
+      if (st_v && ((pre_bits >> (lv + 1)) & 1)) {
         qload(lv + 1, true);
         vs_cur = qscale(lv + 1);
       }
@@ -817,8 +832,8 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       v_direct = !vq;
     }
     if (!wave_active) {
-      if (k_direct) issue_all(dk, false, pre_c);
-      if (v_direct) issue_all(dv, true, pre_c);
+      if (k_direct && st_k) issue_all(dk, false, pre_c);
+      if (v_direct && st_v) issue_all(dv, true, pre_c);
       return;
     }
     // Hand-interleaved: each step of a phase is a scheduling region of its own, so
@@ -842,9 +857,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       // one load per step: bunched at the step start, the loads of all waves queue at
       // the memory pipeline and stall the issuing waves
       if (kk < NLD) {
-        if (k_direct) issue(dk, false, kk, pre_c);
+        if (k_direct && st_k) issue(dk, false, kk, pre_c);
       } else {
-        if (v_direct) issue(dv, true, kk - NLD, pre_c);
+        if (v_direct && st_v) issue(dv, true, kk - NLD, pre_c);
       }
       if (kk + 2 < NKK) {
         ka[kk + 2][0] = k_operand(offK_rd, kk + 2, 0);
@@ -969,7 +984,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // virtual row i*G, so each token is written exactly once; 16 bytes per thread and item.
   if (MODE == kModePrefill && wr.slots) {
     const int i_lo = (v0 + G - 1) / G;
-    const int i_hi = min(C, (v0 + kBM + G - 1) / G);
+    const int i_hi = min(C, (v0 + BM + G - 1) / G);
     const int n_items = max(0, i_hi - i_lo) * 2 * CPR;
     for (int it = (int)threadIdx.x; it < n_items; it += (int)blockDim.x) {
       const int tok = i_lo + it / (2 * CPR);
@@ -1029,7 +1044,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // key-part 1 waves publish (output, max, sum); key-part 0 waves combine and store.
   float* mbuf = reinterpret_cast<float*>(smem);
   constexpr int OPW = NDB * 16;                    // output floats per lane
-  static_assert(KS == 1 || (kRowWaves * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
+  static_assert(KS == 1 || (RW * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
   float* my = mbuf + rw * (OPW + 2) * 64;
   // a row that saw no key here (sum 0) takes a reference far below any other, so a merge
   // with another part of its keys gives it no weight
@@ -1072,7 +1087,7 @@ constexpr int kPlanBuckets = 32;
 
 __global__ void __launch_bounds__(kPlanThreads)
 prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ plen, int batch,
-                    int G, int total_q, int bt_stride, int max_tiles, int padded, int real,
+                    int G, int total_q, int bt_stride, int max_tiles, int bm, int padded, int real,
                     int32_t* __restrict__ order) {
   __shared__ uint64_t key[kPlanMax];
   __shared__ int s_max, s_min;
@@ -1094,8 +1109,8 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
     const int cu_b = min(max(cu[b], 0), total_q);
     const int C = max(0, min(cu[b + 1], total_q) - cu_b);
     const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
-    const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * kBM;
-    const int64_t cost = v0 < nrows ? min(P0 + (min(nrows, v0 + kBM) - 1) / G + 1, (int64_t)0x3fffffff) : 0;
+    const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * bm;
+    const int64_t cost = v0 < nrows ? min(P0 + (min(nrows, v0 + bm) - 1) / G + 1, (int64_t)0x3fffffff) : 0;
     key[i] = (uint64_t)cost;
     atomicMax(&s_max, (int)cost);
     if (cost > 0) atomicMin(&s_min, (int)cost);
@@ -1159,7 +1174,17 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   const PfWrite wr{slots, (uint16_t*)p.k, (uint16_t*)p.v};
   const int G = hq / p.num_kv_heads;
   const long long rows = (long long)max_q_len * G;
-  const int max_tiles = (int)((rows + kBM - 1) / kBM);
+  const int cus = device_cu_count();
+  // Quantised pool at head dim 96 on a grid of at least four rounds of one 256-row
+  // work-group per CU: 8 row waves per work-group, each staging and widening one tensor of
+  // its block of every tile, so a widened tile serves twice the rows.  Measured against
+  // the 4-row-wave form: ragged mix at head dim 96 (fp16) 0.96x; at head dim 64 (bf16)
+  // 1.02-1.03x; long_prefix (head dim 128, 2.5 rounds) 1.02x.  The 16-bit pool keeps 4 row
+  // waves and two independent work-groups per CU everywhere (8 row waves: 1.05-1.06x).
+  const long long real8 = (long long)batch * p.num_kv_heads * ((rows + 255) / 256);
+  const bool rw8 = MODE == kModePrefill && QB != 0 && D == 96 && real8 >= 4LL * cus;
+  const int bm = rw8 ? 256 : kBM;
+  const int max_tiles = (int)((rows + bm - 1) / bm);
   const long long real = (long long)batch * p.num_kv_heads * cas.nks * max_tiles;
   if (real == 0) return hipSuccess;
   const long long padded = (real + kNumXcd - 1) / kNumXcd * kNumXcd;
@@ -1167,15 +1192,25 @@ static hipError_t launch_prefill_t(const kvb_pool& p, const void* q, const void*
   const float c = fmaxf(scale * 1.4426950408889634f, 1e-30f);
   // Up to two work-groups per CU fit: with fewer work-groups than 2 x CUs the keys are
   // split inside each work-group instead, so every SIMD still runs two waves.
-  const bool split = real < 2LL * device_cu_count();
+  const bool split = !rw8 && real < 2LL * cus;
   // a plan pays off only on a grid of several rounds
   const int32_t* order = nullptr;
   if (MODE == kModePrefill && plan_ws && !split && padded / kNumXcd <= kPlanMax) {
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(kNumXcd), dim3(kPlanThreads), 0, s, cu, plen,
-                       batch, G, total_q, bt_stride, max_tiles, (int)padded, (int)real, plan_ws);
+                       batch, G, total_q, bt_stride, max_tiles, bm, (int)padded, (int)real, plan_ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     order = plan_ws;
+  }
+  if constexpr (MODE == kModePrefill && QB != 0 && D == 96) {
+    if (rw8) {
+      hipLaunchKernelGGL((prefill_kernel<T, D, 1, MODE, QB, 8>), dim3((unsigned)padded), dim3(512), 0, s,
+                         (const uint16_t*)p.k, (const uint16_t*)p.v, p.block_stride, p.num_blocks,
+                         (const uint16_t*)q, (const uint16_t*)kn, (const uint16_t*)vn, (uint16_t*)out,
+                         cu, plen, bt, bt_stride, batch, hq, p.num_kv_heads, total_q, max_tiles, c,
+                         (int)padded, (int)real, order, cas, wr, qz);
+      return hipGetLastError();
+    }
   }
   if (split)
     hipLaunchKernelGGL((prefill_kernel<T, D, 2, MODE, QB>), dim3((unsigned)padded), dim3(512), 0, s,

@@ -214,18 +214,21 @@ def test_prefill_dispatch_plan_is_a_stable_longest_first_permutation(batch, G, c
     kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale, mq, mp,
                       workspace=ws)
     torch.cuda.synchronize()
-    max_tiles = (mq * G + 127) // 128
+    # 128-row work-groups (the 16-bit pool's form)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bm = 128
+    max_tiles = (mq * G + bm - 1) // bm
     real = batch * hkv * max_tiles
     padded = (real + 7) // 8 * 8
     per = padded // 8
-    assert per <= 4096 and real >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert per <= 4096 and real >= 2 * cus
     order = ws[:real].cpu().numpy()
     cu = np.asarray(w.cu_q_lens, dtype=np.int64)
 
     def cost(lid):
         tile, b = lid % max_tiles, (lid // max_tiles) % batch
-        nrows, v0 = int(cu[b + 1] - cu[b]) * G, tile * 128
-        return int(w.prefix_lens[b]) + (min(nrows, v0 + 128) - 1) // G + 1 if v0 < nrows else 0
+        nrows, v0 = int(cu[b + 1] - cu[b]) * G, tile * bm
+        return int(w.prefix_lens[b]) + (min(nrows, v0 + bm) - 1) // G + 1 if v0 < nrows else 0
 
     for lo in range(0, real, per):
         n = min(per, real - lo)
