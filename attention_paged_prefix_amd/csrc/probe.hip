@@ -158,4 +158,12 @@ double kvb_probe_mfma_flops(int iters, int blocks) {
   return (double)blocks * 4.0 * iters * kMfmaChains * 32768.0;
 }
 
+// Peak engine clock of the current device in kHz (the driver's figure), or -1.
+int kvb_probe_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev) != hipSuccess) return -1;
+  return khz;
+}
+
 }  // extern "C"

@@ -303,6 +303,8 @@ class Probe:
                                          ctypes.c_int, ctypes.c_void_p]
         lib.kvb_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
         lib.kvb_probe_mfma_flops.restype = ctypes.c_double
+        lib.kvb_probe_clock_khz.argtypes = []
+        lib.kvb_probe_clock_khz.restype = ctypes.c_int
         self.lib = lib
         self.torch = torch
         self.buf = torch.ones(FLUSH_BYTES // 2, dtype=torch.int16, device="cuda:0")
@@ -351,14 +353,21 @@ class Probe:
         settle(torch, rd, min(settle_ms, 100))
         rms = time_each(torch, rd, 10)
         del big
-        return {"mfma_bf16_tflops": fl / (np.median(ms) * 1e-3) / 1e12,
+        tflops = fl / (np.median(ms) * 1e-3) / 1e12
+        khz = int(self.lib.kvb_probe_clock_khz())
+        return {"mfma_bf16_tflops": tflops,
                 "mfma_probe": f"{blocks} work-groups x 4 waves x {iters} x 4 independent "
                               f"v_mfma_f32_32x32x16_bf16 on random N(0,1) bf16 operands, median "
                               f"of 10 launches of {np.median(ms):.3f} ms",
                 "hbm_read_gbps": 4 * FLUSH_BYTES / (np.median(rms) * 1e-3) / 1e9,
                 "hbm_probe": f"4 GiB read with 16-byte loads (32 work-groups per CU), median of "
                              f"10 launches of {np.median(rms):.3f} ms",
-                "compute_units": self.cus}
+                "compute_units": self.cus,
+                # the driver's peak engine clock, and the clock at which the probe's MFMA rate
+                # would be the full dense rate (4096 bf16 flop per clock per CU)
+                "clock_mhz_peak": khz / 1000.0 if khz > 0 else None,
+                "nominal_mfma_tflops_at_peak_clock": self.cus * 4096 * khz * 1e3 / 1e12 if khz > 0 else None,
+                "mfma_probe_effective_clock_mhz": tflops * 1e12 / (self.cus * 4096) / 1e6}
 
 
 def time_each(torch, fn, n: int, before=None):
@@ -692,6 +701,7 @@ def main(argv=None):
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"]["gpu_prefill_speedup"] = res["roofline"]["achieved"] / res["cpu_baseline"]["value"]
 
     print(json.dumps(res))
     return 0
