@@ -485,7 +485,7 @@ def main(argv=None):
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed back-to-back runs before timing so clocks reach steady state")
     ap.add_argument("--config", default="ragged_d96", choices=sorted(CONFIG_NAMES))
-    ap.add_argument("--other-configs", default="shared_prompt,long_prefix,ragged_d64",
+    ap.add_argument("--other-configs", default="shared_prompt,long_prefix,ragged_d64,tiny",
                     help="comma-separated workloads whose prefill is also timed ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-blocks", type=int, default=0, help="decode split size (0 = auto)")
@@ -675,6 +675,8 @@ def main(argv=None):
         e["write_kv"] = {"tokens": wo.total_q, "ms": ms,
                          "gbps": write_kv_bytes(wo.total_q, wo) / (ms * 1e-3) / 1e9}
         e["workload"] = CONFIG_NAMES[name]
+        if name == "tiny":
+            e["note"] = "latency-bound correctness case (648 pairs): its time, not a roofline fraction"
         others[name] = e
         progress(f"{name} prefill timed: {e['tflops_cold_mean']:.0f} TFLOP/s cold")
         del uo
