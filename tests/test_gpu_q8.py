@@ -405,3 +405,41 @@ def test_write_then_decode_q4_end_to_end():
     assert np.array_equal(pool.k.cpu().numpy(), quant.pack_nibbles(kc))
     ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, "fp16")
     assert u.max_err(got, ref, "fp16") <= u.TOL["fp16"]
+
+
+@pytest.mark.parametrize("bits,dt", [(8, "fp16"), (4, "fp16"), (8, "bf16")])
+def test_prefill_quant_eight_row_waves_matches_oracle(bits, dt):
+    """Head dim 96 through a quantised pool on a grid of at least four rounds of 256-row
+    work-groups, the form with 8 row waves (K blocks staged by waves 0-3, V blocks by 4-7),
+    every output row against the oracle: prefixes of 0, 1, 63, 64 and 65 tokens, one past
+    64 tiles (table refill with codes staged a tile ahead), chunks of 1 to 200 tokens."""
+    import attention_paged_prefix_amd as kvb
+    from oracle import quant
+    u = _util()
+    rng = np.random.default_rng(860 + bits)
+    batch, hq, hkv, d = 32, 32, 8, 96
+    P = [0, 1, 63, 64, 65, 4500] + [int(x) for x in rng.integers(0, 3000, size=batch - 6)]
+    C = [200, 1, 17, 64, 129, 150] + [int(x) for x in rng.integers(1, 201, size=batch - 6)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert batch * hkv * ((max(C) * (hq // hkv) + 255) // 256) >= 4 * cus
+    w = make_custom(870 + bits, dt, hq, hkv, d, P, C, share="pairs", poison=False)
+    slots = _prefix_slots(w)
+    if bits == 8:
+        kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
+        ks = channel_scales(oracle_f32(kt, dt))
+        kc, vc, vs = _poisoned(w.k_pool.shape[0], hkv, d)
+        kc, vc, vs = quant.write_kv_q8(kc, vc, vs, ks, kt, vt, slots, dt)
+        pool = _pool_q8(kc, vc, vs, ks)
+        fn = kvb.paged_prefill_q8
+    else:
+        kc, vc, vs, ks, _, _ = _oracle_q4_pool(w, slots)
+        pool = _pool_q4(kc, vc, vs, ks)
+        fn = kvb.paged_prefill_q4
+    got = u.to_bits(fn(pool, u.to_dev(w.q, dt), u.to_dev(w.k_new, dt), u.to_dev(w.v_new, dt),
+                       u.idev(w.cu_q_lens), u.idev(w.prefix_lens), u.idev(w.block_tables), w.scale,
+                       int(w.q_lens.max()), int(w.prefix_lens.max())))
+    torch.cuda.synchronize()
+    ref = quant.paged_prefill_q8(kc, vc, vs, ks, w.q, w.k_new, w.v_new, w.cu_q_lens, w.prefix_lens,
+                                 w.block_tables, hq, w.scale, dt)
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
