@@ -1076,10 +1076,12 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 // Longest-first dispatch plan.  The dispatcher starts work-groups in grid order, so on a
 // grid of several rounds the last work-groups to start set the tail.  One work-group per
 // XCD range (the logical ids one XCD runs) computes every item's key count (prefix plus
-// the causal part of its last row; 0 for tiles past the chunk), sorts the range by it in
-// 32 buckets relative to the range's largest count, largest first, and writes the item
-// for each position (table order when every non-empty item is within 2x of the largest).  Within a bucket items keep table order (tiles of one sequence and
-// KV head together, so they share its K/V through L2), and the plan is deterministic.
+// the causal part of its last row; 0 for tiles past the chunk), orders the range by it in
+// 32 buckets relative to the range's largest count (a stable counting sort), largest
+// first, and writes the item for each position (table order when every non-empty item
+// is within 2x of the largest).  Within a bucket items keep table order (tiles of one
+// sequence and KV head together, so they share its K/V through L2), and the plan is
+// deterministic.
 // Items never leave their XCD range, so each XCD keeps its KV heads in L2.
 constexpr int kPlanThreads = 256;
 constexpr int kPlanMax = 4096;          // items per XCD range sorted in LDS
@@ -1089,20 +1091,19 @@ __global__ void __launch_bounds__(kPlanThreads)
 prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ plen, int batch,
                     int G, int total_q, int bt_stride, int max_tiles, int bm, int padded, int real,
                     int32_t* __restrict__ order) {
-  __shared__ uint64_t key[kPlanMax];
-  __shared__ int s_max, s_min;
+  constexpr int NB = kPlanBuckets + 1;               // cost buckets, then the empty items
+  constexpr int NW = kPlanThreads / 64;
+  __shared__ int cost_s[kPlanMax];
+  __shared__ int cnt[NB * kPlanThreads];             // [bucket][thread]: counts, then offsets
+  __shared__ int s_wmax[NW], s_wmin[NW], s_wsum[NW];
   const int per = padded / kNumXcd;
   const int lo = blockIdx.x * per;
   const int n = min(per, real - lo);
   if (n <= 0) return;
-  int N = 1;
-  while (N < n) N <<= 1;
-  if (threadIdx.x == 0) {
-    s_max = 0;
-    s_min = 0x7fffffff;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kPlanThreads) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // item costs: prefix plus the causal keys of the tile's last row (0: an empty tile)
+  int mx = 0, mn = 0x7fffffff;
+  for (int i = t; i < n; i += kPlanThreads) {
     const int lid = lo + i;
     const int tile = lid % max_tiles;
     const int b = (lid / max_tiles) % batch;
@@ -1110,49 +1111,70 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
     const int C = max(0, min(cu[b + 1], total_q) - cu_b);
     const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
     const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * bm;
-    const int64_t cost = v0 < nrows ? min(P0 + (min(nrows, v0 + bm) - 1) / G + 1, (int64_t)0x3fffffff) : 0;
-    key[i] = (uint64_t)cost;
-    atomicMax(&s_max, (int)cost);
-    if (cost > 0) atomicMin(&s_min, (int)cost);
+    const int cost = (int)(v0 < nrows ? min(P0 + (min(nrows, v0 + bm) - 1) / G + 1, (int64_t)0x3fffffff) : 0);
+    cost_s[i] = cost;
+    mx = max(mx, cost);
+    if (cost > 0) mn = min(mn, cost);
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    mx = max(mx, __shfl_xor(mx, sh, 64));
+    mn = min(mn, __shfl_xor(mn, sh, 64));
+  }
+  if (lane == 0) {
+    s_wmax[wv] = mx;
+    s_wmin[wv] = mn;
   }
   __syncthreads();
-  const int64_t cmax = s_max, cmin = s_min;
-  if (2 * cmin > cmax) {
+  int cmax = s_wmax[0], cmin = s_wmin[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) {
+    cmax = max(cmax, s_wmax[k]);
+    cmin = min(cmin, s_wmin[k]);
+  }
+  if (2 * (int64_t)cmin > cmax) {
     // every tile within 2x of the largest: nothing to balance, and table order keeps
     // the tiles of one sequence and KV head together
-    for (int i = threadIdx.x; i < n; i += kPlanThreads) order[lo + i] = lo + i;
+    for (int i = t; i < n; i += kPlanThreads) order[lo + i] = lo + i;
     return;
   }
-  for (int i = threadIdx.x; i < N; i += kPlanThreads) {
-    uint64_t k = ~0ull;                 // padding sorts last
-    if (i < n) {
-      const int64_t cost = (int64_t)key[i];
-      // empty tiles after every bucket; bucket kPlanBuckets - 1 holds the largest counts
-      const int64_t rank = cost > 0 ? kPlanBuckets - 1 - min((int64_t)kPlanBuckets - 1, cost * kPlanBuckets / (cmax + 1))
-                                    : kPlanBuckets;
-      k = ((uint64_t)rank << 32) | (uint32_t)(lo + i);
-    }
-    key[i] = k;
+  // bucket kPlanBuckets - 1 holds the largest counts; empty tiles after every bucket
+  auto bucket = [&](int c) {
+    return c > 0 ? kPlanBuckets - 1 - (int)min((int64_t)kPlanBuckets - 1, (int64_t)c * kPlanBuckets / ((int64_t)cmax + 1))
+                 : kPlanBuckets;
+  };
+  // Stable counting sort by bucket: thread t takes the contiguous items [i0, i1), counts
+  // them per bucket in its own column, the counts are scanned in (bucket, thread) order,
+  // and each thread places its items in order from its column's offsets.
+  const int K = (n + kPlanThreads - 1) / kPlanThreads;
+  const int i0 = min(n, t * K), i1 = min(n, i0 + K);
+  for (int b = 0; b < NB; ++b) cnt[b * kPlanThreads + t] = 0;
+  for (int i = i0; i < i1; ++i) ++cnt[bucket(cost_s[i]) * kPlanThreads + t];
+  __syncthreads();
+  // exclusive scan of the NB * kPlanThreads counts (bucket-major): thread t owns the
+  // consecutive entries [NB t, NB t + NB)
+  int run = 0;
+  for (int k = 0; k < NB; ++k) run += cnt[NB * t + k];
+  int incl = run;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int y = __shfl_up(incl, sh, 64);
+    incl += lane >= sh ? y : 0;
+  }
+  if (lane == 63) s_wsum[wv] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int k = 0; k < wv; ++k) base += s_wsum[k];
+  for (int k = 0; k < NB; ++k) {
+    const int c = cnt[NB * t + k];
+    cnt[NB * t + k] = base;
+    base += c;
   }
   __syncthreads();
-  // Bitonic sort.  A wave's pairs i cover the same 128 consecutive elements (per 256
-  // pairs) in every pass with stride <= 64, so such a pass depends only on the same wave's
-  // previous pass (LDS operations of one wave complete in order) unless that pass had a
-  // larger stride: a wave fence suffices there, and only passes with a larger stride, or
-  // right after one, wait for the whole work-group.
-  for (int size = 2; size <= N; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride > 64 || (stride == 64 && size >= 256)) __syncthreads();
-      for (int i = threadIdx.x; i < N / 2; i += kPlanThreads) {
-        const int a = 2 * i - (i & (stride - 1));      // pair (a, a + stride), bit `stride` of a clear
-        const uint64_t x = key[a], y = key[a + stride];
-        if ((x > y) == ((a & size) == 0)) { key[a] = y; key[a + stride] = x; }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += kPlanThreads) order[lo + i] = (int32_t)(uint32_t)key[i];
+  for (int i = i0; i < i1; ++i) {
+    const int pos = cnt[bucket(cost_s[i]) * kPlanThreads + t]++;
+    order[lo + pos] = lo + i;
+  }
 }
 
 int64_t prefill_plan_bytes(int batch, int hq, int total_q) {
