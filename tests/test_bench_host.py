@@ -47,3 +47,21 @@ def test_traffic_only_while_sources_match(tmp_path, monkeypatch):
     assert bench.read_traffic("missing") is None
     src.write_text("kernel v2\n")                                  # kernel changed since
     assert bench.read_traffic("kern_work") is None
+
+
+def test_counters_only_while_sources_match(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    h = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    (prof / "kern_work.sq.txt").write_text(
+        "# command (A): rocprofv3 --pmc MfmaUtil ...\n"
+        f"source_files: k.hip\nsource_sha256_16: {h}\nMfmaUtil_per_dispatch: 55.5\n"
+        "mfma_util_percent: 55.50\nvalu_per_mfma: 5.852\nl2_hit_rate: 0.8453\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.read_counters("kern_work") == {"mfma_util_percent": 55.5, "valu_per_mfma": 5.852,
+                                                "l2_hit_rate": 0.8453}
+    assert bench.read_counters("missing") is None
+    src.write_text("kernel v2\n")                                  # kernel changed since
+    assert bench.read_counters("kern_work") is None
