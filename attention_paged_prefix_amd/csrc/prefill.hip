@@ -242,10 +242,15 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   constexpr int QNL = (kBlock * QROW + 1023) / 1024;
   constexpr uint32_t QAREA = QB ? 1024u * QNL : 0u;
 
-  // [key part][parity][K | V][64 x D], then (quantised pool) per wave: K codes, V codes
+  // Tile buffers per key part: NBUF for K and NBUF for V.  Two (tiles loaded one step
+  // ahead) in general; three (two steps ahead, so a step's loads stay in flight across its
+  // barrier) for the 16-bit ordinary prefill at head dims 64 and 96, where they fit with
+  // two work-groups per CU.
+  constexpr int NBUF = (MODE == kModePrefill && QB == 0 && RW == 4 && D <= 96) ? 3 : 2;
+  // [key part][K | V buffers][64 x D], then (quantised pool) per wave: K codes, V codes
   // (8 row waves: the codes of its one tensor)
   constexpr uint32_t QW = (RW == 8 ? 1u : 2u) * QAREA;       // code bytes per wave
-  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 4 * HT + KS * RW * QW / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[KS * 2 * NBUF * HT + KS * RW * QW / 2];
 
   int lid = xcd_logical_id(blockIdx.x, padded);
   if (lid >= real) return;
@@ -384,11 +389,15 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // m_run: the row's reference (exp2 domain); l_run: this lane's half of the row sum
   float m_run = 0.f, l_run = 0.f;
 
-  // ---- LDS: key part kh owns 4 tile buffers (bytes): K parity 0, V parity 0, K parity 1,
-  // V parity 1.  All read and write addresses are a per-lane register plus a constant.
+  // ---- LDS: key part kh owns 2*NBUF tile buffers (bytes): K0 V0 K1 V1 with two, K0 K1 K2
+  // V0 V1 V2 with three.  All read and write addresses are a per-lane register plus a
+  // constant.
   char* const lds = reinterpret_cast<char*>(smem);
-  const uint32_t part_base = (uint32_t)(kh * 4 * HTB);
-  constexpr uint32_t kOffK0 = 0, kOffV0 = HTB, kOffK1 = 2 * HTB, kOffV1 = 3 * HTB;
+  const uint32_t part_base = (uint32_t)(kh * 2 * NBUF * HTB);
+  // byte offsets of K buffer i and V buffer i within the key part (two buffers: K0 V0 K1 V1)
+  constexpr auto kOffK = [](int i) -> uint32_t { return (uint32_t)((NBUF == 2 ? 2 * i : i) * HTB); };
+  constexpr auto kOffV = [](int i) -> uint32_t { return (uint32_t)((NBUF == 2 ? 2 * i + 1 : NBUF + i) * HTB); };
+  constexpr uint32_t kOffK0 = kOffK(0), kOffV0 = kOffV(0), kOffK1 = kOffK(1);
 
   // ---- loader: the 4 waves of key part kh stage that part's tiles; wave (w & 3) loads
   // block (w & 3) of a tile.  Instruction m of a block fills LDS chunks 64m..64m+63 of
@@ -524,7 +533,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // into its code area (K codes, then V codes; no other wave reads them) and later widens
   // them into the 16-bit tile.  Lane L widens row L/4 of the block, 8-code chunks
   // (L%4)*NCQ .. +NCQ-1.
-  const uint32_t q_area = (uint32_t)(KS * 4 * HTB) + (uint32_t)w * QW;
+  const uint32_t q_area = (uint32_t)(KS * 2 * NBUF * HTB) + (uint32_t)w * QW;
   // LDS offset of the staged V codes within the wave's area
   constexpr uint32_t QV = RW == 8 ? 0u : QAREA;
   constexpr int NCQ = D / 32;
@@ -762,6 +771,11 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   f32x16 s_cur[2];
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (NBUF == 3) {
+    // two steps ahead: K of tile 2 and V of tile 1 fly while the first scores are taken
+    issue_all(desc(2, false, kOffK(2)), false, Gen{});
+    issue_all(desc(1, true, kOffV(1)), true, Gen{});
+  }
   if (wave_active) {
     s_cur[0] = f32x16{};
     s_cur[1] = f32x16{};
@@ -790,27 +804,29 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   }
   __syncthreads();                                  // K buffer 0 is reloaded in step 0
 
-  // ---- step j: loads K of tile j+2 into K buffer (j&1) and V of tile j+1 into V buffer
-  // ((j+1)&1); S MFMAs of tile j+1 from K buffer ((j+1)&1); PV MFMAs of tile j from V
-  // buffer (j&1).  The buffer parity is a compile-time constant (the loop is unrolled by
-  // two), so every LDS address is a register plus an immediate.
+  // ---- step j: loads K of tile j+NBUF and V of tile j+NBUF-1; S MFMAs of tile j+1, PV
+  // MFMAs of tile j.  Tile t sits in K buffer t mod NBUF and V buffer t mod NBUF.  The
+  // buffer index is a compile-time constant (the loop is unrolled by NBUF), so every LDS
+  // address is a register plus an immediate.
   auto step = [&](int j, auto par_c, auto pre_c) {
-    constexpr int PAR = decltype(par_c)::value;
-    constexpr uint32_t offK_ld = PAR ? kOffK1 : kOffK0, offV_ld = PAR ? kOffV0 : kOffV1;
-    constexpr uint32_t offK_rd = PAR ? kOffK0 : kOffK1, offV_rd = PAR ? kOffV1 : kOffV0;
+    constexpr int PAR = decltype(par_c)::value;                 // j mod NBUF
+    // K of tile j+NBUF into K buffer PAR (it held tile j, read in step j-1), V of tile
+    // j+NBUF-1 into the V buffer of tile j-1; S of tile j+1 and PV of tile j read theirs
+    constexpr uint32_t offK_ld = kOffK(PAR), offV_ld = kOffV((PAR + NBUF - 1) % NBUF);
+    constexpr uint32_t offK_rd = kOffK((PAR + 1) % NBUF), offV_rd = kOffV(PAR);
     // next 64 tiles of the sequence (a quantised pool stages codes one tile further)
-    if (j + 2 + (QB ? 1 : 0) - u0 >= 64) {
+    if (j + NBUF + (QB ? 1 : 0) - u0 >= 64) {
       keep_branch();
       u0 = j + 1;
       refill(u0);
     }
-    const int lk = j + 2 - u0, lv = j + 1 - u0;
+    const int lk = j + NBUF - u0, lv = j + NBUF - 1 - u0;
     const LdDesc dk = desc(lk, false, offK_ld);
     const LdDesc dv = desc(lv, true, offV_ld);
-    const bool need_mask = (mask_bits >> lv) & 1;
-    // K of tile j+2 and V of tile j+1: loaded straight into LDS, or (prefix tiles of a
-    // quantised pool) widened from the codes staged in the previous step, whose place
-    // then takes the codes of K j+3 and V j+2
+    const bool need_mask = (mask_bits >> (j + 1 - u0)) & 1;
+    // K of tile j+NBUF and V of tile j+NBUF-1: loaded straight into LDS, or (prefix tiles
+    // of a quantised pool, two buffers) widened from the codes staged in the previous
+    // step, whose place then takes the codes of K j+3 and V j+2
     bool k_direct = true, v_direct = true;
     if constexpr (QB != 0) {
       if (!decltype(pre_c)::value && j + 1 == n_pre_part) {   // tile j+1: the chunk's first own tile
@@ -933,37 +949,84 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 #pragma unroll
     for (int h = 0; h < 2; ++h) s_cur[h] = s_nxt[h];
   };
+  // End of a step: this wave's loads for the next step have landed (two buffers: all of
+  // them; three: all but the NKK issued in this step, which the step after next reads),
+  // then the work-group's barrier.
+  // (With three buffers the barrier is the bare instruction: __syncthreads() fences
+  // work-group memory, which waits for every outstanding load, the in-flight LDS-direct
+  // ones included.  LDS reads of this step complete first, and the empty asm statements
+  // keep the compiler from moving memory operations across.)
   auto sync = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);                  // this wave's LDS-direct loads have landed
-    __syncthreads();
+    if constexpr (NBUF == 2) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_s_waitcnt((NKK & 15) | ((NKK >> 4) << 14) | (7 << 4));   // vmcnt(NKK) lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
-  // Steps j, j+1 whose loads (K of tile j+3 at the latest) are prefix tiles of this key
+  using Par2 = std::integral_constant<int, 2>;
+  // Steps whose loads (K of tile j + 2 NBUF - 1 at the latest) are prefix tiles of this key
   // part take the precomputed offsets; the chunk's own tiles and the tail the general
   // form.  Every step ends in one barrier in both loops, so the key parts may switch
-  // loops at different steps.
+  // loops at different steps.  The loops are unrolled by NBUF, so the buffer of every step
+  // is a compile-time constant.
   int j = 0;
-  for (; j + 3 < n_pre_part && j + 2 < nstage; j += 2) {
-    step(j, Par0{}, Pre{});
-    sync();
-    step(j + 1, Par1{}, Pre{});
-    sync();
+  if constexpr (NBUF == 2) {
+    for (; j + 3 < n_pre_part && j + 2 < nstage; j += 2) {
+      step(j, Par0{}, Pre{});
+      sync();
+      step(j + 1, Par1{}, Pre{});
+      sync();
+    }
+    for (; j + 2 < nstage; j += 2) {
+      step(j, Par0{}, Gen{});
+      sync();
+      step(j + 1, Par1{}, Gen{});
+      sync();
+    }
+    if (j + 1 < nstage) {
+      step(j, Par0{}, Gen{});
+      sync();
+      ++j;
+    }
+  } else {
+    for (; j + 5 < n_pre_part && j + 3 < nstage; j += 3) {
+      step(j, Par0{}, Pre{});
+      sync();
+      step(j + 1, Par1{}, Pre{});
+      sync();
+      step(j + 2, Par2{}, Pre{});
+      sync();
+    }
+    for (; j + 3 < nstage; j += 3) {
+      step(j, Par0{}, Gen{});
+      sync();
+      step(j + 1, Par1{}, Gen{});
+      sync();
+      step(j + 2, Par2{}, Gen{});
+      sync();
+    }
+    if (j + 1 < nstage) {
+      step(j, Par0{}, Gen{});
+      sync();
+      ++j;
+    }
+    if (j + 1 < nstage) {
+      step(j, Par1{}, Gen{});
+      sync();
+      ++j;
+    }
+    // the last steps' loads (past the end, or not read again) land before LDS is reused
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  for (; j + 2 < nstage; j += 2) {
-    step(j, Par0{}, Gen{});
-    sync();
-    step(j + 1, Par1{}, Gen{});
-    sync();
-  }
-  if (j + 1 < nstage) {
-    step(j, Par0{}, Gen{});
-    sync();
-    ++j;
-  }
-  // last tile: probabilities and PV (V buffer parity of the last step)
+  // last tile: probabilities and PV (V buffer of the last step)
   auto last = [&](auto par_c) {
-    constexpr uint32_t off = decltype(par_c)::value ? kOffV1 : kOffV0;
+    constexpr uint32_t off = kOffV(decltype(par_c)::value);
     u32x4 pw[4];
     float ls = probs(s_cur, pw);
     if (__any(!(ls <= kPfSumLimit))) {
@@ -976,8 +1039,10 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       o[i >> 2] = T::mfma32(v_operand(off, i >> 2, i & 3), __builtin_bit_cast(s16x8, pw[i & 3]), o[i >> 2]);
   };
   if (wave_active) {
-    if (j & 1) last(std::integral_constant<int, 1>{});
-    else last(std::integral_constant<int, 0>{});
+    const int par = j % NBUF;
+    if (par == 0) last(Par0{});
+    else if (NBUF == 2 || par == 1) last(Par1{});
+    else last(Par2{});
   }
 
   // Fused slot scatter: token i of the chunk is written by the work-group holding its first
@@ -1044,7 +1109,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   // key-part 1 waves publish (output, max, sum); key-part 0 waves combine and store.
   float* mbuf = reinterpret_cast<float*>(smem);
   constexpr int OPW = NDB * 16;                    // output floats per lane
-  static_assert(KS == 1 || (RW * (OPW + 2) * 64) * 4 <= KS * 4 * HT * 2, "merge buffer fits");
+  static_assert(KS == 1 || (RW * (OPW + 2) * 64) * 4 <= KS * 2 * NBUF * HT * 2, "merge buffer fits");
   float* my = mbuf + rw * (OPW + 2) * 64;
   // a row that saw no key here (sum 0) takes a reference far below any other, so a merge
   // with another part of its keys gives it no weight
