@@ -136,6 +136,35 @@ def test_prefill_large_grid_matches_oracle(case):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+# 16-bit pools at head dims 64 and 96 stage K/V two tiles ahead through three buffers per
+# tensor: key-tile counts per wave in every residue mod 3, around the refill of the
+# per-wave tile descriptors (every 64 tiles), in the small-grid form (two key parts per
+# work-group) and the large-grid form (one).
+THREE_BUFFER_CASES = [
+    (221, "fp16", 32, 8, 96, [8200, 8263, 4097, 4160], [1, 63, 64, 130], "none", False),
+    (222, "bf16", 16, 4, 64, [8190, 8255, 4031, 3968, 130, 191], [2, 65, 1, 127, 64, 3], "pairs", False),
+    (223, "fp16", 32, 8, 96, [4000, 4033, 4095, 4160], [600, 540, 513, 700], "none", True),
+    (224, "bf16", 32, 8, 64, [4031, 4096, 4097, 4223], [700, 650, 520, 600], "pairs", True),
+]
+
+
+@pytest.mark.parametrize("case", THREE_BUFFER_CASES, ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_large{int(c[8])}")
+def test_prefill_three_buffer_pipeline_matches_oracle(case):
+    u = _util()
+    seed, dt, hq, hkv, d, P, C, share, large = case
+    G = hq // hkv
+    groups = len(P) * hkv * ((max(C) * G + 127) // 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert (groups >= 2 * cus) == large
+    w = make_custom(seed, dt, hq, hkv, d, P, C, share=share, poison=True)
+    got = u.to_bits(u.Dev(w).prefill())
+    ref = u.oracle_prefill(w)
+    import oracle
+    assert np.isfinite(oracle.decode_bits(got, dt)).all()
+    err = u.max_err(got, ref, dt)
+    assert err <= u.TOL[dt], f"max abs err {err}"
+
+
 @pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:2],
                          ids=lambda c: f"seed{c[0]}_{c[1]}_d{c[4]}_G{c[2]//c[3]}")
 def test_prefill_write_equals_prefill_and_write_kv(case):
