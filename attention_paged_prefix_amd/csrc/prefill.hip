@@ -1140,13 +1140,14 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
 
 // Longest-first dispatch plan.  The dispatcher starts work-groups in grid order, so on a
 // grid of several rounds the last work-groups to start set the tail.  One work-group per
-// XCD range (the logical ids one XCD runs) computes every item's key count (prefix plus
-// the causal part of its last row; 0 for tiles past the chunk), orders the range by it in
-// 32 buckets relative to the range's largest count (a stable counting sort), largest
-// first, and writes the item for each position (table order when every non-empty item
-// is within 2x of the largest).  Within a bucket items keep table order (tiles of one
-// sequence and KV head together, so they share its K/V through L2), and the plan is
-// deterministic.
+// XCD range (the logical ids one XCD runs) gives every item the key count of its
+// sequence's last row (prefix plus chunk; 0 for tiles past the chunk), orders the range
+// by it in 32 buckets relative to the range's largest count (a stable counting sort),
+// largest first, and writes the item for each position (table order when every
+// non-empty item is within 2x of the largest).  All row tiles of one (sequence, KV head)
+// share that key, so they stay together in table order and stream its K/V through L2 at
+// about the same time (keyed by each tile's own last row, the tiles of a long chunk fell
+// into two buckets and re-read the prefix from HBM later); the plan is deterministic.
 // Items never leave their XCD range, so each XCD keeps its KV heads in L2.
 constexpr int kPlanThreads = 256;
 constexpr int kPlanMax = 4096;          // items per XCD range sorted in LDS
@@ -1166,7 +1167,7 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
   const int n = min(per, real - lo);
   if (n <= 0) return;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  // item costs: prefix plus the causal keys of the tile's last row (0: an empty tile)
+  // item costs: prefix plus chunk of the item's sequence (0: an empty tile)
   int mx = 0, mn = 0x7fffffff;
   for (int i = t; i < n; i += kPlanThreads) {
     const int lid = lo + i;
@@ -1176,7 +1177,7 @@ prefill_plan_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ 
     const int C = max(0, min(cu[b + 1], total_q) - cu_b);
     const int64_t P0 = max((int64_t)0, min((int64_t)plen[b], (int64_t)bt_stride * kBlock));
     const int64_t nrows = (int64_t)C * G, v0 = (int64_t)tile * bm;
-    const int cost = (int)(v0 < nrows ? min(P0 + (min(nrows, v0 + bm) - 1) / G + 1, (int64_t)0x3fffffff) : 0);
+    const int cost = (int)(v0 < nrows ? min(P0 + C, (int64_t)0x3fffffff) : 0);
     cost_s[i] = cost;
     mx = max(mx, cost);
     if (cost > 0) mn = min(mn, cost);

@@ -224,8 +224,9 @@ def test_prefill_dispatch_plan_gives_same_bits():
 def test_prefill_dispatch_plan_is_a_stable_longest_first_permutation(batch, G, cmax):
     """The plan the prefill writes into its workspace: within each XCD's range of logical
     work items a permutation of that range, ordered by 32 cost buckets (key count of the
-    item's last row relative to the range's largest, empty items last) and, inside a
-    bucket, by table order.  Ranges of 512 and 4096 items (several sort passes across the
+    last row of the item's sequence, relative to the range's largest; empty items last)
+    and, inside a bucket, by table order, so the row tiles of one sequence and KV head
+    stay adjacent.  Ranges of 512 and 4096 items (several sort passes across the
     waves of the plan's work-group, several pairs per thread)."""
     import attention_paged_prefix_amd as kvb
     u = _util()
@@ -256,8 +257,8 @@ def test_prefill_dispatch_plan_is_a_stable_longest_first_permutation(batch, G, c
 
     def cost(lid):
         tile, b = lid % max_tiles, (lid // max_tiles) % batch
-        nrows, v0 = int(cu[b + 1] - cu[b]) * G, tile * bm
-        return int(w.prefix_lens[b]) + (min(nrows, v0 + bm) - 1) // G + 1 if v0 < nrows else 0
+        C, v0 = int(cu[b + 1] - cu[b]), tile * bm
+        return int(w.prefix_lens[b]) + C if v0 < C * G else 0
 
     for lo in range(0, real, per):
         n = min(per, real - lo)
@@ -270,6 +271,10 @@ def test_prefill_dispatch_plan_is_a_stable_longest_first_permutation(batch, G, c
             continue
         keys = [((31 - min(31, cost(l) * 32 // (cmx + 1))) if cost(l) > 0 else 32, l) for l in got.tolist()]
         assert keys == sorted(keys)
+        # the non-empty tiles of each (sequence, KV head) are consecutive in the order
+        grp = [l // max_tiles for l in got.tolist() if cost(l) > 0]
+        starts = [g for i, g in enumerate(grp) if i == 0 or grp[i - 1] != g]
+        assert len(starts) == len(set(grp))
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES + LARGE_GRID_CASES[:1],
