@@ -101,9 +101,9 @@ kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_n
  * workspace: (device, optional) NULL, or at least kvb_paged_prefill_workspace_size(...)
  * bytes, 16-byte aligned (else KVB_ERR_WORKSPACE / KVB_ERR_INVALID).  With it, a grid
  * of several rounds of work-groups is started longest first (a small plan kernel sorts
- * each XCD's work items by key count into the workspace first), which shortens the tail
- * on ragged batches; the results are the same bits either way.  Its contents on entry
- * do not matter. */
+ * each XCD's work items by the key count of their sequence, prefix plus chunk, into the
+ * workspace first), which shortens the tail on ragged batches; the results are the same
+ * bits either way.  Its contents on entry do not matter. */
 kvb_status kvb_paged_prefill(const kvb_pool* pool, const void* q, const void* k_new,
                              const void* v_new, void* out, const int32_t* cu_q_lens,
                              const int32_t* prefix_lens, const int32_t* block_tables,
