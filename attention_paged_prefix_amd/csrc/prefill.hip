@@ -672,10 +672,12 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     }
   };
   // exp2 of the two scores of pair e (kp4 = e/4, element e%4) of a tile, packed
-  // At head dims 64 and 96 phase 2 of a step (PV MFMAs) also takes the exponentials of
-  // the first half of the next tile's scores (pe), so that both phases carry about the
-  // same VALU work under their MFMAs; at 128 the registers are not there.
-  constexpr bool kEarlyExp = D <= 96;
+  // At head dims 64 and 96 (and 128 for the 16-bit pool with one key part) phase 2 of a
+  // step (PV MFMAs) also takes the exponentials of the first half of the next tile's
+  // scores (pe), so that both phases carry about the same VALU work under their MFMAs;
+  // the other forms at 128 do not have the registers (the code pools spill, and with two
+  // key parts it measured slower).
+  constexpr bool kEarlyExp = D <= 96 || (D == 128 && QB == 0 && KS == 1);
   float pe[16];
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) pe[rr] = 0.f;
@@ -1072,6 +1074,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
   const bool rvalid_e = vrow_e < nrows;
   const int i_e = vrow_e / G;
   const int64_t row_e = (int64_t)(cu_b + i_e) * hq + kvh * G + (vrow_e - i_e * G);
+  const int hf_e = (tid_e >> 5) & 1;                 // the lane's half of the row's columns
 
   // Final values of this lane's row: get(db, r) is the unnormalised output, M the
   // reference max and L the row sum.  Ordinary prefill stores the normalised row in the
@@ -1084,9 +1087,9 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<float4*>(wo + 32 * db + r4 * 8 + hf * 4) =
+          *reinterpret_cast<float4*>(wo + 32 * db + r4 * 8 + hf_e * 4) =
               make_float4(get(db, 4 * r4), get(db, 4 * r4 + 1), get(db, 4 * r4 + 2), get(db, 4 * r4 + 3));
-      if (hf == 0) {
+      if (hf_e == 0) {
         cas.ws_ml[(row_e * cas.ws_slots + ks) * 2 + 0] = M;
         cas.ws_ml[(row_e * cas.ws_slots + ks) * 2 + 1] = L;
       }
@@ -1101,7 +1104,7 @@ prefill_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
         uint2 uu;
         uu.x = pack2<T>(get(db, 4 * r4 + 0) * inv, get(db, 4 * r4 + 1) * inv);
         uu.y = pack2<T>(get(db, 4 * r4 + 2) * inv, get(db, 4 * r4 + 3) * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * db + r4 * 8 + hf * 4) = uu;
+        *reinterpret_cast<uint2*>(orow + 32 * db + r4 * 8 + hf_e * 4) = uu;
       }
   };
 
