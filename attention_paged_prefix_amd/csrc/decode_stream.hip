@@ -67,13 +67,19 @@ int64_t stream_hdr_bytes(int batch) { return ((int64_t)(batch + 3) * 4 + 255) / 
 static int64_t stream_ml_bytes(int64_t records, int nhc) { return (records * nhc * 8 + 255) / 256 * 256; }
 
 // One step's loads: per block, the K and V rows of one KV head in 16-byte chunks (16-bit
-// pool: D/32 chunks per lane; codes: 128/QB per chunk), and (codes) the V scales of the
-// four key rows whose probabilities the lane holds for the PV product.
-template <int D, int QB> struct StrStep {
+// pool: D/32 chunks per lane; codes: 128/QB per chunk), and the V scales of the code
+// pools.  Over a bf16 pool the V scales go into the probabilities of the PV product
+// (kScaleP: the scales of the four key rows whose probabilities the lane holds); over an
+// fp16 pool the V codes are scaled while staged (the scale of each chunk's key row),
+// since a probability (up to 2^8 under the lazy rescale) times a V scale (up to
+// 65504/127) can leave the fp16 range, while code * scale cannot.
+template <typename T, int D, int QB> struct StrStep {
   static constexpr int VCH = QB ? (D * QB / 8 + 63) / 64 : D / 32;
+  static constexpr bool kScaleP = QB != 0 && std::is_same<T, BF16>::value;
   uint4 k[2][VCH];
   uint4 v[2][VCH];
-  f32x4 vsc[QB ? 2 : 1];
+  f32x4 vsp[kScaleP ? 2 : 1];
+  float vsr[2][QB != 0 && !kScaleP ? VCH : 1];
 };
 
 template <typename T, int D, int QB>
@@ -83,7 +89,8 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
                      uint16_t* __restrict__ out, const int32_t* __restrict__ ctx_lens,
                      const int32_t* __restrict__ bt, float c_log2, DecStream ds, DecQ8 q8) {
   constexpr bool Q8 = QB != 0;
-  using Step = StrStep<D, QB>;
+  using Step = StrStep<T, D, QB>;
+  constexpr bool kScaleP = Step::kScaleP;
   constexpr int NKK = D / 32;
   constexpr int NDB = D / 16;
   constexpr int CPR = D / 8;                // 16-byte chunks per 16-bit V row
@@ -248,10 +255,18 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
           R.k[hb][j] = buf_load16(rk, (uint32_t)(j * 64 + lane) * 16);
           R.v[hb][j] = buf_load16(rv, (uint32_t)(j * 64 + lane) * 16);
         }
-        // V scales of key rows 4*g4 .. 4*g4+3 (rows past the context read as 0)
+        // V scales (rows past the context read as 0): of key rows 4*g4 .. 4*g4+3, or of
+        // the key row of each chunk
         const float* sb = q8.v_scale + ((int64_t)(pb >= 0 ? pb : 0) * ds.hkv + kvh) * kBlock;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(sb, (uint32_t)(rows * 4));
-        R.vsc[hb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * g4, 0, 0));
+        if constexpr (kScaleP) {
+          R.vsp[hb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * g4, 0, 0));
+        } else {
+#pragma unroll
+          for (int j = 0; j < VCH; ++j)
+            R.vsr[hb][j] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j * 64 + lane) / CPRQ * 4, 0, 0));
+        }
       } else {
         const int64_t off = (int64_t)(pb >= 0 ? pb : 0) * block_stride + (int64_t)kvh * kBlock * D;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + off, (uint32_t)(rows * D * 2));
@@ -326,7 +341,8 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   };
 
   // K and V of a step into this wave's LDS slot in their natural [key][d] layout (codes
-  // widened to the 16-bit type, exactly); rows past the context arrive as zeros.
+  // widened to the 16-bit type: K codes exactly, V codes exactly over a bf16 pool and
+  // times their key's V scale over an fp16 pool); rows past the context arrive as zeros.
   auto stage = [&](const Step& R) __attribute__((always_inline)) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -340,7 +356,7 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
           uint16_t* krow = kslot + (hb * 16 + row) * KROW + col;
           if constexpr (QB == 8) {
             uint4 lo, hi;
-            codes_to<T>(R.v[hb][j], 1.f, lo, hi);
+            codes_to<T>(R.v[hb][j], kScaleP ? 1.f : R.vsr[hb][kScaleP ? 0 : j], lo, hi);
             *reinterpret_cast<uint4*>(vrow) = lo;
             *reinterpret_cast<uint4*>(vrow + 8) = hi;
             codes_to<T>(R.k[hb][j], 1.f, lo, hi);
@@ -348,7 +364,7 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
             *reinterpret_cast<uint4*>(krow + 8) = hi;
           } else {
             uint4 o4[4];
-            nibbles_to<T>(R.v[hb][j], 1.f, o4);
+            nibbles_to<T>(R.v[hb][j], kScaleP ? 1.f : R.vsr[hb][kScaleP ? 0 : j], o4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vrow + 8 * i) = o4[i];
             nibbles_to<T>(R.k[hb][j], 1.f, o4);
@@ -386,11 +402,11 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
   };
 
   // Softmax update and O^T += V^T P^T for the step whose V is in the LDS slot (rows0,
-  // rows1: valid keys of its two blocks).  Code pools: the slot holds the V codes, and the
-  // V scale of each key multiplies its probability in the PV operand instead (sum_k p_k
-  // s_k c_k: one multiply per probability instead of one per value); the row sum takes
-  // the probabilities themselves.
-  auto update = [&](const f32x4 (&s)[2], int rows0, int rows1, const f32x4 (&vs)[Q8 ? 2 : 1])
+  // rows1: valid keys of its two blocks).  Code pools over bf16 (kScaleP): the slot holds
+  // the V codes, and the V scale of each key multiplies its probability in the PV operand
+  // instead (sum_k p_k s_k c_k: one multiply per probability instead of one per value);
+  // the row sum takes the probabilities themselves.
+  auto update = [&](const f32x4 (&s)[2], int rows0, int rows1, const f32x4 (&vs)[kScaleP ? 2 : 1])
       __attribute__((always_inline)) {
     const int rows[2] = {rows0, rows1};
     float t[8];
@@ -423,7 +439,7 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
       const float p0v = fast_exp2(t[2 * e] - m_run);
       const float p1v = fast_exp2(t[2 * e + 1] - m_run);
       l_run += p0v + p1v;
-      if constexpr (Q8)
+      if constexpr (kScaleP)
         pw[e] = pack2<T>(p0v * vs[e >> 1][2 * (e & 1)], p1v * vs[e >> 1][2 * (e & 1) + 1]);
       else
         pw[e] = pack2<T>(p0v, p1v);
@@ -548,9 +564,9 @@ decode_stream_kernel(const uint16_t* __restrict__ kp, const uint16_t* __restrict
       fresh = true;
     }
     const Desc n2 = nx.n ? claim() : Desc{0, 0, 0, 0, 0};
-    f32x4 vs[Q8 ? 2 : 1];
+    f32x4 vs[kScaleP ? 2 : 1];
 #pragma unroll
-    for (int i = 0; i < (Q8 ? 2 : 1); ++i) vs[i] = X.vsc[i];
+    for (int i = 0; i < (kScaleP ? 2 : 1); ++i) vs[i] = X.vsp[i];
     load(n2, X);
     update(s, cur.rows0, cur.rows1, vs);
     if (change) finish_unit(cur.u);

@@ -132,6 +132,41 @@ def test_decode_q8_matches_oracle(case, split):
     assert err <= u.TOL[dt], f"max abs err {err}"
 
 
+def test_decode_q8_fp16_large_values_growing_scores():
+    """An fp16 8-bit pool whose V values reach a few times 10^4 (V scales above 256) under
+    scores that grow along the context, so that probabilities come close to 2^8 before
+    each rescale: probability times V scale would leave the fp16 range, code times V
+    scale does not.  Outputs finite and within 2e-3 of the largest reference value."""
+    import attention_paged_prefix_amd as kvb
+    import oracle
+    from oracle import quant
+    u = _util()
+    rng = np.random.default_rng(817)
+    w = make_custom(817, "fp16", 8, 2, 64, [600, 333, 17], kind="decode", share="none", poison=False)
+    G = w.num_q_heads // w.num_kv_heads
+    q = oracle.decode_bits(w.q, "fp16")
+    k = oracle.decode_bits(w.k_pool, "fp16")
+    v = oracle.decode_bits(w.v_pool, "fp16")
+    for b, n in enumerate(w.context_lens):
+        for j in range(int(n)):
+            blk, row = int(w.block_tables[b][j // 16]), j % 16
+            for h in range(w.num_kv_heads):
+                k[blk, h, row, :] = q[b, h * G, :] * (6.0 * j / max(1, int(n))) + 0.1 * k[blk, h, row, :]
+    v = np.clip(v * 3.0e4, -6.0e4, 6.0e4)
+    w.k_pool, w.v_pool = round_to_bits(k, "fp16"), round_to_bits(v, "fp16")
+    kc, vc, vs, ks, _, _ = _oracle_q8_pool(w, _context_slots(w))
+    assert float(np.nanmax(vs)) > 256.0
+    pool = _pool_q8(kc, vc, vs, ks)
+    got = u.to_bits(kvb.paged_decode_q8(pool, u.to_dev(w.q, "fp16"), u.idev(w.context_lens),
+                                        u.idev(w.block_tables), w.scale, int(w.context_lens.max())))
+    torch.cuda.synchronize()
+    ref = quant.paged_decode_q8(kc, vc, vs, ks, w.q, w.context_lens, w.block_tables, w.scale, "fp16")
+    vals = oracle.decode_bits(got, "fp16")
+    assert np.isfinite(vals).all()
+    err = float(np.max(np.abs(vals - ref)))
+    assert err <= 2e-3 * float(np.max(np.abs(ref))), f"max abs err {err} of {float(np.max(np.abs(ref)))}"
+
+
 def test_write_then_decode_q8_end_to_end():
     """Every context token written by the GPU's quantising scatter, then decoded on the
     GPU; the oracle writes and decodes the same tokens itself."""
