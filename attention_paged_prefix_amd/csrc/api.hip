@@ -209,8 +209,10 @@ kvb_status kvb_paged_prefill_pooled(const kvb_pool* pool, const void* q, void* o
 size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
                                        int32_t head_dim, int32_t max_context_len,
                                        int32_t split_blocks) {
+  // (every context empty, max_context_len 0: the plan still writes the zero rows, through
+  // its header and merge, so it takes the same workspace as any other)
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
-      max_context_len <= 0 || split_blocks < 0)
+      max_context_len < 0 || split_blocks < 0)
     return 0;
   return (size_t)decode_plan_for(batch, num_kv_heads, num_q_heads, head_dim, max_context_len,
                                  split_blocks).bytes;
@@ -334,7 +336,7 @@ size_t kvb_paged_decode_cascade_workspace_size(int32_t batch, int32_t num_kv_hea
                                                int32_t max_context_len, int32_t shared_len,
                                                int32_t split_blocks) {
   if (batch <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
-      max_context_len <= 0 || split_blocks < 0 || shared_len < 0 || shared_len % 16)
+      max_context_len < 0 || split_blocks < 0 || shared_len < 0 || shared_len % 16)
     return 0;
   const CascadePlan c = cascade_plans(batch, num_kv_heads, num_q_heads, max_context_len,
                                       shared_len, split_blocks);

@@ -150,9 +150,22 @@ def test_decode_validation_and_workspace(lib):
     # records = waves + units (8) of 4 heads: a 256-byte header, then (max, sum) pairs
     # (rounded up to 256 bytes), then d floats per head
     assert lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 16) == 256 + 4352 + 136 * 4 * 128 * 4
-    # ranges longer than 128 blocks are taken as 128
+    # ranges longer than 64 blocks are taken as 64
     assert (lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 256)
-            == lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 128))
+            == lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 4000, 64))
+
+
+def test_decode_workspace_size_matches_the_call_when_every_context_is_empty(lib):
+    """max_context_len 0 (every context empty): the call still writes the zero rows through
+    its plan, and the size query reports that plan's workspace, so a caller that follows
+    the query is not refused."""
+    p = pool()
+    need = lib.kvb_paged_decode_workspace_size(4, 2, 8, 128, 0, 0)
+    assert need > 0
+    assert decode(lib, p, maxc=0, stride=1) == WS
+    assert decode(lib, p, maxc=0, stride=1, ws=FAKE, wsb=need - 1) == WS
+    needc = lib.kvb_paged_decode_cascade_workspace_size(4, 2, 8, 128, 0, 0, 0)
+    assert needc > 0
 
 
 def decode_noalloc(lib, p, **kw):

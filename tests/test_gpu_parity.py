@@ -378,6 +378,26 @@ def test_decode_zero_context_gives_zero_row():
     assert u.max_err(got[:1], ref[:1], "bf16") <= 2e-2
 
 
+def test_decode_every_context_empty_gives_zero_rows():
+    """max_context_len 0 (every context empty): every output row is zero, through the
+    workspace the size queries report, in the plain form (default and forced split plans),
+    the allocation-free form and the cascade form without a shared prefix.  Outputs start
+    out non-zero."""
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    w = make_custom(306, "fp16", 8, 2, 64, [0, 0, 0], kind="decode", poison=True)
+    assert int(w.context_lens.max()) == 0
+    dev = u.Dev(w)
+    fill = lambda: torch.full_like(dev.q, 7.0)   # noqa: E731
+    outs = [dev.decode(out=fill()), dev.decode(split_blocks=4, out=fill()),
+            kvb.paged_decode_noalloc(dev.pool, dev.q, dev.ctx, dev.bt, w.scale, 0, out=fill()),
+            kvb.paged_decode_cascade(dev.pool, dev.q, dev.ctx, dev.bt, u.idev(np.zeros(1, np.int32)), 0,
+                                     w.scale, 0, out=fill())]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert (u.to_bits(o) == 0).all()
+
+
 @pytest.mark.parametrize("batch", [1024, 1025])
 def test_decode_batch_at_the_balanced_form_bound(batch):
     """1024 sequences: the largest batch of the balanced form (prefix sums of all block

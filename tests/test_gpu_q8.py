@@ -167,6 +167,24 @@ def test_decode_q8_fp16_large_values_growing_scores():
     assert err <= 2e-3 * float(np.max(np.abs(ref))), f"max abs err {err} of {float(np.max(np.abs(ref)))}"
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_decode_quant_every_context_empty_gives_zero_rows(bits):
+    """max_context_len 0 over the 8-bit and 4-bit pools: zero rows, through the workspace
+    the size query reports."""
+    import attention_paged_prefix_amd as kvb
+    u = _util()
+    w = make_custom(818, "bf16", 8, 2, 128, [0, 0], kind="decode", poison=False)
+    nb = w.k_pool.shape[0]
+    kc, vc, vs = _poisoned(nb, 2, 128) if bits == 8 else _poisoned4(nb, 2, 128)
+    ks = np.full((2, 128), 0.01, np.float32)
+    pool = _pool_q8(kc, vc, vs, ks) if bits == 8 else _pool_q4(kc, vc, vs, ks)
+    fn = kvb.paged_decode_q8 if bits == 8 else kvb.paged_decode_q4
+    out = torch.full_like(u.to_dev(w.q, "bf16"), 7.0)
+    fn(pool, u.to_dev(w.q, "bf16"), u.idev(w.context_lens), u.idev(w.block_tables), w.scale, 0, out=out)
+    torch.cuda.synchronize()
+    assert (u.to_bits(out) == 0).all()
+
+
 def test_write_then_decode_q8_end_to_end():
     """Every context token written by the GPU's quantising scatter, then decoded on the
     GPU; the oracle writes and decodes the same tokens itself."""
