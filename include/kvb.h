@@ -94,9 +94,9 @@ kvb_status kvb_write_kv(const kvb_pool* pool, const void* k_new, const void* v_n
  * [total_q][num_kv_heads][head_dim]; cu_q_lens: (device) int32 [batch+1], non-decreasing,
  * cu_q_lens[0] = 0, cu_q_lens[batch] = total_q; prefix_lens: (device) int32 [batch] >= 0;
  * block_tables: (device) int32 [batch][block_table_stride] with
- * block_table_stride >= ceil(max_prefix_len/16).  max_q_len >= every chunk length and
- * max_prefix_len >= every prefix length (host bounds used for the launch grid; a
- * larger value only costs idle work-groups).  Only pool entries of the prefix are read,
+ * block_table_stride >= ceil(max_prefix_len/16).  max_q_len >= every chunk length (and
+ * <= total_q, else KVB_ERR_INVALID) and max_prefix_len >= every prefix length (host
+ * bounds used for the launch grid; a larger value only costs idle work-groups).  Only pool entries of the prefix are read,
  * so kvb_write_kv of the same chunk may run before or after this call.
  * workspace: (device, optional) NULL, or at least kvb_paged_prefill_workspace_size(...)
  * bytes, 16-byte aligned (else KVB_ERR_WORKSPACE / KVB_ERR_INVALID).  With it, a grid

@@ -1,7 +1,8 @@
 """Seeded random GPU parity sweep: random shapes (dtype, head dim, KV heads, GQA group,
 batch, prefix and chunk lengths with a bias toward block and tile edges, sharing) through
 the prefill (plain, with the fused slot scatter, pooled; empty chunks inside a batch; both
-pool layouts), the decode (split plans forced at random), the cascade decode and the 8-bit
+pool layouts; block-table rows longer than needed; host bounds above the batch's), the
+decode (split plans forced at random, both pool layouts), the cascade decode and the 8-bit
 and 4-bit pools, each against the oracle within the decode/prefill tolerance.  Every
 failing case is reported with its parameters."""
 import numpy as np
@@ -62,14 +63,22 @@ def test_random_prefill(seed):
         if max(C) == 0:
             C[0] = 3
         share = str(r.choice(["none", "pairs", "all"]))
-        case = (seed * 1000 + i, dt, hq, hkv, d, P, C, share)
-        w = make_custom(case[0], dt, hq, hkv, d, P, C, share=share, poison=True)
+        extra = int(r.choice([0, 0, 3]))            # block-table rows longer than needed
+        case = (seed * 1000 + i, dt, hq, hkv, d, P, C, share, extra)
+        w = make_custom(case[0], dt, hq, hkv, d, P, C, share=share, poison=True, stride_extra=extra)
         layout = str(r.choice(["split", "interleaved"]))
         dev = u.Dev(w, pool_layout=layout)
         got = u.to_bits(dev.prefill())
         torch.cuda.synchronize()
         ref = u.oracle_prefill(w)
         s.check("prefill", got, ref, dt, case + (layout,))
+        # host bounds larger than the batch's (allowed up to total_q: only idle work-groups)
+        loose = u.to_bits(kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt,
+                                            w.scale, min(int(w.q_lens.max()) + 17, int(w.total_q)),
+                                            int(w.prefix_lens.max()) + 16 * extra))
+        torch.cuda.synchronize()
+        if not np.array_equal(loose, got):
+            s.bad.append(("prefill_loose_bounds", None, case))
         if layout == "interleaved":                  # the scatter checks below read dev.k / dev.v
             continue
         out = kvb.paged_prefill(dev.pool, dev.q, dev.k_new, dev.v_new, dev.cu, dev.pl, dev.bt, w.scale,
@@ -97,9 +106,12 @@ def test_random_decode_and_cascade(seed):
         ctx = s.lens(B, 0, 3000)
         share = str(r.choice(["none", "pairs", "all"]))
         sb = int(r.choice([0, 0, 1, 3, 17, 64]))
-        case = (seed * 1000 + i, dt, hq, hkv, d, ctx, share, sb)
-        w = make_custom(case[0], dt, hq, hkv, d, ctx, kind="decode", share=share, poison=True)
-        got = u.to_bits(u.Dev(w).decode(split_blocks=sb))
+        extra = int(r.choice([0, 0, 3]))
+        layout = str(r.choice(["split", "interleaved"]))
+        case = (seed * 1000 + i, dt, hq, hkv, d, ctx, share, sb, extra, layout)
+        w = make_custom(case[0], dt, hq, hkv, d, ctx, kind="decode", share=share, poison=True,
+                        stride_extra=extra)
+        got = u.to_bits(u.Dev(w, pool_layout=layout).decode(split_blocks=sb))
         torch.cuda.synchronize()
         s.check("decode", got, u.oracle_decode(w), dt, case)
     for i in range(8):
