@@ -1,4 +1,4 @@
-"""Seeded random GPU parity sweep: random shapes (dtype, head dim, KV heads, GQA group,
+"""Seeded random GPU parity sweep: random shapes (dtype, head dim, KV heads, GQA group up to 32,
 batch, prefix and chunk lengths with a bias toward block and tile edges, sharing) through
 the prefill (plain, with the fused slot scatter, pooled; empty chunks inside a batch; both
 pool layouts; block-table rows longer than needed; host bounds above the batch's), the
@@ -39,6 +39,8 @@ class Sweep:
         dt = str(r.choice(["fp16", "bf16"]))
         d = int(r.choice([64, 96, 128]))
         hkv = int(r.choice([1, 2, 4, 8]))
+        if r.random() < 0.2:                        # groups at and past 16 query heads
+            return dt, d, min(hkv, 2), min(hkv, 2) * int(r.choice([16, 17, 20, 32]))
         return dt, d, hkv, hkv * int(r.choice([1, 2, 3, 4, 5, 8]))
 
     def check(self, kind, got_bits, ref, dt, case):
