@@ -212,7 +212,9 @@ kvb_status kvb_paged_decode_cascade(const kvb_pool* pool, const void* q, void* o
  * current device's compute-unit count (the decode plan sizes its grid to the device), so a
  * size holds for the device that is current when it is queried; call the size query and
  * the decode with the same device current.  The
- * decode sizes take num_kv_heads too: the split plan counts (sequence, KV head) units. */
+ * decode sizes take num_kv_heads too: the split plan counts (sequence, KV head) units;
+ * they are 0 only for an empty batch or invalid arguments (max_context_len 0, every
+ * context empty, still takes the plan's workspace: the call writes the zero rows). */
 size_t kvb_paged_prefill_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                                         int32_t total_q, int32_t max_prefix_len);
 size_t kvb_paged_decode_workspace_size(int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
