@@ -101,7 +101,8 @@ def _oracle_q8_pool(w, slots):
     every context slot written by the oracle, the other slots poisoned."""
     from oracle import quant
     kt, vt = _tokens_at(w.k_pool, slots), _tokens_at(w.v_pool, slots)
-    k_scale = channel_scales(oracle_f32(kt, w.dtype))
+    k_scale = channel_scales(oracle_f32(kt, w.dtype)) if len(slots) \
+        else np.full((w.num_kv_heads, w.head_dim), 0.01, np.float32)
     kc, vc, vs = _poisoned(w.k_pool.shape[0], w.num_kv_heads, w.head_dim)
     kc, vc, vs = quant.write_kv_q8(kc, vc, vs, k_scale, kt, vt, slots, w.dtype)
     return kc, vc, vs, k_scale, kt, vt
