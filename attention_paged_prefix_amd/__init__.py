@@ -40,6 +40,19 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _index(device, dtype, min_rows: int, **tensors) -> None:
+    """The kernels read index tensors through raw device pointers: each must be a contiguous
+    ``dtype`` tensor on ``device`` (any GPU when None) with at least ``min_rows`` rows
+    (elements when 1-D); None passes."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        on = t.is_cuda if device is None else t.device == device
+        if t.dtype != dtype or not t.is_contiguous() or not on or t.dim() == 0 or t.shape[0] < min_rows:
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of at least {min_rows} "
+                             f"rows on {device if device is not None else 'the GPU'}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -92,6 +105,9 @@ def version() -> str:
 def write_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
              stream=None) -> None:
     """kvb_write_kv: scatter ``k_new/v_new [T][Hkv][d]`` into pool slots ``slot_mapping`` (int64)."""
+    _index(k_new.device, torch.int64, 0, slot_mapping=slot_mapping)
+    if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
+        raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
     lib = _lib.load()
     ps = pool.c_struct()
     _lib.check("kvb_write_kv", lib.kvb_write_kv(
@@ -126,6 +142,12 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Option
     return workspace
 
 
+def _prefill_index(q, cu_q_lens, prefix_lens, block_tables) -> None:
+    batch = prefix_lens.numel() if isinstance(prefix_lens, torch.Tensor) else 0
+    _index(q.device, torch.int32, batch, prefix_lens=prefix_lens, block_tables=block_tables)
+    _index(q.device, torch.int32, batch + 1, cu_q_lens=cu_q_lens)
+
+
 def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                   cu_q_lens: torch.Tensor, prefix_lens: torch.Tensor, block_tables: torch.Tensor,
                   scale: float, max_q_len: int, max_prefix_len: int,
@@ -138,6 +160,7 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     of longest first (same results).  With ``slot_mapping`` (int64 [T]) the call is
     kvb_paged_prefill_write: the chunk's K/V is also written into the pool at those slots,
     as write_kv would, in the same launch."""
+    _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -175,6 +198,7 @@ def paged_prefill_pooled(pool: Pool, q: torch.Tensor, cu_q_lens: torch.Tensor,
                          stream=None) -> torch.Tensor:
     """kvb_paged_prefill_pooled: as ``paged_prefill``, with the chunk's own K/V read from
     the pool (written there by ``write_kv`` first) through ``block_tables``."""
+    _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -194,6 +218,7 @@ def paged_decode(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvb_paged_decode.  ``q [B][Hq][d]``, ``context_lens`` int32 [B] (including the current
     token), ``block_tables`` int32 [B][stride]."""
+    _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -215,6 +240,7 @@ def paged_decode_noalloc(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
     """kvb_paged_decode_noalloc: ``paged_decode`` with the split partials in the library's
     static device scratch instead of a workspace.  ``out`` is required: this call allocates
     nothing.  Calls that overlap on one GPU share the scratch and race."""
+    _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     lib = _lib.load()
     B, hq, d = q.shape
     ps = pool.c_struct()
@@ -229,6 +255,8 @@ def gather_kv(pool: Pool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
               cu_seq_lens: torch.Tensor, max_len: int, k_out: torch.Tensor, v_out: torch.Tensor,
               stream=None) -> None:
     """kvb_gather_kv (indexing check): logical tokens of every sequence, contiguous."""
+    _index(k_out.device, torch.int32, seq_lens.numel(), block_tables=block_tables, seq_lens=seq_lens)
+    _index(k_out.device, torch.int32, seq_lens.numel() + 1, cu_seq_lens=cu_seq_lens)
     lib = _lib.load()
     ps = pool.c_struct()
     _lib.check("kvb_gather_kv", lib.kvb_gather_kv(
@@ -244,6 +272,8 @@ def paged_decode_cascade(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvb_paged_decode_cascade.  As ``paged_decode``; the first ``shared_len`` tokens of
     every sequence are the blocks ``shared_blocks`` (int32), read once for all queries."""
+    _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
+    _index(q.device, torch.int32, (max(int(shared_len), 0) + 15) // 16, shared_blocks=shared_blocks)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -264,6 +294,7 @@ def copy_blocks(src: Pool, dst: Pool, src_ids: torch.Tensor, dst_ids: torch.Tens
                 stream=None) -> None:
     """kvb_copy_blocks: block dst_ids[i] of ``dst`` becomes a copy of block src_ids[i] of
     ``src`` (K and V, every head).  ``src_ids``/``dst_ids``: int32 device tensors."""
+    _index(None, torch.int32, src_ids.numel(), src_ids=src_ids, dst_ids=dst_ids)
     lib = _lib.load()
     a, b = src.c_struct(), dst.c_struct()
     _lib.check("kvb_copy_blocks", lib.kvb_copy_blocks(
@@ -337,6 +368,9 @@ def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_map
                 stream=None) -> None:
     """kvb_write_kv_q8: code ``k_new/v_new [T][Hkv][d]`` (fp16/bf16) into the 8-bit pool's
     slots ``slot_mapping`` (int64), writing each token's V scale."""
+    _index(k_new.device, torch.int64, 0, slot_mapping=slot_mapping)
+    if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
+        raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
     lib = _lib.load()
     if k_new.dtype not in _DT or v_new.dtype != k_new.dtype:
         raise ValueError("k_new/v_new must both be float16 or bfloat16")
@@ -351,6 +385,7 @@ def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
                     split_blocks: int = 0, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvb_paged_decode_q8: ``paged_decode`` over the 8-bit pool; ``q``/``out`` fp16 or bf16."""
+    _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")
@@ -381,6 +416,7 @@ def paged_prefill_q8(pool: PoolQ8, q: torch.Tensor, k_new: torch.Tensor, v_new: 
                      stream=None) -> torch.Tensor:
     """kvb_paged_prefill_q8: ``paged_prefill`` with the cached prefix in the 8-bit pool;
     ``q``, ``k_new``, ``v_new``, ``out`` fp16 or bf16."""
+    _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")
