@@ -53,6 +53,20 @@ def _index(device, dtype, min_rows: int, **tensors) -> None:
                              f"rows on {device if device is not None else 'the GPU'}")
 
 
+def _gpu(**tensors) -> None:
+    """Tensors the kernels read or write through raw pointers must be in GPU memory (None
+    passes)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _pool_memory(*tensors) -> None:
+    # pools may also sit in pinned host memory, which the GPU reaches at the same address
+    if not all(t.is_cuda or t.is_pinned() for t in tensors):
+        raise ValueError("pool tensors must be in GPU memory or in pinned host memory")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -94,6 +108,7 @@ class Pool:
     def c_struct(self) -> KvbPool:
         if self.k.dtype not in _DT:
             raise ValueError(f"unsupported pool dtype {self.k.dtype}")
+        _pool_memory(self.k, self.v)
         return KvbPool(self.k.data_ptr(), self.v.data_ptr(), self.block_stride, self.num_blocks,
                        BLOCK_SIZE, self.num_kv_heads, self.head_dim, _DT[self.k.dtype])
 
@@ -108,6 +123,7 @@ def write_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping:
     _index(k_new.device, torch.int64, 0, slot_mapping=slot_mapping)
     if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
         raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
+    _gpu(k_new=k_new, v_new=v_new)
     lib = _lib.load()
     ps = pool.c_struct()
     _lib.check("kvb_write_kv", lib.kvb_write_kv(
@@ -161,6 +177,12 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     kvb_paged_prefill_write: the chunk's K/V is also written into the pool at those slots,
     as write_kv would, in the same launch."""
     _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
+    if slot_mapping is not None:
+        # the kernel reads total_q int64 slots through this pointer
+        _index(q.device, torch.int64, q.shape[0], slot_mapping=slot_mapping)
+        if slot_mapping.numel() != q.shape[0]:
+            raise ValueError("slot_mapping must hold one slot per query row")
+    _gpu(q=q, k_new=k_new, v_new=v_new, out=out, workspace=workspace)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -174,11 +196,6 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     ps = pool.c_struct()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if slot_mapping is not None:
-        # the kernel reads total_q int64 slots through this pointer
-        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T or \
-                slot_mapping.device != q.device or not slot_mapping.is_contiguous():
-            raise ValueError("slot_mapping must be a contiguous int64 tensor of total_q entries "
-                             "on q's device")
         _lib.check("kvb_paged_prefill_write", lib.kvb_paged_prefill_write(
             ctypes.byref(ps), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(slot_mapping),
             _ptr(cu_q_lens), _ptr(prefix_lens), _ptr(block_tables), int(block_tables.shape[1]), batch,
@@ -199,6 +216,7 @@ def paged_prefill_pooled(pool: Pool, q: torch.Tensor, cu_q_lens: torch.Tensor,
     """kvb_paged_prefill_pooled: as ``paged_prefill``, with the chunk's own K/V read from
     the pool (written there by ``write_kv`` first) through ``block_tables``."""
     _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
+    _gpu(q=q, out=out)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -219,6 +237,7 @@ def paged_decode(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
     """kvb_paged_decode.  ``q [B][Hq][d]``, ``context_lens`` int32 [B] (including the current
     token), ``block_tables`` int32 [B][stride]."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
+    _gpu(q=q, out=out, workspace=workspace)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -241,6 +260,7 @@ def paged_decode_noalloc(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
     static device scratch instead of a workspace.  ``out`` is required: this call allocates
     nothing.  Calls that overlap on one GPU share the scratch and race."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
+    _gpu(q=q, out=out)
     lib = _lib.load()
     B, hq, d = q.shape
     ps = pool.c_struct()
@@ -257,6 +277,7 @@ def gather_kv(pool: Pool, block_tables: torch.Tensor, seq_lens: torch.Tensor,
     """kvb_gather_kv (indexing check): logical tokens of every sequence, contiguous."""
     _index(k_out.device, torch.int32, seq_lens.numel(), block_tables=block_tables, seq_lens=seq_lens)
     _index(k_out.device, torch.int32, seq_lens.numel() + 1, cu_seq_lens=cu_seq_lens)
+    _gpu(k_out=k_out, v_out=v_out)
     lib = _lib.load()
     ps = pool.c_struct()
     _lib.check("kvb_gather_kv", lib.kvb_gather_kv(
@@ -274,6 +295,7 @@ def paged_decode_cascade(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
     every sequence are the blocks ``shared_blocks`` (int32), read once for all queries."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     _index(q.device, torch.int32, (max(int(shared_len), 0) + 15) // 16, shared_blocks=shared_blocks)
+    _gpu(q=q, out=out, workspace=workspace)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -351,6 +373,7 @@ class PoolQ8:
         if self.v.shape != self.k.shape or self.v_scale.shape != (nb, hkv, bs) or \
                 self.k_scale.shape != (hkv, d):
             raise ValueError("quantised pool tensor shapes do not match")
+        _pool_memory(self.k, self.v, self.v_scale, self.k_scale)
         return KvbPoolQ8(self.k.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(),
                          self.k_scale.data_ptr(), hkv * bs * row_bytes, nb, bs, hkv, d)
 
@@ -371,6 +394,7 @@ def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_map
     _index(k_new.device, torch.int64, 0, slot_mapping=slot_mapping)
     if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
         raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
+    _gpu(k_new=k_new, v_new=v_new)
     lib = _lib.load()
     if k_new.dtype not in _DT or v_new.dtype != k_new.dtype:
         raise ValueError("k_new/v_new must both be float16 or bfloat16")
@@ -386,6 +410,7 @@ def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """kvb_paged_decode_q8: ``paged_decode`` over the 8-bit pool; ``q``/``out`` fp16 or bf16."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
+    _gpu(q=q, out=out, workspace=workspace)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")
@@ -417,6 +442,7 @@ def paged_prefill_q8(pool: PoolQ8, q: torch.Tensor, k_new: torch.Tensor, v_new: 
     """kvb_paged_prefill_q8: ``paged_prefill`` with the cached prefix in the 8-bit pool;
     ``q``, ``k_new``, ``v_new``, ``out`` fp16 or bf16."""
     _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
+    _gpu(q=q, k_new=k_new, v_new=v_new, out=out, workspace=workspace)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")
