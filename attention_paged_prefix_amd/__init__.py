@@ -61,6 +61,27 @@ def _gpu(**tensors) -> None:
             raise ValueError(f"{name} must be a GPU tensor")
 
 
+def _shaped(shape, dtypes, **tensors) -> None:
+    """Data tensors are addressed from the pool's head dim and the call's sizes: each must be
+    contiguous, of one of ``dtypes`` and of exactly ``shape`` (None passes)."""
+    for name, t in tensors.items():
+        if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype not in dtypes
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(shape)} "
+                             f"and dtype {' or '.join(str(d) for d in dtypes)}")
+
+
+def _qkv(pool, q, k_new=None, v_new=None, out=None) -> None:
+    # q/out [rows][Hq][d] and k_new/v_new [rows][Hkv][d] at the pool's head dim; a 16-bit pool
+    # also fixes their dtype
+    if q.dim() != 3:
+        raise ValueError("q must be [rows][num_q_heads][head_dim]")
+    dts = (pool.k.dtype,) if isinstance(pool, Pool) else tuple(_DT)
+    _shaped((q.shape[0], q.shape[1], pool.head_dim), dts, q=q)
+    _shaped(q.shape, (q.dtype,), out=out)
+    _shaped((q.shape[0], pool.num_kv_heads, pool.head_dim), (q.dtype,), k_new=k_new, v_new=v_new)
+
+
 def _pool_memory(*tensors) -> None:
     # pools may also sit in pinned host memory, which the GPU reaches at the same address
     if not all(t.is_cuda or t.is_pinned() for t in tensors):
@@ -124,6 +145,9 @@ def write_kv(pool: Pool, k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping:
     if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
         raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
     _gpu(k_new=k_new, v_new=v_new)
+    _shaped((k_new.shape[0], pool.num_kv_heads, pool.head_dim),
+            (pool.k.dtype,) if isinstance(pool, Pool) else tuple(_DT), k_new=k_new)
+    _shaped(k_new.shape, (k_new.dtype,), v_new=v_new)
     lib = _lib.load()
     ps = pool.c_struct()
     _lib.check("kvb_write_kv", lib.kvb_write_kv(
@@ -183,6 +207,7 @@ def paged_prefill(pool: Pool, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
         if slot_mapping.numel() != q.shape[0]:
             raise ValueError("slot_mapping must hold one slot per query row")
     _gpu(q=q, k_new=k_new, v_new=v_new, out=out, workspace=workspace)
+    _qkv(pool, q, k_new, v_new, out)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -217,6 +242,7 @@ def paged_prefill_pooled(pool: Pool, q: torch.Tensor, cu_q_lens: torch.Tensor,
     the pool (written there by ``write_kv`` first) through ``block_tables``."""
     _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
     _gpu(q=q, out=out)
+    _qkv(pool, q, out=out)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -238,6 +264,7 @@ def paged_decode(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor,
     token), ``block_tables`` int32 [B][stride]."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     _gpu(q=q, out=out, workspace=workspace)
+    _qkv(pool, q, out=out)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -261,6 +288,7 @@ def paged_decode_noalloc(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
     nothing.  Calls that overlap on one GPU share the scratch and race."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     _gpu(q=q, out=out)
+    _qkv(pool, q, out=out)
     lib = _lib.load()
     B, hq, d = q.shape
     ps = pool.c_struct()
@@ -296,6 +324,7 @@ def paged_decode_cascade(pool: Pool, q: torch.Tensor, context_lens: torch.Tensor
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     _index(q.device, torch.int32, (max(int(shared_len), 0) + 15) // 16, shared_blocks=shared_blocks)
     _gpu(q=q, out=out, workspace=workspace)
+    _qkv(pool, q, out=out)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -395,6 +424,9 @@ def write_kv_q8(pool: PoolQ8, k_new: torch.Tensor, v_new: torch.Tensor, slot_map
     if min(k_new.shape[0], v_new.shape[0]) < slot_mapping.numel():
         raise ValueError("k_new/v_new need a row for every entry of slot_mapping")
     _gpu(k_new=k_new, v_new=v_new)
+    _shaped((k_new.shape[0], pool.num_kv_heads, pool.head_dim),
+            (pool.k.dtype,) if isinstance(pool, Pool) else tuple(_DT), k_new=k_new)
+    _shaped(k_new.shape, (k_new.dtype,), v_new=v_new)
     lib = _lib.load()
     if k_new.dtype not in _DT or v_new.dtype != k_new.dtype:
         raise ValueError("k_new/v_new must both be float16 or bfloat16")
@@ -411,6 +443,7 @@ def paged_decode_q8(pool: PoolQ8, q: torch.Tensor, context_lens: torch.Tensor,
     """kvb_paged_decode_q8: ``paged_decode`` over the 8-bit pool; ``q``/``out`` fp16 or bf16."""
     _index(q.device, torch.int32, q.shape[0], context_lens=context_lens, block_tables=block_tables)
     _gpu(q=q, out=out, workspace=workspace)
+    _qkv(pool, q, out=out)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")
@@ -443,6 +476,7 @@ def paged_prefill_q8(pool: PoolQ8, q: torch.Tensor, k_new: torch.Tensor, v_new: 
     ``q``, ``k_new``, ``v_new``, ``out`` fp16 or bf16."""
     _prefill_index(q, cu_q_lens, prefix_lens, block_tables)
     _gpu(q=q, k_new=k_new, v_new=v_new, out=out, workspace=workspace)
+    _qkv(pool, q, k_new, v_new, out)
     lib = _lib.load()
     if q.dtype not in _DT:
         raise ValueError("q must be float16 or bfloat16")

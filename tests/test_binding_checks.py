@@ -124,3 +124,27 @@ def test_pools_in_pageable_host_memory_are_rejected():
     q8 = kvb.PoolQ8(codes, codes.clone(), torch.zeros(NB, HKV, 16), torch.zeros(HKV, D))
     with pytest.raises(ValueError, match="pool tensors"):
         q8.c_struct()
+
+
+def test_data_tensor_shapes_follow_the_pool():
+    pool, f16 = _pool(), torch.float16
+    q, kn = torch.zeros(5, HQ, D, dtype=f16), torch.zeros(5, HKV, D, dtype=f16)
+    kvb._qkv(pool, q, kn, kn.clone(), torch.zeros_like(q))          # well formed: no error
+    bad = [
+        (dict(q=torch.zeros(5, HQ, D // 2, dtype=f16)), "q must"),   # head dim of another pool
+        (dict(q=q.to(torch.bfloat16)), "q must"),                    # not the pool's dtype
+        (dict(q=torch.zeros(5, 2 * HQ, D, dtype=f16)[:, ::2]), "q must"),
+        (dict(out=torch.zeros(4, HQ, D, dtype=f16)), "out must"),
+        (dict(k_new=torch.zeros(5, HKV + 1, D, dtype=f16)), "k_new must"),
+        (dict(v_new=torch.zeros(4, HKV, D, dtype=f16)), "v_new must"),
+    ]
+    for change, msg in bad:
+        a = dict(q=q, k_new=kn, v_new=kn, out=None)
+        a.update(change)
+        with pytest.raises(ValueError, match=msg):
+            kvb._qkv(pool, **a)
+    codes = torch.zeros(NB, HKV, 16, D, dtype=torch.int8)
+    q8 = kvb.PoolQ8(codes, codes.clone(), torch.zeros(NB, HKV, 16), torch.zeros(HKV, D))
+    kvb._qkv(q8, q.to(torch.bfloat16))                               # code pools take either
+    with pytest.raises(ValueError, match="q must"):
+        kvb._qkv(q8, q.float())
